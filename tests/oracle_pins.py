@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each pin takes an ``oracle.Oracle`` and raises ``AssertionError`` when the
+oracle disagrees with what the pages or the mathematics fix:
+
+* hand-worked values (``tests/golden/*.txt``, each file citing its passage);
+* the order of the key against IEEE float order, exhaustively over all
+  65,536 BF16 patterns (numpy float32 comparisons, not the key formula);
+* brute force over every k-subset of tiny rows;
+* numpy's own sort (a different sort from the oracle's qsort) for the k-th
+  key and for the top-k values of NaN-free rows;
+* closed forms (constant rows, short rows, -inf blocks, pinned newest block,
+  clamped lengths) and the inverse-table round trip of the page transform.
+
+The same pins are run against copies of the oracle built from deliberately
+altered sources (``test_oracle_pins.py``), to show that a plausible mistake
+anywhere in the oracle fails at least one of them.
+"""
+from __future__ import annotations
+
+import itertools
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOKEN, BLOCK = 0, 1
+
+
+def bf16_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _all_patterns():
+    return np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def _nan_mask(bits):
+    return np.isnan(bf16_to_f32(bits))
+
+
+# ---------------------------------------------------------------- key pins
+def pin_key_fixed_points(orc):
+    """Hand-worked keys (golden/key_fixed_points.txt)."""
+    with open(os.path.join(GOLDEN, "key_fixed_points.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            b, k, what = line.split()[:3]
+            got = int(orc.key(np.array([int(b, 16)], np.uint16))[0])
+            assert got == int(k, 16), f"key({b}) = {got:#06x}, expected {k} ({what})"
+
+
+def pin_key_bijection(orc):
+    """The key is a bijection of the 16-bit patterns (ties only for equal bits)."""
+    keys = orc.key(_all_patterns())
+    assert np.array_equal(np.sort(keys), np.arange(1 << 16, dtype=np.uint16)), \
+        "key is not a permutation of 0..65535"
+
+
+def pin_key_follows_float_order(orc):
+    """For every pair of non-NaN patterns: key order == IEEE value order,
+    with -0 directly below +0 (the pages' value order)."""
+    bits = _all_patterns()
+    vals = bf16_to_f32(bits)
+    ok = ~np.isnan(vals)
+    b, v = bits[ok], vals[ok]
+    positive_sign = (b & 0x8000) == 0        # breaks the +0 / -0 tie: -0 first
+    order = np.lexsort((positive_sign, v))
+    keys = orc.key(b[order]).astype(np.int64)
+    assert np.all(np.diff(keys) > 0), "keys not strictly increasing in value order"
+
+
+def pin_key_nan_placement(orc):
+    """Positive NaNs above +inf, negative NaNs below -inf (reading of the
+    pages: NaNs compare through the key like any pattern)."""
+    bits = _all_patterns()
+    keys = orc.key(bits).astype(np.int64)
+    nan = _nan_mask(bits)
+    neg = (bits & 0x8000) != 0
+    finite_keys = keys[~nan]
+    assert keys[nan & ~neg].min() > finite_keys.max(), "+NaN not above +inf"
+    assert keys[nan & neg].max() < finite_keys.min(), "-NaN not below -inf"
+
+
+def pin_is_nan(orc):
+    """oracle_is_nan agrees with IEEE isnan on all patterns (sampled)."""
+    bits = _all_patterns()
+    ref = _nan_mask(bits)
+    for b in list(range(0x7F70, 0x7F90)) + list(range(0xFF70, 0xFF90)) + [0, 0x8000, 0x7FFF, 0xFFFF]:
+        assert orc.is_nan(b) == bool(ref[b]), f"is_nan({b:#06x})"
+
+
+# ---------------------------------------------------------- block key pins
+def pin_block_key_max(orc):
+    """Non-NaN blocks without zeros: the block key is the key of the float
+    maximum (numpy argmax over float values)."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    for _ in range(400):
+        bits = rng.integers(0, 1 << 16, size=8).astype(np.uint16)
+        vals = bf16_to_f32(bits)
+        if np.isnan(vals).any() or (vals == 0).any():
+            continue
+        mx = bits[int(np.argmax(vals))]
+        assert orc.block_key(bits) == int(orc.key(np.array([mx], np.uint16))[0]), \
+            f"block max of {bits}"
+
+
+def pin_block_key_nan(orc):
+    """A block holding a NaN of either sign, anywhere, is the canonical
+    positive NaN (key 0xFFFF) -- the reading taken of NaN propagation."""
+    rng = np.random.Generator(np.random.PCG64(12))
+    for nanbits in (0x7FC0, 0xFFC0, 0x7F81, 0xFFFF, 0x7FFF, 0xFF81):
+        for pos in range(8):
+            bits = rng.integers(0x0000, 0x7F00, size=8).astype(np.uint16)
+            bits[pos] = nanbits
+            assert orc.block_key(bits) == 0xFFFF, f"NaN block {bits}"
+
+
+def pin_block_key_special(orc):
+    """Closed forms: all -inf -> key(-inf); +0 beats -0; all -0 -> key(-0)."""
+    assert orc.block_key([0xFF80] * 8) == 0x007F
+    assert orc.block_key([0x8000] * 7 + [0x0000]) == 0x8000
+    assert orc.block_key([0x8000] * 8) == 0x7FFF
+    assert orc.block_key([0xFF80] * 7 + [0xBF80]) == 0x407F     # -1.0 beats -inf
+
+
+def pin_row_keys_block(orc):
+    """Block rows: n = ceil(v/8), the newest block keyed as +inf whatever it
+    holds, the others keyed from their 8 logits."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    row = rng.integers(0, 1 << 16, size=64).astype(np.uint16)
+    row[56:64] = 0xFF80                               # an all -inf block
+    for v in (1, 7, 8, 9, 23, 24, 57, 64):
+        keys = orc.row_keys(row, v, BLOCK)
+        n = (v + 7) // 8
+        assert keys.size == n, f"v={v}: n={keys.size}, expected {n}"
+        assert keys[-1] == 0xFF80, f"v={v}: newest block not pinned"
+        for b in range(n - 1):
+            assert keys[b] == orc.block_key(row[8 * b:8 * b + 8]), f"v={v} block {b}"
+
+
+# --------------------------------------------------------- selection pins
+def _valid_topk_sets(keys, k):
+    """All index sets S, |S| = k, with no unselected key above a selected one."""
+    n = keys.size
+    sets = []
+    for S in itertools.combinations(range(n), k):
+        sel = keys[list(S)]
+        rest = np.delete(keys, list(S))
+        if rest.size == 0 or sel.min() >= rest.max():
+            sets.append(frozenset(S))
+    return sets
+
+
+def pin_bruteforce_tiny_rows(orc):
+    """Every n <= 9, k < n: the oracle's index set is one of the valid top-k
+    sets found by enumerating all k-subsets, in both modes."""
+    rng = np.random.Generator(np.random.PCG64(14))
+    alphabets = [
+        None,                                               # any pattern
+        np.array([0x3F80, 0xBF80, 0x0000, 0x8000], np.uint16),    # ties, +/-0
+        np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x4000], np.uint16),  # NaN, inf
+    ]
+    for trial in range(90):
+        n = 2 + trial % 8
+        alpha = alphabets[trial % 3]
+        if alpha is None:
+            row = rng.integers(0, 1 << 16, size=n).astype(np.uint16)
+        else:
+            row = alpha[rng.integers(0, alpha.size, size=n)]
+        keys = orc.row_keys(row, n, TOKEN)
+        for k in range(1, n):
+            out = orc.topk_row(row, n, k, TOKEN)
+            valid = _valid_topk_sets(keys, k)
+            assert frozenset(out.tolist()) in valid, f"token row {row}, k={k}: {out}"
+    for trial in range(40):
+        nb = 2 + trial % 6
+        row = rng.integers(0, 1 << 16, size=8 * nb).astype(np.uint16)
+        if trial % 2:
+            row[rng.integers(0, 8 * nb, size=3)] = 0xFF80
+            row[8 * (trial % (nb - 1)): 8 * (trial % (nb - 1)) + 8] = 0xFF80
+        keys = orc.row_keys(row, 8 * nb, BLOCK)
+        for k in range(1, nb):
+            out = orc.topk_row(row, 8 * nb, k, BLOCK)
+            sel = out[out >= 0]
+            nneg = int((out < 0).sum())
+            assert not (keys[sel] == 0x007F).any(), "a -inf block kept its index"
+            # -1 entries stand for selected -inf blocks: complete the set with
+            # the -inf blocks the row holds (any choice is equally valid).
+            infb = [b for b in range(nb) if keys[b] == 0x007F and b not in sel]
+            full = set(sel.tolist()) | set(infb[:nneg])
+            assert len(full) == k, f"block row k={k}: {out}"
+            assert frozenset(full) in _valid_topk_sets(keys, k), f"block row k={k}: {out}"
+
+
+def pin_threshold_by_numpy_sort(orc):
+    """numpy's sort gives the k-th key; the oracle's T, counts and selection
+    agree: count(key > T) < k <= count(key >= T), selected >= T >= unselected."""
+    rng = np.random.Generator(np.random.PCG64(15))
+    for trial in range(30):
+        n = int(rng.integers(20, 3000))
+        k = int(rng.integers(1, n))
+        if trial % 3 == 0:
+            row = rng.integers(0, 1 << 16, size=n).astype(np.uint16)
+        elif trial % 3 == 1:
+            row = rng.choice(np.array([0x3F80, 0x4000, 0xBF80, 0x0000, 0x8000], np.uint16), n)
+        else:
+            row = rng.integers(0x3F00, 0x3F20, size=n).astype(np.uint16)
+        keys = orc.row_keys(row, n, TOKEN)
+        T_np = int(np.sort(keys)[n - k])
+        res = orc.threshold(keys, k)
+        assert res is not None
+        T, gt, eq = res
+        assert T == T_np, f"T {T:#x} != numpy {T_np:#x}"
+        assert gt == int((keys > T).sum()) and eq == int((keys == T).sum())
+        assert gt < k <= gt + eq
+        out = orc.topk_row(row, n, k, TOKEN)
+        sel = np.zeros(n, bool)
+        sel[out] = True
+        assert sel.sum() == k, "indices not distinct"
+        assert keys[sel].min() >= T and (keys[~sel].max() if (~sel).any() else 0) <= T
+
+
+def pin_values_match_numpy_topk(orc):
+    """NaN-free, zero-free rows: the selected values are the k largest float
+    values (numpy sort of float32), as a multiset."""
+    rng = np.random.Generator(np.random.PCG64(16))
+    for n, k in ((16384, 512), (16384, 2048), (5000, 700), (100, 99)):
+        f = rng.standard_normal(n, dtype=np.float32)
+        f[f == 0] = 1.0
+        bits = ((f.view(np.uint32) + 0x8000) >> 16).astype(np.uint16)
+        vals = bf16_to_f32(bits)
+        assert not np.isnan(vals).any()
+        out = orc.topk_row(bits, n, k, TOKEN)
+        assert np.array_equal(np.sort(vals[out]), np.sort(vals)[n - k:]), f"n={n} k={k}"
+
+
+# ------------------------------------------------------ closed-form pins
+def pin_short_rows(orc):
+    """n <= k: 0..n-1 in order then -1 (token); no logits consulted."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    row = rng.integers(0, 1 << 16, size=100).astype(np.uint16)
+    for v, k in ((0, 5), (1, 1), (5, 5), (5, 9), (100, 100), (37, 512)):
+        out = orc.topk_row(row, v, k, TOKEN)
+        exp = list(range(min(v, k))) + [-1] * (k - min(v, k))
+        assert out.tolist() == exp, f"v={v} k={k}"
+
+
+def pin_clamped_lengths(orc):
+    """valid_len below 0 acts as 0, above the width as the width."""
+    rng = np.random.Generator(np.random.PCG64(18))
+    row = rng.integers(0, 0x7F00, size=40).astype(np.uint16)
+    assert orc.topk_row(row, -5, 4, TOKEN).tolist() == [-1] * 4
+    assert orc.topk_row(row, -5, 4, BLOCK).tolist() == [-1] * 4
+    a = orc.topk_row(row, 1000, 7, TOKEN)
+    b = orc.topk_row(row, 40, 7, TOKEN)
+    assert sorted(a.tolist()) == sorted(b.tolist())
+
+
+def pin_constant_row(orc):
+    """A constant row: any k distinct indices (all keys equal)."""
+    for bits in (0x3F80, 0xFF80, 0x8000, 0x7FC0):
+        row = np.full(333, bits, np.uint16)
+        out = orc.topk_row(row, 333, 100, TOKEN)
+        assert len(set(out.tolist())) == 100 and out.min() >= 0 and out.max() < 333
+
+
+def pin_block_neg_inf_rows(orc):
+    """Block rows of -inf blocks: n > k gives the pinned newest block and
+    k-1 entries of -1; n <= k gives -1 for every -inf block, the newest kept."""
+    row = np.full(8 * 50, 0xFF80, np.uint16)
+    out = orc.topk_row(row, 400, 10, BLOCK)
+    assert sorted(out.tolist()) == [-1] * 9 + [49]
+    out = orc.topk_row(row, 400, 60, BLOCK)
+    assert out.tolist() == [-1] * 49 + [49] + [-1] * 10
+    row[8 * 3] = 0x3F80                       # block 3 holds a 1.0
+    out = orc.topk_row(row, 400, 2, BLOCK)
+    assert sorted(out.tolist()) == [3, 49]
+
+
+def pin_poison_not_selected(orc):
+    """Logits past valid_len (poisoned with +NaN, the top key) never appear."""
+    rng = np.random.Generator(np.random.PCG64(19))
+    row = rng.integers(0, 0x7F00, size=512).astype(np.uint16)
+    for v in (3, 100, 257, 511):
+        row2 = row.copy()
+        row2[v:] = 0x7FFF
+        out = orc.topk_row(row2, v, 2, TOKEN)
+        assert out.max() < v
+        outb = orc.topk_row(row2, v, 2, BLOCK)
+        assert outb.max() < (v + 7) // 8
+
+
+def pin_page_transform_roundtrip(orc):
+    """Inverting the permuted block table recovers the untransformed result."""
+    rng = np.random.Generator(np.random.PCG64(20))
+    width, P = 4096, 64
+    pages = rng.permutation(width // P).astype(np.int32)
+    inv = np.empty_like(pages)
+    inv[pages] = np.arange(pages.size, dtype=np.int32)
+    row = rng.integers(0, 0x7F00, size=width).astype(np.uint16)
+    for v, k in ((4096, 512), (3000, 100), (77, 100)):
+        plain = orc.topk_row(row, v, k, TOKEN)
+        mapped = orc.topk_row(row, v, k, TOKEN, pages=pages, page_size=P)
+        back = np.where(mapped >= 0, inv[np.maximum(mapped, 0) // P] * P + mapped % P, -1)
+        assert np.array_equal(back, plain), f"v={v} k={k}"
+
+
+def pin_worked_examples(orc):
+    """Hand-worked rows (golden/worked_examples.txt)."""
+    with open(os.path.join(GOLDEN, "worked_examples.txt")) as f:
+        for line in f:
+            if line.lstrip().startswith("#") or not line.strip():
+                continue
+            name, mode, v, k, P, pages, bits, kind, exp = [s.strip() for s in line.split("|")]
+            mode = TOKEN if mode == "token" else BLOCK
+            row = np.array([int(b, 16) for b in bits.split(",")], np.uint16)
+            pg = None if pages == "-" else np.array([int(p) for p in pages.split(",")], np.int32)
+            out = orc.topk_row(row, int(v), int(k), mode, pages=pg,
+                               page_size=int(P) if pg is not None else 64)
+            expected = [int(e) for e in exp.split(",")]
+            if kind == "set":
+                assert sorted(out.tolist()) == sorted(expected), f"{name}: {out.tolist()}"
+            else:
+                assert out.tolist() == expected, f"{name}: {out.tolist()}"
+
+
+ALL_PINS = [
+    pin_key_fixed_points,
+    pin_key_bijection,
+    pin_key_follows_float_order,
+    pin_key_nan_placement,
+    pin_is_nan,
+    pin_block_key_max,
+    pin_block_key_nan,
+    pin_block_key_special,
+    pin_row_keys_block,
+    pin_bruteforce_tiny_rows,
+    pin_threshold_by_numpy_sort,
+    pin_values_match_numpy_topk,
+    pin_short_rows,
+    pin_clamped_lengths,
+    pin_constant_row,
+    pin_block_neg_inf_rows,
+    pin_poison_not_selected,
+    pin_page_transform_roundtrip,
+    pin_worked_examples,
+]
+
+
+def failing_pins(orc):
+    """Names of the pins this oracle fails (crashes count as failures)."""
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001
+            bad.append(f"{pin.__name__}: {type(e).__name__}: {e}"[:200])
+    return bad
+
+
+if __name__ == "__main__":
+    # python oracle_pins.py <library>: run every pin against one compiled copy
+    # of the oracle; exit status 0 when all pass, 1 when any fails.
+    import sys
+
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import oracle as _oracle
+
+    failures = failing_pins(_oracle.Oracle(sys.argv[1]))
+    for line in failures:
+        print(line)
+    sys.exit(1 if failures else 0)

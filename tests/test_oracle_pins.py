@@ -1,0 +1,65 @@
+"""The CPU oracle against its pins, and the pins against planted mistakes.
+
+A planted mistake is a one-line change to a temporary copy of
+oracle/topk_oracle.c, compiled on the CPU; the real oracle is untouched.
+Every such copy must fail at least one pin.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(orc, pin):
+    pin(orc)
+
+
+# (description, exact text in topk_oracle.c, replacement)
+MUTANTS = [
+    ("negative key flips 15 bits", "return (uint16_t)(bits ^ 0xFFFFu);",
+     "return (uint16_t)(bits ^ 0x7FFFu);"),
+    ("positive key not flipped", "return (uint16_t)(bits ^ 0x8000u);",
+     "return (uint16_t)(bits);"),
+    ("sign test inverted", "if (bits & 0x8000u)\n        return (uint16_t)(bits ^ 0xFFFFu);",
+     "if (!(bits & 0x8000u))\n        return (uint16_t)(bits ^ 0xFFFFu);"),
+    ("ascending sort", "return a->key > b->key ? -1 : 1;", "return a->key > b->key ? 1 : -1;"),
+    ("newest block not pinned", "keys[n - 1] = oracle_key(0x7F80u);",
+     "keys[n - 1] = oracle_block_key(row + (int64_t)8 * (n - 1));"),
+    ("-inf blocks keep their index", "out[j] = -1;\n    for (j = cnt",
+     "out[j] = out[j];\n    for (j = cnt"),
+    ("block count floors", "return (v + 7) / 8;", "return v / 8;"),
+    ("page offset dropped", "* page_size + out[j] % page_size;", "* page_size;"),
+    ("page index by offset", "pages[out[j] / page_size]", "pages[out[j] % page_size]"),
+    ("NaN ignored in block max", "return oracle_key(0x7FFFu);", "break;"),
+    ("inf counted as NaN", "((bits & 0x007Fu) != 0u)", "1"),
+    ("no upper clamp", "if (v > width)\n        return width;", "if (v > width)\n        return v - 0;"),
+    ("k-th is one off", "t = items[k - 1].key;", "t = items[k].key;"),
+    ("short rows use <", "if (n <= k) {\n        for (j = 0; j < n; ++j)",
+     "if (n < k) {\n        for (j = 0; j < n; ++j)"),
+    ("block max keeps first", "if (k > best)\n            best = k;", "if (k < best)\n            best = k;"),
+    ("tie count includes >", "else if (keys[i] == t)", "if (keys[i] >= t)"),
+]
+
+
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, desc, old, new):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {desc}"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.compile_source(str(path), str(tmp_path / "libmutant.so"))
+    # In a child process: a mutant may corrupt memory (e.g. a missing clamp).
+    pins = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_pins.py")
+    res = subprocess.run([sys.executable, pins, lib], capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode != 0, f"no pin catches the planted mistake: {desc}"
