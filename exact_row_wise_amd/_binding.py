@@ -1,0 +1,167 @@
+"""ctypes binding of libtopk (argument marshalling only).
+
+``topk_bf16_rows`` mirrors the C entry point of the same name in
+``include/libtopk.h``: it checks that the tensors are on the GPU with the
+right dtype and layout, passes their device pointers, sizes and the
+current HIP stream, and raises on a non-zero status.  Every step of the
+selection runs in the HIP kernels of libtopk.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # loaded first: libtopk then shares torch's HIP runtime
+
+MODE_TOKEN = 0
+MODE_BLOCK = 1
+
+PATH_SHORT = 0
+PATH_SAMPLED = 1
+PATH_SAMPLED_TIES = 2
+PATH_DIRECT_FORCED = 3
+PATH_DIRECT_MISJUDGED = 4
+PATH_DIRECT_OVERFLOW = 5
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "libtopk.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class TopkError(RuntimeError):
+    """A non-zero status from libtopk."""
+
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"libtopk status {status}: {detail}")
+        self.status = status
+
+
+class _BlockTable(ctypes.Structure):
+    _fields_ = [("pages", ctypes.c_void_p), ("row_stride", ctypes.c_int64),
+                ("page_size", ctypes.c_int32)]
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("force_direct", ctypes.c_int32), ("path_codes", ctypes.c_void_p)]
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def library():
+    """Load libtopk.so (built in-tree by ``python -m exact_row_wise_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB):
+            raise ImportError(
+                f"{_LIB} is missing: build it with `python -m exact_row_wise_amd.build`")
+        lib = ctypes.CDLL(_LIB)
+        sig = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+               ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_BlockTable),
+               ctypes.c_void_p]
+        lib.topk_bf16_rows.argtypes = sig + [ctypes.c_void_p]
+        lib.topk_bf16_rows.restype = ctypes.c_int
+        lib.topk_bf16_rows_ex.argtypes = sig + [ctypes.POINTER(_Options), ctypes.c_void_p]
+        lib.topk_bf16_rows_ex.restype = ctypes.c_int
+        lib.topk_status_string.argtypes = [ctypes.c_int]
+        lib.topk_status_string.restype = ctypes.c_char_p
+        lib.topk_last_error.argtypes = []
+        lib.topk_last_error.restype = ctypes.c_char_p
+        lib.topk_release_scratch.argtypes = []
+        lib.topk_release_scratch.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return library().topk_status_string(int(status)).decode()
+
+
+def release_scratch() -> None:
+    rc = library().topk_release_scratch()
+    if rc != 0:
+        raise TopkError(rc, library().topk_last_error().decode())
+
+
+def _mode(mode) -> int:
+    if mode in (MODE_TOKEN, "token"):
+        return MODE_TOKEN
+    if mode in (MODE_BLOCK, "block"):
+        return MODE_BLOCK
+    return int(mode)  # passed through; the library rejects unknown modes
+
+
+def topk_bf16_rows(logits: torch.Tensor, valid_len: torch.Tensor, k: int, mode=MODE_TOKEN,
+                   block_table: torch.Tensor | None = None, page_size: int = 64,
+                   out: torch.Tensor | None = None, width: int | None = None,
+                   force_direct: bool = False, path_codes: torch.Tensor | None = None,
+                   stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """Exact top-k indices of every row (see include/libtopk.h).
+
+    logits      [rows, >= width] BF16 (or int16/uint16 bit patterns) on the
+                GPU; unit stride along a row, the row stride a multiple of 8
+                elements, 16-byte aligned
+    valid_len   int32 [rows] on the GPU
+    k           1 .. 2048
+    mode        "token"/0 or "block"/1
+    block_table optional int32 [rows, >= ceil(width / page_size)] on the GPU
+    out         optional int32 [rows, k] contiguous on the GPU (allocated if None)
+    width       logits per row (default: logits.shape[1])
+    force_direct, path_codes   test hooks of topk_bf16_rows_ex
+    stream      torch stream (default: the current stream)
+    Returns out.
+    """
+    lib = library()
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [rows, row_stride]")
+    if logits.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("logits must be bfloat16 (or 16-bit integer bit patterns)")
+    rows = logits.shape[0]
+    if width is None:
+        width = logits.shape[1]
+    if logits.shape[1] > 1 and logits.stride(1) != 1:
+        raise ValueError("logits rows must have unit stride")
+    row_stride = logits.stride(0)
+    if valid_len.dtype != torch.int32 or valid_len.numel() != rows:
+        raise ValueError("valid_len must be int32 [rows]")
+    dev = logits.device
+    if dev.type != "cuda" or valid_len.device != dev:
+        raise ValueError("logits and valid_len must be on the same GPU")
+    valid_len = valid_len.contiguous()
+    if out is None:
+        out = torch.empty((rows, int(k)), dtype=torch.int32, device=dev)
+    elif (out.dtype != torch.int32 or tuple(out.shape) != (rows, int(k))
+          or not out.is_contiguous() or out.device != dev):
+        raise ValueError("out must be a contiguous int32 [rows, k] tensor on the same GPU")
+    bt = None
+    if block_table is not None:
+        if (block_table.dtype != torch.int32 or block_table.dim() != 2
+                or block_table.device != dev or block_table.shape[0] != rows
+                or (rows > 0 and block_table.stride(1) != 1)):
+            raise ValueError("block_table must be int32 [rows, pages] on the same GPU")
+        bt = _BlockTable(block_table.data_ptr(), block_table.stride(0), int(page_size))
+    opts = None
+    if force_direct or path_codes is not None:
+        if path_codes is not None and (path_codes.dtype != torch.int32
+                                       or path_codes.numel() != rows
+                                       or path_codes.device != dev):
+            raise ValueError("path_codes must be int32 [rows] on the same GPU")
+        opts = _Options(1 if force_direct else 0,
+                        path_codes.data_ptr() if path_codes is not None else None)
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        args = (logits.data_ptr(), int(row_stride), valid_len.data_ptr(), int(rows),
+                int(width), int(k), _mode(mode), ctypes.byref(bt) if bt is not None else None,
+                out.data_ptr())
+        if opts is None:
+            rc = lib.topk_bf16_rows(*args, ctypes.c_void_p(s.cuda_stream))
+        else:
+            rc = lib.topk_bf16_rows_ex(*args, ctypes.byref(opts), ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise TopkError(rc, lib.topk_last_error().decode())
+    return out

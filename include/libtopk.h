@@ -1,0 +1,146 @@
+/*
+ * libtopk.h -- exact per-row top-k of BF16 logits on AMD Instinct MI355X
+ * (gfx950).  Plain C ABI: no C++ types, no exceptions, no torch types.
+ *
+ * What is computed (vLLM API page "vllm.models.deepseek_v41.nvidia.
+ * specialized_decode.attention.decode_topk_cute", module docstring,
+ * paragraph "What this module computes"):
+ *
+ *   For each row r, with v = valid_len[r] clamped to [0, width]:
+ *   - TOPK_MODE_TOKEN: the row has n = v elements, element i is logit i.
+ *   - TOPK_MODE_BLOCK: the row has n = ceil(v / 8) elements; element b is
+ *     the NaN-propagating maximum of logits 8b .. 8b+7, except the newest
+ *     element n-1, which counts as +inf whatever it holds.  A block holding
+ *     a NaN evaluates to the canonical positive NaN.
+ *   Elements are compared through the order-preserving 16-bit key of their
+ *   BF16 bits, key(x) = x ^ (x has its sign bit set ? 0xFFFF : 0x8000)
+ *   (sglang PR #39305, section "What is kept from DeepSelect"), so the
+ *   selection is exact: positive NaNs rank above +inf, negative NaNs below
+ *   -inf, -0 just below +0.
+ *   - n >  k: out[r] holds, in no particular order, the indices of k
+ *     elements such that no unselected element has a larger key (every key
+ *     above the k-th largest, then enough keys equal to it).
+ *   - n <= k: out[r] = 0, 1, ..., n-1, then -1 up to k.  Token rows with
+ *     n <= k read no logits (vLLM kimi_k3 indexer page, IndexerSelect,
+ *     short-context bypass).
+ *   - Block mode writes -1 in place of every selected block whose key is
+ *     that of -inf.
+ *   - With a block table, every index i >= 0 is written as
+ *     pages[r][i >> log2(P)] * P + (i & (P - 1)), P = page_size (vLLM
+ *     kimi_k3 indexer page, IndexerSelect.emit); -1 stays -1.
+ *
+ * Layout and ownership.  Every pointer argument except block_table and
+ * options is device memory owned by the caller; the library never frees
+ * or retains it past the call.  logits is row-major [rows, row_stride]
+ * BF16 bit patterns, 16-byte aligned, row_stride a multiple of 8
+ * elements; valid_len is int32 [rows]; out is int32 [rows, k], row-major;
+ * pages is int32 [rows, pages_row_stride].
+ *
+ * Execution.  The call enqueues its kernels on `stream` (a hipStream_t;
+ * NULL = the default stream) and returns without waiting.  It allocates
+ * nothing on the hot path: rows wider than one workgroup's share use a
+ * per-(device, stream) scratch buffer that the library allocates and
+ * zeroes on first use for that stream (so the first call on a stream must
+ * not be under graph capture) and grows, after synchronizing that stream,
+ * when a larger call needs more.  Every launch leaves the scratch zeroed.
+ * Calls that overlap on one stream's scratch are serialized by the
+ * stream; calls on different streams get different scratch buffers.
+ *
+ * Errors.  Argument errors are reported before anything is enqueued, by
+ * a negative status; out is then untouched.  Values are never errors:
+ * valid_len outside [0, width] is clamped and NaNs are ordinary keys.
+ */
+#ifndef LIBTOPK_H
+#define LIBTOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TOPK_MAX_K 2048
+#define TOPK_MAX_WIDTH (1 << 20)
+
+enum topk_mode {
+    TOPK_MODE_TOKEN = 0, /* one element per logit */
+    TOPK_MODE_BLOCK = 1  /* one element per aligned group of 8 logits */
+};
+
+enum topk_status {
+    TOPK_OK = 0,
+    TOPK_ERR_INVALID_ARG = -1, /* null pointer, k outside [1, 2048], bad
+                                  mode, width outside [0, 2^20], rows < 0,
+                                  row_stride < width, bad block table */
+    TOPK_ERR_MISALIGNED = -2,  /* logits not 16-byte aligned, or
+                                  row_stride not a multiple of 8 */
+    TOPK_ERR_HIP = -3          /* a HIP runtime call or launch failed;
+                                  topk_last_error() has the detail */
+};
+
+/* Per-row path codes written when topk_options_t.path_codes is set. */
+enum topk_path {
+    TOPK_PATH_SHORT = 0,         /* n <= k: 0..n-1 then -1 */
+    TOPK_PATH_SAMPLED = 1,       /* sampled cutoff, k-th key above it */
+    TOPK_PATH_SAMPLED_TIES = 2,  /* sampled cutoff equal to the k-th key */
+    TOPK_PATH_DIRECT_FORCED = 3, /* direct radix, requested */
+    TOPK_PATH_DIRECT_MISJUDGED = 4, /* direct radix: fewer than k keys at
+                                       or above the sampled cutoff */
+    TOPK_PATH_DIRECT_OVERFLOW = 5   /* direct radix: more survivors above
+                                       the cutoff than the buffers hold */
+};
+
+/* Optional block table of the page transform (host struct; `pages` is a
+ * device pointer). */
+typedef struct topk_block_table {
+    const int32_t *pages;     /* device int32 [rows, row_stride]          */
+    int64_t row_stride;       /* entries between rows; >= ceil(width/P)   */
+    int32_t page_size;        /* P: tokens per page, a power of two >= 1  */
+} topk_block_table_t;
+
+/* Test and diagnosis options (host struct). */
+typedef struct topk_options {
+    int32_t force_direct;     /* 1: every row takes the direct radix path */
+    int32_t *path_codes;      /* device int32 [rows] or NULL: topk_path   */
+} topk_options_t;
+
+/* Exact top-k of every row (see above).
+ *   logits       device BF16 bits [rows, row_stride], 16-byte aligned
+ *   row_stride   elements between rows; multiple of 8; >= width
+ *   valid_len    device int32 [rows]; clamped to [0, width]
+ *   rows         >= 0 (0: nothing is enqueued)
+ *   width        logits per row, 0 .. 2^20
+ *   k            1 .. 2048
+ *   mode         TOPK_MODE_TOKEN or TOPK_MODE_BLOCK
+ *   block_table  host pointer to a table descriptor, or NULL
+ *   out          device int32 [rows, k]
+ *   stream       hipStream_t, NULL for the default stream
+ * Returns TOPK_OK or a negative topk_status. */
+int topk_bf16_rows(const uint16_t *logits, int64_t row_stride,
+                   const int32_t *valid_len, int32_t rows, int32_t width,
+                   int32_t k, int32_t mode,
+                   const topk_block_table_t *block_table, int32_t *out,
+                   void *stream);
+
+/* topk_bf16_rows with test and diagnosis options (NULL = none). */
+int topk_bf16_rows_ex(const uint16_t *logits, int64_t row_stride,
+                      const int32_t *valid_len, int32_t rows, int32_t width,
+                      int32_t k, int32_t mode,
+                      const topk_block_table_t *block_table, int32_t *out,
+                      const topk_options_t *options, void *stream);
+
+/* A static string naming a status code. */
+const char *topk_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char *topk_last_error(void);
+
+/* Release every scratch buffer the library holds (synchronizes the
+ * streams they belong to).  Optional; for tests and clean shutdown. */
+int topk_release_scratch(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBTOPK_H */

@@ -1,0 +1,71 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point the
+header declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_row_wise_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libtopk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(topk_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert "topk_bf16_rows" in names and "topk_status_string" in names
+    assert len(names) >= 5
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(T.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libtopk.so does not export {name}"
+
+
+def test_status_strings():
+    assert T.status_string(0) == "ok"
+    for s in (-1, -2, -3):
+        assert T.status_string(s) and T.status_string(s) != "unknown status"
+    assert T.status_string(12345) == "unknown status"
+
+
+def _call(**kw):
+    lib = T.library()
+    a = dict(logits=16, row_stride=16, valid_len=64, rows=4, width=16, k=8, mode=0,
+             bt=None, out=128, stream=None)
+    a.update(kw)
+    return lib.topk_bf16_rows(a["logits"], a["row_stride"], a["valid_len"], a["rows"],
+                              a["width"], a["k"], a["mode"], a["bt"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), -1), (dict(k=2049), -1), (dict(mode=2), -1), (dict(rows=-1), -1),
+    (dict(width=-1), -1), (dict(width=(1 << 20) + 8, row_stride=(1 << 20) + 8), -1),
+    (dict(row_stride=8), -1), (dict(row_stride=20), -2), (dict(logits=None), -1),
+    (dict(valid_len=None), -1), (dict(out=None), -1), (dict(logits=24), -2),
+    (dict(out=130), -2),
+])
+def test_rejects_bad_arguments(kw, status):
+    assert _call(**kw) == status
+    assert T.library().topk_last_error()
+
+
+def test_rows_zero_is_a_noop():
+    assert _call(rows=0, logits=None, valid_len=None, out=None) == 0
+
+
+def test_bad_block_table():
+    bt = T._binding._BlockTable(None, 1, 64)
+    assert _call(bt=ctypes.pointer(bt)) == -1
+    bt = T._binding._BlockTable(256, 1, 48)          # not a power of two
+    assert _call(bt=ctypes.pointer(bt)) == -1
+    bt = T._binding._BlockTable(256, 0, 8)           # rows too short for width 16
+    assert _call(bt=ctypes.pointer(bt)) == -1

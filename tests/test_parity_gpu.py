@@ -1,0 +1,242 @@
+"""GPU parity: libtopk (through its C ABI) against the CPU oracle.
+
+Every workload runs at full size with every row checked, plus reduced and
+edge-case shapes; the direct radix path is exercised both on request and on
+rows built to defeat the sampled cutoff.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from checker import check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+T = None
+
+
+def setup_module(module):
+    global T
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_row_wise_amd as _T
+    T = _T
+    T.library()
+
+
+def _dev(d):
+    L = torch.from_numpy(np.ascontiguousarray(d["logits"]).view(np.int16)).cuda()
+    VL = torch.from_numpy(np.ascontiguousarray(d["valid_len"])).cuda()
+    P = None if d.get("pages") is None else torch.from_numpy(np.ascontiguousarray(d["pages"])).cuda()
+    return L, VL, P
+
+
+def run_gpu(d, force_direct=False, stream=None):
+    L, VL, P = _dev(d)
+    rows = L.shape[0]
+    pc = torch.full((rows,), -9, dtype=torch.int32, device="cuda")
+    out = T.topk_bf16_rows(L, VL, d["k"], d["mode"], block_table=P,
+                           page_size=d.get("page_size") or 64, width=d["width"],
+                           force_direct=force_direct, path_codes=pc, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), pc.cpu().numpy()
+
+
+def run_oracle(d):
+    return oracle.topk(d["logits"], d["valid_len"], d["k"], d["mode"], width=d["width"],
+                       pages=d.get("pages"), page_size=d.get("page_size") or 64, threads=16)
+
+
+def assert_parity(d, g, o):
+    bad = check(oracle.default(), d, g, o)
+    assert not bad, "\n".join(bad)
+
+
+def _paths(pc):
+    u, c = np.unique(pc, return_counts=True)
+    return dict(zip(u.tolist(), c.tolist()))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_workload_full_size(cfg):
+    d = W.make(cfg)
+    print(f"workload {cfg} {d['name']} rows={d['logits'].shape[0]}", flush=True)
+    g, pc = run_gpu(d)
+    o = run_oracle(d)
+    assert_parity(d, g, o)
+    paths = _paths(pc)
+    print("paths", paths, flush=True)
+    assert -9 not in paths
+    fallback = paths.get(T.PATH_DIRECT_MISJUDGED, 0) + paths.get(T.PATH_DIRECT_OVERFLOW, 0)
+    assert fallback <= max(1, d["logits"].shape[0] // 100), paths
+
+
+@pytest.mark.parametrize("cfg,rows,width", [(1, 4, 16384), (2, 64, 16384), (3, 8, 150000),
+                                            (4, 6, 1048576), (5, 160, 16384)])
+def test_workload_direct_path(cfg, rows, width):
+    d = W.make(cfg, rows=rows, width=width, seed=100 + cfg)
+    g, pc = run_gpu(d, force_direct=True)
+    assert_parity(d, g, run_oracle(d))
+    n = np.minimum(np.maximum(d["valid_len"], 0), width)
+    if d["mode"] == 1:
+        n = (n + 7) // 8
+    long_rows = n > d["k"]
+    assert np.all(pc[long_rows] == T.PATH_DIRECT_FORCED)
+    assert np.all(pc[~long_rows] == T.PATH_SHORT)
+
+
+def _random_rows(rng, rows, width, kind):
+    if kind == "normal":
+        x = rng.standard_normal((rows, width), dtype=np.float32)
+        return W.f32_to_bf16_bits(x)
+    if kind == "bits":
+        return rng.integers(0, 1 << 16, size=(rows, width), dtype=np.uint32).astype(np.uint16)
+    if kind == "ties":
+        lv = np.array([0x3F80, 0x4000, 0xBF80, 0x0000, 0x8000, 0xFF80, 0x7F80], np.uint16)
+        return lv[rng.integers(0, lv.size, size=(rows, width))]
+    raise ValueError(kind)
+
+
+def _make(rng, rows, width, k, mode, kind, stride_pad=0, lens=None, pages=False):
+    stride = (width + 7) // 8 * 8 + 8 * stride_pad
+    L = np.full((rows, stride), W.POISON, np.uint16)
+    L[:, :width] = _random_rows(rng, rows, width, kind)
+    if lens is None:
+        lens = np.full(rows, width, np.int32)
+    lens = np.asarray(lens, np.int32)
+    for r in range(rows):
+        v = max(0, min(int(lens[r]), width))
+        L[r, v:] = W.POISON
+    P = None
+    if pages:
+        npg = (width + 63) // 64
+        P = np.stack([rng.permutation(npg) for _ in range(rows)]).astype(np.int32)
+    return dict(logits=L, valid_len=lens, k=k, mode=mode, width=width, pages=P,
+                page_size=64 if pages else 0, name="edge")
+
+
+EDGE = [
+    # (width, k, mode, kind, stride_pad)
+    (1, 1, 0, "bits", 0), (7, 3, 0, "bits", 1), (9, 8, 0, "normal", 0), (100, 1, 0, "ties", 0),
+    (1000, 999, 0, "bits", 0), (2049, 2048, 0, "normal", 0), (5000, 17, 0, "ties", 2),
+    (16384, 2048, 0, "bits", 0), (16385, 512, 0, "normal", 0), (16392, 100, 0, "ties", 0),
+    (40000, 1, 0, "normal", 0), (70001, 2048, 0, "bits", 3),
+    (8, 1, 1, "bits", 0), (17, 2, 1, "bits", 0), (800, 50, 1, "ties", 0),
+    (32768, 2048, 1, "normal", 0), (32776, 1024, 1, "bits", 0), (100001, 7, 1, "normal", 1),
+    (300000, 2048, 1, "ties", 0),
+]
+
+
+@pytest.mark.parametrize("width,k,mode,kind,pad", EDGE)
+def test_edge_shapes(width, k, mode, kind, pad):
+    rng = np.random.Generator(np.random.PCG64(width * 7 + k + 13 * mode))
+    rows = 6
+    lens = [width, width - 1, max(0, width // 3), -5, width + 100, k]
+    d = _make(rng, rows, width, k, mode, kind, stride_pad=pad, lens=lens, pages=(width % 2 == 0))
+    print(f"edge width={width} k={k} mode={mode} kind={kind}", flush=True)
+    for fd in (False, True):
+        g, pc = run_gpu(d, force_direct=fd)
+        assert_parity(d, g, run_oracle(d))
+
+
+def test_block_mode_specials():
+    """NaN blocks (either sign) above the pinned block, -inf blocks as -1,
+    +0/-0 blocks, partial newest block."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    width, k = 8 * 6000, 600
+    rows = 4
+    L = W.f32_to_bf16_bits(rng.standard_normal((rows, width), dtype=np.float32))
+    B = L.reshape(rows, -1, 8)
+    nb = B.shape[1]
+    B[0, rng.choice(nb, 300, replace=False), 3] = 0xFFC0      # -NaN in 300 blocks
+    B[1, rng.choice(nb, 700, replace=False), :] = 0xFF80      # 700 -inf blocks
+    B[2, :, :] = 0xFF80                                        # all -inf
+    B[2, rng.choice(nb, 100, replace=False), 5] = 0x8000      # some -0 blocks
+    B[3, :, :] = 0x8000
+    B[3, rng.choice(nb, 50, replace=False), 0] = 0x0000        # +0 beats -0
+    d = dict(logits=L, valid_len=np.array([width, width - 3, width, 8 * 700 + 5], np.int32),
+             k=k, mode=1, width=width, pages=None, page_size=0)
+    for fd in (False, True):
+        g, pc = run_gpu(d, force_direct=fd)
+        assert_parity(d, g, run_oracle(d))
+
+
+def test_block_mode_page_transform():
+    rng = np.random.Generator(np.random.PCG64(78))
+    d = _make(rng, 5, 8 * 4000, 300, 1, "normal", lens=[32000, 31999, 100, 2400, 8 * 300],
+              pages=True)
+    g, _ = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+
+
+def _sampled_positions_wg(nvec):
+    """Positions the one-workgroup token kernel samples: element (j & 7) of
+    the vector in slot j, i.e. vector vid = j * 256 + t, element vid // 256."""
+    vid = np.arange(nvec)
+    return vid * 8 + (vid // 256) % 8
+
+
+def test_crafted_misjudged_row_takes_direct_path():
+    """Sampled positions hold the row's largest values and everything else is
+    lower, so fewer than k keys lie at or above the cutoff."""
+    width, k = 16384, 512
+    L = np.full((2, width), 0x3F00, np.uint16)                # 0.5 everywhere
+    pos = _sampled_positions_wg(width // 8)
+    L[:, pos] = (0x4000 + np.arange(pos.size) % 0x700).astype(np.uint16)
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_DIRECT_MISJUDGED), pc
+
+
+def test_crafted_overflow_row_takes_direct_path():
+    """Sampled positions hold the smallest values, so almost every other key
+    lies above the cutoff and the survivor regions overflow."""
+    rng = np.random.Generator(np.random.PCG64(79))
+    width, k = 16384, 512
+    L = W.f32_to_bf16_bits(np.abs(rng.standard_normal((2, width), dtype=np.float32)) + 1)
+    pos = _sampled_positions_wg(width // 8)
+    L[:, pos] = 0x3C00                                         # tiny positives
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_DIRECT_OVERFLOW), pc
+
+
+def test_team_scratch_reused_across_calls():
+    """Consecutive team launches on one stream see clean scratch."""
+    d = W.make(3, rows=16, width=150000, seed=300)
+    o = run_oracle(d)
+    for _ in range(3):
+        g, _ = run_gpu(d)
+        assert_parity(d, g, o)
+    d4 = W.make(4, rows=9, width=200000, seed=301)
+    g, _ = run_gpu(d4)
+    assert_parity(d4, g, run_oracle(d4))
+
+
+def test_side_stream():
+    d = W.make(2, rows=32, width=8192, seed=302)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g, _ = run_gpu(d, stream=s)
+    assert_parity(d, g, run_oracle(d))
+    d3 = W.make(3, rows=3, width=60000, seed=303)
+    with torch.cuda.stream(s):
+        g, _ = run_gpu(d3, stream=s)
+    assert_parity(d3, g, run_oracle(d3))
+
+
+def test_widest_rows():
+    """Rows of 2^20 logits in token mode (the widest team) and block mode."""
+    rng = np.random.Generator(np.random.PCG64(304))
+    for mode, k in ((0, 2048), (1, 2048), (0, 1)):
+        d = _make(rng, 2, 1 << 20, k, mode, "normal", lens=[1 << 20, 777777])
+        g, pc = run_gpu(d)
+        assert_parity(d, g, run_oracle(d))
