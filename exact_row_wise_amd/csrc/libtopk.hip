@@ -906,9 +906,14 @@ struct Scratch {
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
+// Team scratch: the control words of kTeamBatch rows first, at a fixed
+// place whatever the call (each launch leaves them zeroed for the next, so
+// they must never move or share bytes with a previous call's lists), then
+// the survivor lists of `rows` rows.
+size_t team_ctl_bytes() { return (size_t)kTeamBatch * sizeof(RowCtl); }
+
 size_t team_scratch_bytes(int rows, int capg) {
-  const size_t per = sizeof(RowCtl) + (size_t)capg * 8 + (size_t)TOPK_MAX_K * 4;
-  return (size_t)rows * per;
+  return team_ctl_bytes() + (size_t)rows * ((size_t)capg * 8 + (size_t)TOPK_MAX_K * 4);
 }
 
 int get_scratch(hipStream_t stream, size_t need, void** out) {
@@ -1022,8 +1027,8 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.lcw = kTeamLCW;
   p.capg = capg;
   p.ctl = reinterpret_cast<RowCtl*>(sp);
-  p.gt_list = reinterpret_cast<unsigned long long*>(sp + sizeof(RowCtl) * batch);
-  p.eq_list = reinterpret_cast<uint32_t*>(sp + sizeof(RowCtl) * batch + (size_t)capg * 8 * batch);
+  p.gt_list = reinterpret_cast<unsigned long long*>(sp + team_ctl_bytes());
+  p.eq_list = reinterpret_cast<uint32_t*>(sp + team_ctl_bytes() + (size_t)capg * 8 * batch);
   const size_t lds = lds_bytes(kTeamLCW, k);
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = (rows - r0) < batch ? (rows - r0) : batch;

@@ -210,7 +210,13 @@ def test_crafted_overflow_row_takes_direct_path():
 
 
 def test_team_scratch_reused_across_calls():
-    """Consecutive team launches on one stream see clean scratch."""
+    """Consecutive team launches on one stream see clean scratch, also when
+    a call has more rows than the one before it (regression: the control
+    words once moved with the row count and overlapped old survivor lists)."""
+    for rows in (2, 5):
+        d = W.make(3, rows=rows, width=40000, seed=299 + rows)
+        g, _ = run_gpu(d)
+        assert_parity(d, g, run_oracle(d))
     d = W.make(3, rows=16, width=150000, seed=300)
     o = run_oracle(d)
     for _ in range(3):
