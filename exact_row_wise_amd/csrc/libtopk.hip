@@ -10,17 +10,20 @@
 // Shape of the hot path (decode_topk_cute docstring, paragraph "How." and
 // its sampled and direct ways to the answer), re-planned for CDNA4:
 //   * every logit is read from HBM once, with 16-byte vector loads, into
-//     VGPRs, and turned into packed 16-bit keys there;
+//     VGPRs, and stays there as raw BF16 words;
 //   * a cutoff c is taken from a sample of the row: the q-th largest
 //     sample, q scaled from k with a margin so that at least k keys lie at
 //     or above c with overwhelming probability; two 8-bit LDS radix passes
-//     over the samples find it, and every wave reads the bins itself;
-//   * keys above c are compacted with one wave64 ballot and a lane-mask
-//     count per key into the wave's own region, so no key costs an atomic;
+//     over the sampled keys find it, and every wave reads the bins itself;
+//   * words holding a key above c are compacted, two logits per wave64
+//     ballot step, into the wave's own LDS region (ballot + lane-mask
+//     count, no atomic).  When c is the key of a non-negative value the
+//     test is a signed 16-bit compare of the raw bits, so the key transform
+//     is never applied to the whole row;
 //   * the exact k-th key T over the survivors takes one pass of a
-//     1024-bin LDS histogram of (key - c), which resolves T to the exact
-//     key whenever T - c <= 1024 (else two 8-bit passes); the indices are
-//     then written from per-wave counts, again without atomics;
+//     1024-bin LDS histogram of (key - c), which gives T itself whenever
+//     T - c <= 1024 (else two 8-bit passes); the indices are then written
+//     from per-wave counts, again without atomics;
 //   * rows whose k-th key equals the cutoff take the tie pass: every key
 //     above c, then the first keys equal to c;
 //   * a misjudged sample (fewer than k keys at or above c) or a survivor
@@ -30,9 +33,9 @@
 //     workgroups that share blockIdx % 8 (one XCD, one L2).  Every member
 //     derives the same cutoff from the same samples and writes its
 //     survivors to its own slice of global scratch; a second kernel, one
-//     workgroup per row, reads them after the kernel boundary and finishes
-//     the row.  No workgroup ever waits for another, no atomic or fence
-//     crosses workgroups, and the scratch needs no reset.
+//     1024-thread workgroup per row, reads them after the kernel boundary
+//     and finishes the row.  No workgroup ever waits for another, no atomic
+//     or fence crosses workgroups, and the scratch needs no reset.
 // There is no MFMA: this is a memory-bound selection, and all selection
 // arithmetic is on integer keys.
 
@@ -52,47 +55,50 @@
 
 namespace {
 
-constexpr int kNT = 256;                 // threads per workgroup (4 wave64)
-constexpr int kWaves = kNT / 64;
 constexpr int kCopies = 8;               // replicated bins of whole-row histograms
-constexpr int kTokenVPT = 8;             // 16-byte vectors per thread, token rows
-constexpr int kBlockVPT = 16;            // 16-byte vectors per thread, block rows
+constexpr int kTeamNT = 256;             // filter workgroup size
+constexpr int kSelNT = 1024;             // select workgroup size
+constexpr int kRowNT = 512;              // one-workgroup-per-row size
+constexpr int kTokenVPT = 8;             // 16-byte vectors per thread of a token member
+constexpr int kBlockVPT = 16;            // 16-byte vectors per thread of a block member
 constexpr int kTokenSV = 2;              // sample vectors per thread, token teams
 constexpr int kBlockSV = 4;              // sample vectors per thread, block teams
-constexpr int kTeamLCW = 1024;           // survivor slots per wave of a team member
+constexpr int kTeamLCW = 512;            // survivor entries per wave of a team member
+constexpr int kTieCapWave = TOPK_MAX_K / 4 + 64;  // tie indices per wave of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
 constexpr size_t kTeamScratchMax = size_t(256) << 20;
 constexpr int kRelBins = 1024;           // histogram bins of (key - cutoff)
-constexpr int kSelectMax = 8192;         // survivors the select kernel stages in LDS
-constexpr int kDirectWords = 256 * 8 + 256;   // direct path LDS words
+constexpr int kSelectMin = 6144;         // staged survivor entries with 64 KB of LDS
+constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 
 constexpr uint32_t kKeyNegInf = 0x007Fu; // key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF80u; // key(+inf): the pinned newest block
 constexpr uint32_t kKeyNaN = 0xFFFFu;    // key of the canonical positive NaN
 constexpr uint32_t kNone = 0xFFFFFFFFu;  // empty sample slot
 
-// LDS of the one-workgroup kernel and of the select kernel (32-bit words)
+// LDS (32-bit words), shared by the one-workgroup and the select kernels
 constexpr int kSampHist = 0;                    // 2 x 256 bins, descending keys
 constexpr int kRelHist = kSampHist + 512;       // kRelBins bins / u16 tie list
-constexpr int kBc = kRelHist + kRelBins;        // 64 words
-constexpr int kLists = kBc + 64;                // survivor segments / direct path
+constexpr int kBc = kRelHist + kRelBins;        // 128 words, 16 per per-wave field
+constexpr int kLists = kBc + 128;               // survivor entries / staging / direct path
 enum {
-  BC_CNT = 0,    // 4: survivors per wave
-  BC_CGT = 4,    // 4: keys above T per wave
-  BC_CEQ = 8,    // 4: keys equal to T (or to c) per wave
-  BC_EQ = 12,    // tie-list counter
-  BC_C1 = 13, BC_C2 = 14,   // direct-path write counters
-  BC_TMP = 16,   // 4: reductions
-  BC_X = 20      // 4: reductions
+  BC_CNT = 0,     // entries per wave
+  BC_ECNT = 16,   // survivor keys per wave
+  BC_CGT = 32,    // keys above T per wave
+  BC_CEQ = 48,    // keys equal to T per wave
+  BC_EQ = 64,     // tie-list counter
+  BC_C1 = 65, BC_C2 = 66,   // direct-path write counters
+  BC_TMP = 80,    // 16: reductions
+  BC_X = 96       // 16: reductions
 };
 
 // One team member's slice of global scratch (32-bit words):
-//   [0, 4) survivors of each wave, [4] keys equal to the cutoff, [5] the
-//   cutoff, [6] flags, [7] unused; [8, 8 + 4 kTeamLCW) the waves' survivor
-//   segments (key << 16 | chunk-local index); then up to k chunk-local
-//   indices (u16) of keys equal to the cutoff.
-constexpr int kMemberHdr = 8;
-constexpr int kMemberWords = kMemberHdr + 4 * kTeamLCW + TOPK_MAX_K / 2;
+//   [0, 4)  survivor entries of each wave     [4, 8)  survivor keys of each wave
+//   [8, 12) keys equal to the cutoff per wave [12] the cutoff  [13] flags
+//   [16, 16 + 8 kTeamLCW) the waves' survivor entries (2 words each)
+//   then the waves' tie lists (kTieCapWave chunk-local u16 indices each)
+constexpr int kMemberHdr = 16;
+constexpr int kMemberWords = kMemberHdr + 4 * 2 * kTeamLCW + 4 * kTieCapWave / 2;
 constexpr uint32_t kFlagDirect = 1u;
 
 struct Params {
@@ -109,10 +115,11 @@ struct Params {
   int32_t* out;
   int32_t* path;
   int32_t force_direct;
-  int32_t lcw;         // per-wave survivor slots (one-workgroup kernel)
+  int32_t lcw;         // survivor entries per wave (one-workgroup kernel)
   int32_t G;           // team members per row
   int32_t xcd_map;
   uint32_t* team;      // team scratch: [rows][G][kMemberWords]
+  int32_t sel_cap;     // survivor entries the select kernel stages in LDS
 };
 
 // ------------------------------------------------------------------ keys
@@ -123,6 +130,10 @@ __device__ __forceinline__ uint32_t key2(uint32_t w) {
   const uint32_t neg = w & 0x80008000u;
   const uint32_t flip = neg - (neg >> 15);  // 0x7FFF in each negative half
   return w ^ flip ^ 0x80008000u;
+}
+
+__device__ __forceinline__ uint32_t key1(uint32_t x) {
+  return (x & 0x8000u) ? (x ^ 0xFFFFu) : (x ^ 0x8000u);
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -153,13 +164,18 @@ __device__ __forceinline__ uint32_t half_of(uint32_t w, int h) {
   return h ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// Zero the keys of elements r..7 of one staged vector (r valid elements,
-// 0..8).  Only a row's (or chunk's) last occupied vector slot needs it.
-__device__ __forceinline__ void mask_tail(uint32_t (&w)[4], int r) {
-  w[0] &= r >= 2 ? 0xFFFFFFFFu : (r == 1 ? 0x0000FFFFu : 0u);
-  w[1] &= r >= 4 ? 0xFFFFFFFFu : (r == 3 ? 0x0000FFFFu : 0u);
-  w[2] &= r >= 6 ? 0xFFFFFFFFu : (r == 5 ? 0x0000FFFFu : 0u);
-  w[3] &= r >= 8 ? 0xFFFFFFFFu : (r == 7 ? 0x0000FFFFu : 0u);
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Overwrite elements r..7 of one staged vector (r valid elements, 0..8)
+// with 0xFFFF, whose key is 0 and whose signed value is -1: such an element
+// is never above a cutoff.  Only the last occupied vector slot needs it.
+__device__ __forceinline__ void poison_tail(uint4& v, int r) {
+  v.x |= r >= 2 ? 0u : (r == 1 ? 0xFFFF0000u : 0xFFFFFFFFu);
+  v.y |= r >= 4 ? 0u : (r == 3 ? 0xFFFF0000u : 0xFFFFFFFFu);
+  v.z |= r >= 6 ? 0u : (r == 5 ? 0xFFFF0000u : 0xFFFFFFFFu);
+  v.w |= r >= 8 ? 0u : (r == 7 ? 0xFFFF0000u : 0xFFFFFFFFu);
 }
 
 __device__ __forceinline__ int clamp8(int x) { return x < 0 ? 0 : (x > 8 ? 8 : x); }
@@ -168,25 +184,31 @@ __device__ __forceinline__ int clamp_len(int v, int width) {
   return v < 0 ? 0 : (v > width ? width : v);
 }
 
-// The vector a thread stages in slot j of a run of `count` vectors, or -1.
-// Full slots hold 256 consecutive vectors, lane-ordered within each wave
-// (coalesced 1 KB per wave load).  The last occupied slot jt, holding
-// rem = count - 256 jt vectors, gives each wave an equal consecutive share,
-// so that every wave sees about the same number of keys whatever the
-// length: the per-wave survivor regions stay balanced on short rows.
+// The vector a thread stages in slot j of a run of vectors whose last
+// occupied slot is jt (holding rem vectors), or -1.  Full slots hold NT
+// consecutive vectors, lane-ordered within each wave (coalesced 1 KB per
+// wave load).  Slot jt gives each wave an equal consecutive share, so that
+// every wave sees about the same number of keys whatever the length: the
+// per-wave survivor regions stay balanced on short rows.
+template <int NT>
 __device__ __forceinline__ int slot_vid(int j, int jt, int rem) {
-  if (j < jt) return j * kNT + (int)threadIdx.x;
+  constexpr int NW = NT / 64;
+  if (j < jt) return j * NT + (int)threadIdx.x;
   if (j > jt) return -1;
   const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
-  const int per_w = (rem + kWaves - 1) / kWaves;
+  const int per_w = (rem + NW - 1) / NW;
   const int x = wave * per_w + lane;
-  return (lane < per_w && x < rem) ? jt * kNT + x : -1;
+  return (lane < per_w && x < rem) ? jt * NT + x : -1;
 }
 
 // ----------------------------------------------------------- wave tools
-__device__ __forceinline__ uint32_t mbcnt(unsigned long long m) {
+__device__ __forceinline__ uint32_t mbcnt(unsigned long long m, uint32_t add = 0u) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, add));
+}
+
+__device__ __forceinline__ uint32_t popc(unsigned long long m) {
+  return (uint32_t)__popcll(m);
 }
 
 #define TOPK_DPP(x, ctrl, rmask) \
@@ -238,14 +260,55 @@ __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, u
   above = readlane(acc, L);
 }
 
+// Workgroup-wide version for a histogram of BPT*NT bins, index 0 holding
+// the largest keys: each thread scans BPT consecutive bins, one barrier
+// joins the waves, and the thread holding the answer broadcasts it through
+// tmp (NT/64 + 2 words, free until the caller's next barrier).
+template <int NT, int BPT>
+__device__ __forceinline__ void find_block(const uint32_t* hist, uint32_t need, uint32_t* tmp,
+                                           uint32_t& bin, uint32_t& above) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t h[BPT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    h[b] = hist[tid * BPT + b];
+    s += h[b];
+  }
+  const uint32_t incl = wave_incl_scan(s);
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  uint32_t acc = incl - s;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) acc += w < wave ? tmp[w] : 0u;
+  if (acc < need && need <= acc + s) {
+    uint32_t pos = BPT - 1;
+    bool found = false;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+      const bool hit = !found && acc + h[b] >= need;
+      pos = hit ? (uint32_t)b : pos;
+      found = found || hit;
+      acc += found ? 0u : h[b];
+    }
+    tmp[NW] = (uint32_t)tid * BPT + pos;
+    tmp[NW + 1] = acc;
+  }
+  __syncthreads();
+  bin = tmp[NW];
+  above = tmp[NW + 1];
+}
+
 // Sum over the workgroup (every thread gets the total).
+template <int NT>
 __device__ uint32_t block_sum(uint32_t x, uint32_t* tmp) {
   const uint32_t incl = wave_incl_scan(x);
   if (__lane_id() == 63) tmp[threadIdx.x >> 6] = incl;
   __syncthreads();
   uint32_t t = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += tmp[w];
+  for (int w = 0; w < NT / 64; ++w) t += tmp[w];
   __syncthreads();
   return t;
 }
@@ -257,8 +320,8 @@ __device__ __forceinline__ uint32_t wave_slot(bool pred, uint32_t* ctr) {
   if (m) {
     const int leader = __ffsll(m) - 1;
     uint32_t base = 0;
-    if (__lane_id() == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
-    slot = readlane(base, leader) + mbcnt(m);
+    if (__lane_id() == leader) base = atomicAdd(ctr, popc(m));
+    slot = mbcnt(m, readlane(base, leader));
   }
   return slot;
 }
@@ -308,14 +371,16 @@ __device__ __forceinline__ void set_path(const Params& p, int row, int code) {
 
 // Token rows with n <= k: 0..n-1 then -1, no logits read
 // (decode_topk_cute result definition; kimi_k3 IndexerSelect bypass).
+template <int NT>
 __device__ void write_short_token(const Out& o, int n, int k) {
-  for (int e = threadIdx.x; e < k; e += kNT) o.out[e] = e < n ? o.plain((uint32_t)e) : -1;
+  for (int e = threadIdx.x; e < k; e += NT) o.out[e] = e < n ? o.plain((uint32_t)e) : -1;
 }
 
 // Block rows with n <= k: every block in order, -1 for -inf blocks, the
 // newest pinned at +inf, then -1 padding.
+template <int NT>
 __device__ void write_short_block(const Out& o, const uint4* src, int n, int k) {
-  for (int b = threadIdx.x; b < k; b += kNT) {
+  for (int b = threadIdx.x; b < k; b += NT) {
     if (b < n) {
       const uint32_t key = (b == n - 1) ? kKeyPosInf : block_key4(src[b]);
       o.put((uint32_t)b, (uint32_t)b, key);
@@ -332,7 +397,7 @@ __device__ void write_short_block(const Out& o, const uint4* src, int n, int k) 
 // its note on replicated copies).  Reads the row from global memory; taken
 // when the sampled cutoff misjudged the row, or on request.  n > k.
 // `region` holds kDirectWords words of LDS.
-template <int MODE>
+template <int MODE, int NT>
 __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& o,
                               uint32_t* region, uint32_t* bc) {
   const int tid = threadIdx.x;
@@ -342,13 +407,13 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& 
   uint32_t* sums = region + 256 * kCopies;
   uint32_t b1 = 0, a1 = 0, b2 = 0, a2 = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (int i = tid; i < 256 * kCopies; i += kNT) hist[i] = 0;
+    for (int i = tid; i < 256 * kCopies; i += NT) hist[i] = 0;
     if (tid == 0) {
       bc[BC_C1] = 0;
       bc[BC_C2] = 0;
     }
     __syncthreads();
-    for (int vid = tid; vid < nvec; vid += kNT) {
+    for (int vid = tid; vid < nvec; vid += NT) {
       const uint4 raw = src[vid];
       if constexpr (MODE == TOPK_MODE_BLOCK) {
         const uint32_t key = (vid == n - 1) ? kKeyPosInf : block_key4(raw);
@@ -373,7 +438,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& 
       }
     }
     __syncthreads();
-    {
+    if (tid < 256) {
       uint32_t s = 0;
 #pragma unroll
       for (int c = 0; c < kCopies; ++c) s += hist[tid * kCopies + c];
@@ -394,7 +459,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& 
   const uint32_t T = (b1 << 8) | b2;
   const uint32_t cgt = a1 + a2;
   const uint32_t take = (uint32_t)k - cgt;
-  for (int vid = tid; vid < nvec; vid += kNT) {
+  for (int vid = tid; vid < nvec; vid += NT) {
     const uint4 raw = src[vid];
     if constexpr (MODE == TOPK_MODE_BLOCK) {
       const uint32_t key = (vid == n - 1) ? kKeyPosInf : block_key4(raw);
@@ -462,49 +527,97 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_
   return (b1 << 8) | (255u - i2);
 }
 
-// Survivor compaction of one key: a key above the cutoff goes to this
-// wave's segment at the wave's running count plus its rank among the
-// lanes (ballot + lane-mask count); no atomic.  `cnt` is wave-uniform.
-__device__ __forceinline__ void keep_above(uint32_t key, uint32_t idx, uint32_t c, uint32_t* seg,
-                                           uint32_t lcw, uint32_t& cnt) {
+// Survivor compaction of one raw word (two logits): if either key is above
+// the cutoff c, the word and its word index go to this wave's region (two
+// words per entry) at the wave's running count plus its rank among the
+// lanes (ballot + lane-mask count, no atomic).  With POS (c is the key of a
+// non-negative value, craw its raw bits) the test is a signed 16-bit
+// compare of the raw halves; otherwise the halves are keyed first.
+// wcnt (entries) and ecnt (keys above c) are wave-uniform; entries past
+// lcw all land on the spare slot lcw and are detected from wcnt.
+template <bool POS>
+__device__ __forceinline__ void keep_word(uint32_t w, uint32_t widx, uint32_t c, int32_t craw,
+                                          uint32_t* seg, uint32_t lcw, uint32_t& wcnt,
+                                          uint32_t& ecnt) {
+  bool lo, hi;
+  if constexpr (POS) {
+    lo = (int32_t)(int16_t)(w & 0xFFFFu) > craw;
+    hi = (int32_t)(int16_t)(w >> 16) > craw;
+  } else {
+    const uint32_t kk = key2(w);
+    lo = (kk & 0xFFFFu) > c;
+    hi = (kk >> 16) > c;
+  }
+  const unsigned long long mlo = __ballot(lo), mhi = __ballot(hi);
+  const unsigned long long m = mlo | mhi;
+  const uint32_t pos = min(mbcnt(m, wcnt), lcw);
+  if (lo || hi) {
+    seg[2 * pos] = w;
+    seg[2 * pos + 1] = widx;
+  }
+  wcnt += popc(m);
+  ecnt += popc(mlo) + popc(mhi);
+}
+
+// The same for one block key (one element per entry: key, block index).
+__device__ __forceinline__ void keep_key(uint32_t key, uint32_t idx, uint32_t c, uint32_t* seg,
+                                         uint32_t lcw, uint32_t& wcnt) {
   const bool gt = key > c;
   const unsigned long long m = __ballot(gt);
-  const uint32_t pos = cnt + mbcnt(m);
-  if (gt && pos < lcw) seg[pos] = (key << 16) | idx;
-  cnt += (uint32_t)__popcll(m);
+  const uint32_t pos = min(mbcnt(m, wcnt), lcw);
+  if (gt) {
+    seg[2 * pos] = key;
+    seg[2 * pos + 1] = idx;
+  }
+  wcnt += popc(m);
 }
 
-// Tie collection of one key equal to the cutoff (the rare second pass).
-__device__ __forceinline__ void keep_equal(uint32_t key, uint32_t idx, uint32_t c,
-                                           uint16_t* list, uint32_t cap, uint32_t* ctr) {
-  const bool eq = key == c;
-  const uint32_t slot = wave_slot(eq, ctr);
-  if (eq && slot < cap) list[slot] = (uint16_t)idx;
-}
+// Survivor entries: two words each; token entries are (raw word, word
+// index) holding two candidate keys, block entries (key, block index).
+template <int MODE>
+struct EntryView {
+  const uint32_t* e;
+  __device__ __forceinline__ void keys(uint32_t i, uint32_t& k0, uint32_t& k1) const {
+    if constexpr (MODE == TOPK_MODE_TOKEN) {
+      const uint32_t kk = key2(e[2 * i]);
+      k0 = kk & 0xFFFFu;
+      k1 = kk >> 16;
+    } else {
+      k0 = e[2 * i];
+      k1 = 0u;
+    }
+  }
+  __device__ __forceinline__ uint32_t idx(uint32_t i, uint32_t h) const {
+    if constexpr (MODE == TOPK_MODE_TOKEN) return 2u * e[2 * i + 1] + h;
+    return e[2 * i + 1];
+  }
+};
 
-// Exact k-th key T over survivors spread over the waves (all keys above
-// the cutoff c, at least k of them), then the write.  Wave w sees `cnt`
-// entries get(i) = (key, index); `rel` is a zeroed kRelBins histogram and
-// `sh` 512 free words.  The 1024 bins of (key - c - 1), largest first,
-// resolve T exactly unless T - c > 1024 (then two 8-bit passes over the
-// keys above c + 1024).  The write gives keys above T the slots
-// [0, cgt) and the first keys equal to T the slots after, from per-wave
-// counts (one barrier, no atomics).
-template <class Get>
-__device__ void select_and_write(Get get, uint32_t cnt, uint32_t c, uint32_t k, uint32_t* rel,
-                                 uint32_t* sh, uint32_t* bc, const Out& o) {
+// Exact k-th key T over the survivor entries spread over the waves (every
+// candidate key above the cutoff c counts; at least k of them), then the
+// write.  Wave w sees `cnt` entries; `rel` is a zeroed kRelBins histogram
+// and `sh` 512 free words.  The bins of (key - c - 1), largest first, give
+// T exactly unless T - c > kRelBins (then two 8-bit passes over the keys
+// above c + kRelBins).  Keys above T take the slots [0, cgt), the first
+// keys equal to T the slots after, from per-wave counts (one barrier, no
+// atomics).
+template <int MODE, int NW>
+__device__ void select_and_write(EntryView<MODE> v, uint32_t cnt, uint32_t c, uint32_t k,
+                                 uint32_t* rel, uint32_t* sh, uint32_t* bc, const Out& o) {
   const int lane = __lane_id();
   const int wave = threadIdx.x >> 6;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
     if (i < cnt) {
-      const uint32_t d = get.key(i) - c - 1u;
-      atomicAdd(&rel[(kRelBins - 1) - min(d, (uint32_t)(kRelBins - 1))], 1u);
+      uint32_t k0, k1;
+      v.keys(i, k0, k1);
+      if (k0 > c) atomicAdd(&rel[(kRelBins - 1) - min(k0 - c - 1u, (uint32_t)(kRelBins - 1))], 1u);
+      if (k1 > c) atomicAdd(&rel[(kRelBins - 1) - min(k1 - c - 1u, (uint32_t)(kRelBins - 1))], 1u);
     }
   }
   __syncthreads();
   uint32_t ri, above;
-  find_desc<kRelBins / 64>(rel, k, ri, above);
+  find_block<64 * NW, kRelBins / (64 * NW)>(rel, k, bc + BC_TMP, ri, above);
   uint32_t T, cgt;
   if (ri != 0) {
     T = c + (uint32_t)kRelBins - ri;
@@ -512,13 +625,15 @@ __device__ void select_and_write(Get get, uint32_t cnt, uint32_t c, uint32_t k, 
   } else {
     // the k-th key is at least c + kRelBins: 8-bit passes over those keys
     const uint32_t floor = c + (uint32_t)kRelBins;
-    for (int i = threadIdx.x; i < 512; i += kNT) sh[i] = 0;
+    for (int i = threadIdx.x; i < 512; i += 64 * NW) sh[i] = 0;
     __syncthreads();
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
       if (i < cnt) {
-        const uint32_t key = get.key(i);
-        if (key >= floor) atomicAdd(&sh[255u - (key >> 8)], 1u);
+        uint32_t k0, k1;
+        v.keys(i, k0, k1);
+        if (k0 >= floor) atomicAdd(&sh[255u - (k0 >> 8)], 1u);
+        if (k1 >= floor) atomicAdd(&sh[255u - (k1 >> 8)], 1u);
       }
     }
     __syncthreads();
@@ -528,8 +643,10 @@ __device__ void select_and_write(Get get, uint32_t cnt, uint32_t c, uint32_t k, 
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
       if (i < cnt) {
-        const uint32_t key = get.key(i);
-        if (key >= floor && (key >> 8) == b1) atomicAdd(&sh[256 + 255u - (key & 255u)], 1u);
+        uint32_t k0, k1;
+        v.keys(i, k0, k1);
+        if (k0 >= floor && (k0 >> 8) == b1) atomicAdd(&sh[256 + 255u - (k0 & 255u)], 1u);
+        if (k1 >= floor && (k1 >> 8) == b1) atomicAdd(&sh[256 + 255u - (k1 & 255u)], 1u);
       }
     }
     __syncthreads();
@@ -541,9 +658,10 @@ __device__ void select_and_write(Get get, uint32_t cnt, uint32_t c, uint32_t k, 
   uint32_t ngt = 0, neq = 0;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
-    const uint32_t key = i < cnt ? get.key(i) : 0u;
-    ngt += (uint32_t)__popcll(__ballot(i < cnt && key > T));
-    neq += (uint32_t)__popcll(__ballot(i < cnt && key == T));
+    uint32_t k0 = 0, k1 = 0;
+    if (i < cnt) v.keys(i, k0, k1);
+    ngt += popc(__ballot(k0 > T)) + popc(__ballot(k1 > T));
+    neq += popc(__ballot(k0 == T)) + popc(__ballot(k1 == T));
   }
   if (lane == 0) {
     bc[BC_CGT + wave] = ngt;
@@ -557,30 +675,71 @@ __device__ void select_and_write(Get get, uint32_t cnt, uint32_t c, uint32_t k, 
   }
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
-    const bool ok = i < cnt;
-    const uint32_t key = ok ? get.key(i) : 0u;
-    const bool gt = ok && key > T, eq = ok && key == T;
-    const unsigned long long mg = __ballot(gt);
-    const unsigned long long me = __ballot(eq);
-    if (gt) o.put(bgt + mbcnt(mg), get.idx(i), key);
-    const uint32_t r = beq + mbcnt(me);
-    if (eq && r < take) o.put(cgt + r, get.idx(i), key);
-    bgt += (uint32_t)__popcll(mg);
-    beq += (uint32_t)__popcll(me);
+    uint32_t k0 = 0, k1 = 0;
+    if (i < cnt) v.keys(i, k0, k1);
+    const bool g0 = k0 > T, g1 = k1 > T, e0 = k0 == T, e1 = k1 == T;
+    const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
+    const unsigned long long me0 = __ballot(e0), me1 = __ballot(e1);
+    const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, bgt));
+    if (g0) o.put(p0, v.idx(i, 0), k0);
+    if (g1) o.put(p0 + (g0 ? 1u : 0u), v.idx(i, 1), k1);
+    const uint32_t q0 = mbcnt(me1, mbcnt(me0, beq));
+    if (e0 && q0 < take) o.put(cgt + q0, v.idx(i, 0), k0);
+    const uint32_t q1 = q0 + (e0 ? 1u : 0u);
+    if (e1 && q1 < take) o.put(cgt + q1, v.idx(i, 1), k1);
+    bgt += popc(mg0) + popc(mg1);
+    beq += popc(me0) + popc(me1);
   }
 }
 
-// A wave's survivor segment in LDS: entries key << 16 | index.
-struct SegView {
-  const uint32_t* seg;
-  __device__ __forceinline__ uint32_t key(uint32_t i) const { return seg[i] >> 16; }
-  __device__ __forceinline__ uint32_t idx(uint32_t i) const { return seg[i] & 0xFFFFu; }
-};
+// Every survivor key (above c) of the entries at [base, ...) in order: the
+// tie pass's first part.  Positions come from per-wave key counts.
+template <int MODE>
+__device__ void write_above(EntryView<MODE> v, uint32_t cnt, uint32_t c, uint32_t base,
+                            const Out& o) {
+  const int lane = __lane_id();
+  for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
+    const uint32_t i = b0 + lane;
+    uint32_t k0 = 0, k1 = 0;
+    if (i < cnt) v.keys(i, k0, k1);
+    const bool g0 = k0 > c, g1 = k1 > c;
+    const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
+    const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, base));
+    if (g0) o.put(p0, v.idx(i, 0), k0);
+    if (g1) o.put(p0 + (g0 ? 1u : 0u), v.idx(i, 1), k1);
+    base += popc(mg0) + popc(mg1);
+  }
+}
+
+// Tie collection of one key equal to the cutoff into a list shared by the
+// workgroup, one LDS atomic per wave (the rare pass of the one-workgroup
+// kernel).
+__device__ __forceinline__ void keep_equal_slot(bool eq, uint32_t idx, uint16_t* list,
+                                                uint32_t cap, uint32_t* ctr) {
+  const uint32_t slot = wave_slot(eq, ctr);
+  if (eq && slot < cap) list[slot] = (uint16_t)idx;
+}
+
+// Tie collection into this wave's own list at its running count (no atomic).
+__device__ __forceinline__ void keep_tie(bool eq, uint32_t idx, uint16_t* seg, uint32_t cap,
+                                         uint32_t& tcnt) {
+  const unsigned long long m = __ballot(eq);
+  const uint32_t pos = mbcnt(m, tcnt);
+  if (eq && pos < cap) seg[pos] = (uint16_t)idx;
+  tcnt += popc(m);
+}
+
+// Tie indices each wave of a team member keeps: enough for its share of k.
+__device__ __forceinline__ uint32_t tie_cap(int k) {
+  const uint32_t c = (uint32_t)k / 4u + 64u;
+  return c < (uint32_t)kTieCapWave ? c : (uint32_t)kTieCapWave;
+}
 
 // ============================================ one workgroup per row
-// Rows whose valid vectors fit kNT * VPT: the whole row sits in VGPRs.
-template <int MODE, int VPT>
-__global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
+// Rows whose valid vectors fit NT * VPT: the whole row sits in VGPRs.
+template <int MODE, int NT, int VPT>
+__global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
+  constexpr int NW = NT / 64;
   extern __shared__ uint32_t smem[];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -597,8 +756,8 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
   uint32_t* lists = smem + kLists;
 
   if (n <= k) {
-    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block(o, src, n, k);
-    else write_short_token(o, n, k);
+    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
+    else write_short_token<NT>(o, n, k);
     set_path(p, row, TOPK_PATH_SHORT);
     return;
   }
@@ -606,42 +765,44 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
   int code = TOPK_PATH_DIRECT_FORCED;
   if (!direct) {
     const int nvec = (v + 7) >> 3;
-    const int jt = (nvec - 1) / kNT;  // last vector slot holding row data
-    const int rem = nvec - jt * kNT;  // vectors in it
-    for (int i = tid; i < 512 + kRelBins; i += kNT) smem[i] = 0;  // sample + relative hists
+    const int jt = (nvec - 1) / NT;   // last vector slot holding row data
+    const int rem = nvec - jt * NT;   // vectors in it
+    for (int i = tid; i < 512 + kRelBins; i += NT) smem[i] = 0;  // sample + relative hists
     if (tid == 0) bc[BC_EQ] = 0;
 
-    // -- stage the row: 16-byte loads into VGPRs, keys computed in place
+    // -- stage the row: 16-byte loads into VGPRs
     uint4 raw[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int vid = slot_vid(j, jt, rem);
-      raw[j] = vid >= 0 ? src[vid] : make_uint4(0u, 0u, 0u, 0u);
+      const int vid = slot_vid<NT>(j, jt, rem);
+      raw[j] = vid >= 0 ? src[vid] : make_uint4(~0u, ~0u, ~0u, ~0u);
     }
-    constexpr int kSampleEvery = VPT / 8;  // sampled slots: j % kSampleEvery == 0
-    uint32_t sk[8];
-    uint32_t kw[MODE == TOPK_MODE_BLOCK ? 1 : VPT][4];
+    // sampled slots: every slot in token mode (one logit of every vector),
+    // every SE-th slot in block mode (at most 2048 block keys)
+    constexpr int SE = (MODE == TOPK_MODE_TOKEN || VPT * NT <= 2048) ? 1 : VPT * NT / 2048;
+    constexpr int NSK = VPT / SE;
+    uint32_t sk[NSK];
     uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
-    uint32_t S = 0;  // samples taken over the workgroup
+    uint32_t S = 0;  // samples over the workgroup
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-      const int vid = slot_vid(j, jt, rem);
+      const int vid = slot_vid<NT>(j, jt, rem);
       uint32_t s = kNone;
       if constexpr (MODE == TOPK_MODE_BLOCK) {
         kb[j] = vid >= 0 ? (vid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
-        s = kb[j];
+        s = vid >= 0 ? kb[j] : kNone;
       } else {
-        uint32_t w[4] = {key2(raw[j].x), key2(raw[j].y), key2(raw[j].z), key2(raw[j].w)};
-        if (j == jt) mask_tail(w, vid >= 0 ? clamp8(v - 8 * vid) : 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kw[j][i] = w[i];
-        // sample: element (j & 7) of the vector, element 0 if that is past v
-        const int e = (j / kSampleEvery) & 7;
-        s = (vid * 8 + e < v) ? half_of(w[e >> 1], e & 1) : (w[0] & 0xFFFFu);
+        if (j == jt) poison_tail(raw[j], vid >= 0 ? clamp8(v - 8 * vid) : 0);
+        // sample: logit j mod 8 (that is, (vid / NT) mod 8) of the vector,
+        // logit 0 if that one is past the length
+        const int es = j & 7;
+        const uint32_t se = key1(half_of(word_of(raw[j], es >> 1), es & 1));
+        const uint32_t s0 = key1(raw[j].x & 0xFFFFu);
+        s = vid >= 0 ? ((vid * 8 + es < v) ? se : s0) : kNone;
       }
-      if (j % kSampleEvery == 0) {
-        sk[j / kSampleEvery] = vid >= 0 ? s : kNone;
-        S += (uint32_t)(j < jt ? kNT : (j == jt ? rem : 0));
+      if (j % SE == 0) {
+        sk[j / SE] = s;
+        S += (uint32_t)(j < jt ? NT : (j == jt ? rem : 0));
       }
     }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
@@ -653,41 +814,58 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
     } else {
-      // -- filter + compaction of the keys above the cutoff
+      // -- filter + compaction of the words holding a key above the cutoff
       const uint32_t lcw = (uint32_t)p.lcw;
-      uint32_t* seg = lists + wave * lcw;
-      uint32_t cnt = 0;
+      uint32_t* seg = lists + wave * (lcw + 1) * 2;
+      uint32_t wcnt = 0, ecnt = 0;
+      if constexpr (MODE == TOPK_MODE_BLOCK) {
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        if (j <= jt) {
-          const uint32_t vid = (uint32_t)slot_vid(j, jt, rem);  // keys of -1 slots are 0
-          if constexpr (MODE == TOPK_MODE_BLOCK) {
-            keep_above(kb[j], vid, c, seg, lcw, cnt);
-          } else {
+        for (int j = 0; j < VPT; ++j)
+          if (j <= jt) keep_key(kb[j], (uint32_t)slot_vid<NT>(j, jt, rem), c, seg, lcw, wcnt);
+        ecnt = wcnt;
+      } else if (c >= 0x8000u) {
+        const int32_t craw = (int32_t)(c - 0x8000u);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              keep_above(half_of(kw[j][e >> 1], e & 1), (vid << 3) | (uint32_t)e, c, seg, lcw,
-                         cnt);
+        for (int j = 0; j < VPT; ++j) {
+          if (j <= jt) {
+            const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+              keep_word<true>(word_of(raw[j], q2), w4 + q2, c, craw, seg, lcw, wcnt, ecnt);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+          if (j <= jt) {
+            const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2)
+              keep_word<false>(word_of(raw[j], q2), w4 + q2, c, 0, seg, lcw, wcnt, ecnt);
           }
         }
       }
-      if (lane == 0) bc[BC_CNT + wave] = cnt;
+      if (lane == 0) {
+        bc[BC_CNT + wave] = wcnt;
+        bc[BC_ECNT + wave] = ecnt;
+      }
       __syncthreads();
       uint32_t gt_total = 0, before = 0;
       bool ovf = false;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const uint32_t cw = bc[BC_CNT + w];
-        before += w < wave ? cw : 0u;
-        gt_total += cw;
-        ovf |= cw > lcw;
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t ew = bc[BC_ECNT + w];
+        before += w < wave ? ew : 0u;
+        gt_total += ew;
+        ovf |= bc[BC_CNT + w] > lcw;
       }
+      const uint32_t nent = min(wcnt, lcw);
       if (ovf) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
       } else if (gt_total >= (uint32_t)k) {
         // the k-th key lies above the cutoff: exact select over the survivors
-        select_and_write(SegView{seg}, cnt, c, (uint32_t)k, rel, sh, bc, o);
+        select_and_write<MODE, NW>(EntryView<MODE>{seg}, nent, c, (uint32_t)k, rel, sh, bc, o);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key can only be the cutoff: collect keys equal to it
@@ -695,14 +873,15 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
           if (j <= jt) {
-            const uint32_t vid = (uint32_t)slot_vid(j, jt, rem);
+            const int vid = slot_vid<NT>(j, jt, rem);
             if constexpr (MODE == TOPK_MODE_BLOCK) {
-              keep_equal(kb[j], vid, c, ties, (uint32_t)k, &bc[BC_EQ]);
+              keep_equal_slot(kb[j] == c, (uint32_t)vid, ties, (uint32_t)k, &bc[BC_EQ]);
             } else {
 #pragma unroll
-              for (int e = 0; e < 8; ++e)
-                keep_equal(half_of(kw[j][e >> 1], e & 1), (vid << 3) | (uint32_t)e, c, ties,
-                           (uint32_t)k, &bc[BC_EQ]);
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t key = key1(half_of(word_of(raw[j], e >> 1), e & 1));
+                keep_equal_slot(key == c, (uint32_t)(vid * 8 + e), ties, (uint32_t)k, &bc[BC_EQ]);
+              }
             }
           }
         }
@@ -712,9 +891,9 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
           direct = true;
           code = TOPK_PATH_DIRECT_MISJUDGED;
         } else {
-          for (uint32_t i = lane; i < cnt; i += 64) o.put(before + i, seg[i] & 0xFFFFu, seg[i] >> 16);
+          write_above<MODE>(EntryView<MODE>{seg}, nent, c, before, o);
           const uint32_t take = (uint32_t)k - gt_total;
-          for (uint32_t i = tid; i < take; i += kNT) o.put(gt_total + i, ties[i], c);
+          for (uint32_t i = tid; i < take; i += NT) o.put(gt_total + i, ties[i], c);
           code = TOPK_PATH_SAMPLED_TIES;
         }
       }
@@ -722,7 +901,7 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE>(src, v, n, k, o, lists, bc);
+    direct_select<MODE, NT>(src, v, n, k, o, lists, bc);
   }
   set_path(p, row, code);
 }
@@ -731,11 +910,13 @@ __global__ __launch_bounds__(kNT) void topk_rows_wg(Params p) {
 // Stage 1: every member of a row's team stages its chunk of the row (the
 // chunks split the valid length), derives the row's cutoff from samples
 // spread over the whole row (the same in every member), and writes the
-// keys above it, and if any, the keys equal to it, to its scratch slice.
+// words holding keys above it, and if any, the indices of keys equal to
+// it, to its scratch slice.
 template <int MODE, int VPT, int SV>
-__global__ __launch_bounds__(kNT) void topk_team_filter(Params p) {
+__global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
+  constexpr int NT = kTeamNT;
   __shared__ uint32_t sh[512];
-  __shared__ uint32_t bc[64];
+  __shared__ uint32_t bc[128];
   const int G = p.G;
   int lrow, member;
   if (p.xcd_map) {
@@ -760,8 +941,8 @@ __global__ __launch_bounds__(kNT) void topk_team_filter(Params p) {
   if (n <= k) {
     if (member == 0) {
       const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
-      if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block(o, src, n, k);
-      else write_short_token(o, n, k);
+      if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
+      else write_short_token<NT>(o, n, k);
       set_path(p, row, TOPK_PATH_SHORT);
     }
     return;
@@ -772,35 +953,25 @@ __global__ __launch_bounds__(kNT) void topk_team_filter(Params p) {
   const int per = (nvec + G - 1) / G;
   const int vb = min(member * per, nvec);
   const int ve = min(vb + per, nvec);
-  const int jt = ve > vb ? (ve - vb - 1) / kNT : -1;  // last occupied slot
-  const int rem = (ve - vb) - jt * kNT;               // vectors in it
-  for (int i = tid; i < 512; i += kNT) sh[i] = 0;
-  if (tid == 0) bc[BC_EQ] = 0;
+  const int jt = ve > vb ? (ve - vb - 1) / NT : -1;  // last occupied slot
+  const int rem = (ve - vb) - jt * NT;               // vectors in it
+  for (int i = tid; i < 512; i += NT) sh[i] = 0;
 
-  // -- chunk loads and sample loads, all issued before any use
-  uint4 raw[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int lvid = slot_vid(j, jt, rem);
-    raw[j] = lvid >= 0 ? src[vb + lvid] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  const int ns = min(SV * kNT, nvec);  // sample vectors, spread over the row
+  // -- sample loads and chunk loads, all issued before any use
+  const int ns = min(SV * NT, nvec);  // sample vectors, spread over the row
   uint4 sraw[SV];
   int spos[SV];
 #pragma unroll
   for (int j = 0; j < SV; ++j) {
-    const int s = j * kNT + tid;
+    const int s = j * NT + tid;
     spos[j] = s < ns ? (int)(((int64_t)(2 * s + 1) * nvec) / (2 * (int64_t)ns)) : -1;
-    sraw[j] = spos[j] >= 0 ? src[spos[j]] : make_uint4(0u, 0u, 0u, 0u);
+    sraw[j] = spos[j] >= 0 ? src[spos[j]] : make_uint4(~0u, ~0u, ~0u, ~0u);
   }
-  // block keys right away, so the raw vectors die early
-  uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
-  if constexpr (MODE == TOPK_MODE_BLOCK) {
+  uint4 raw[VPT];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int lvid = slot_vid(j, jt, rem);
-      kb[j] = lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
-    }
+  for (int j = 0; j < VPT; ++j) {
+    const int lvid = slot_vid<NT>(j, jt, rem);
+    raw[j] = lvid >= 0 ? src[vb + lvid] : make_uint4(~0u, ~0u, ~0u, ~0u);
   }
 
   // -- sample keys and the cutoff (identical in every member)
@@ -814,98 +985,115 @@ __global__ __launch_bounds__(kNT) void topk_team_filter(Params p) {
       sk[j] = vid < 0 ? kNone : (vid == n - 1 ? kKeyPosInf : block_key4(sraw[j]));
       my_samples += vid >= 0 ? 1u : 0u;
     } else {
-      const uint32_t w[4] = {key2(sraw[j].x), key2(sraw[j].y), key2(sraw[j].z),
-                             key2(sraw[j].w)};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = vid >= 0 && vid * 8 + e < v;
-        sk[j * 8 + e] = ok ? half_of(w[e >> 1], e & 1) : kNone;
+        sk[j * 8 + e] = ok ? key1(half_of(word_of(sraw[j], e >> 1), e & 1)) : kNone;
         my_samples += ok ? 1u : 0u;
       }
     }
   }
-  const uint32_t S = block_sum(my_samples, bc + BC_TMP);  // also publishes the zeroed hists
+  // block keys (and the tail's poison) before the barriers
+  uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int lvid = slot_vid<NT>(j, jt, rem);
+    if constexpr (MODE == TOPK_MODE_BLOCK) {
+      kb[j] = lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
+    } else {
+      if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
+    }
+  }
+  const uint32_t S = block_sum<NT>(my_samples, bc + BC_TMP);  // also publishes the zeroed hists
   const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
   const uint32_t c = sample_cutoff(sk, q, sh);
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
     // a zero cutoff would admit the zero keys of slots past the length:
     // every member sees the same cutoff and flags the row for the direct path
     if (tid == 0) {
-      slice[5] = c;
-      slice[6] = kFlagDirect;
+      slice[12] = c;
+      slice[13] = kFlagDirect;
     }
     return;
   }
 
-  // -- keys of the chunk; the ones above the cutoff go straight to scratch
-  uint32_t* seg = slice + kMemberHdr + wave * kTeamLCW;
-  uint32_t cnt = 0, neq = 0;
+  // -- the words above the cutoff go straight to this wave's scratch region
+  uint32_t* seg = slice + kMemberHdr + wave * 2 * kTeamLCW;
+  const uint32_t lcw = kTeamLCW - 1;  // the last entry is the spare slot
+  uint32_t wcnt = 0, ecnt = 0, neq = 0;
+  if constexpr (MODE == TOPK_MODE_BLOCK) {
 #pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    if (j <= jt) {
-      const int lvid = slot_vid(j, jt, rem);
-      const int vid = vb + lvid;
-      if constexpr (MODE == TOPK_MODE_BLOCK) {
-        keep_above(kb[j], (uint32_t)lvid, c, seg, kTeamLCW, cnt);
-        neq += (uint32_t)__popcll(__ballot(kb[j] == c));
-      } else {
-        uint32_t w[4] = {key2(raw[j].x), key2(raw[j].y), key2(raw[j].z), key2(raw[j].w)};
-        if (j == jt) mask_tail(w, lvid >= 0 ? clamp8(v - 8 * vid) : 0);
+    for (int j = 0; j < VPT; ++j) {
+      if (j <= jt) {
+        keep_key(kb[j], (uint32_t)slot_vid<NT>(j, jt, rem), c, seg, lcw, wcnt);
+        neq += popc(__ballot(kb[j] == c));
+      }
+    }
+    ecnt = wcnt;
+  } else if (c >= 0x8000u) {
+    const int32_t craw = (int32_t)(c - 0x8000u);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t key = half_of(w[e >> 1], e & 1);
-          keep_above(key, ((uint32_t)lvid << 3) | (uint32_t)e, c, seg, kTeamLCW, cnt);
-          neq += (uint32_t)__popcll(__ballot(key == c));
+    for (int j = 0; j < VPT; ++j) {
+      if (j <= jt) {
+        const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const uint32_t w = word_of(raw[j], q2);
+          keep_word<true>(w, w4 + q2, c, craw, seg, lcw, wcnt, ecnt);
+          neq += popc(__ballot((w & 0xFFFFu) == (uint32_t)craw)) +
+                 popc(__ballot((w >> 16) == (uint32_t)craw));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      if (j <= jt) {
+        const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const uint32_t w = word_of(raw[j], q2);
+          keep_word<false>(w, w4 + q2, c, 0, seg, lcw, wcnt, ecnt);
+          const uint32_t kk = key2(w);
+          neq += popc(__ballot((kk & 0xFFFFu) == c)) + popc(__ballot((kk >> 16) == c));
         }
       }
     }
   }
   if (lane == 0) {
-    slice[wave] = cnt;
-    bc[BC_CEQ + wave] = neq;
+    slice[wave] = wcnt;
+    slice[4 + wave] = ecnt;
+    bc[BC_X + wave] = neq;
   }
   __syncthreads();
-  const uint32_t eq_total = bc[BC_CEQ] + bc[BC_CEQ + 1] + bc[BC_CEQ + 2] + bc[BC_CEQ + 3];
+  const uint32_t eq_total = bc[BC_X] + bc[BC_X + 1] + bc[BC_X + 2] + bc[BC_X + 3];
+  uint32_t tcnt = 0;
   if (eq_total) {
-    // second pass: up to k chunk-local indices of keys equal to the cutoff
-    uint16_t* ties = reinterpret_cast<uint16_t*>(slice + kMemberHdr + 4 * kTeamLCW);
+    // second pass: chunk-local indices of keys equal to the cutoff
+    uint16_t* tseg =
+        reinterpret_cast<uint16_t*>(slice + kMemberHdr + 8 * kTeamLCW) + wave * kTieCapWave;
+    const uint32_t cap = tie_cap(k);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       if (j <= jt) {
-        const int lvid = slot_vid(j, jt, rem);
-        const int vid = vb + lvid;
+        const int lvid = slot_vid<NT>(j, jt, rem);
         if constexpr (MODE == TOPK_MODE_BLOCK) {
-          keep_equal(kb[j], (uint32_t)lvid, c, ties, (uint32_t)k, &bc[BC_EQ]);
+          keep_tie(kb[j] == c, (uint32_t)lvid, tseg, cap, tcnt);
         } else {
-          uint32_t w[4] = {key2(raw[j].x), key2(raw[j].y), key2(raw[j].z), key2(raw[j].w)};
-          if (j == jt) mask_tail(w, lvid >= 0 ? clamp8(v - 8 * vid) : 0);
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            keep_equal(half_of(w[e >> 1], e & 1), ((uint32_t)lvid << 3) | (uint32_t)e, c, ties,
-                       (uint32_t)k, &bc[BC_EQ]);
+            keep_tie(key1(half_of(word_of(raw[j], e >> 1), e & 1)) == c,
+                     (uint32_t)(lvid * 8 + e), tseg, cap, tcnt);
         }
       }
     }
   }
+  if (lane == 0) slice[8 + wave] = tcnt;
   if (tid == 0) {
-    slice[4] = eq_total;
-    slice[5] = c;
-    slice[6] = 0u;
+    slice[12] = c;
+    slice[13] = 0u;
   }
 }
-
-// Survivors staged in LDS by the select kernel.
-struct StageView {
-  const uint16_t* keys;
-  const uint32_t* idxs;
-  __device__ __forceinline__ uint32_t key(uint32_t i) const { return keys[i]; }
-  __device__ __forceinline__ uint32_t idx(uint32_t i) const { return idxs[i]; }
-};
-
-// LDS of the select kernel (words), after the shared first kLists words
-constexpr int kSelPrefix = kLists;                     // 4 G + 1 segment starts, G + 1 tie starts
-constexpr int kSelStage = kSelPrefix + 512;            // u16 keys, then u32 indices
-constexpr int kSelWords = kSelStage + kSelectMax / 2 + kSelectMax;
 
 // Index of the segment holding flattened entry i: the last s with
 // start[s] <= i (start[0] = 0, nseg + 1 entries).
@@ -919,12 +1107,21 @@ __device__ __forceinline__ int find_segment(const uint32_t* start, int nseg, uin
   return lo;
 }
 
-// Stage 2: one workgroup per row reads the team's slices (written by the
-// previous kernel, so plain loads see them), checks the cutoff held, and
-// writes the row: exact select over the survivors, the tie pass, or the
-// direct path.
+// LDS of the select kernel past kLists (words)
+constexpr int kSelSegc = 0;          // entries per segment (4 G <= 256)
+constexpr int kSelStart = 256;       // 4 G + 1 entry starts
+constexpr int kSelEstart = 520;      // 4 G + 1 key starts
+constexpr int kSelTstart = 784;      // 4 G + 1 tie starts
+constexpr int kSelStage = 1048;      // staged entries, 2 words each
+constexpr int kSelFixed = kLists + kSelStage;  // words before the staged entries
+
+// Stage 2: one 1024-thread workgroup per row reads the team's slices
+// (written by the previous kernel, so plain loads see them), checks that
+// the cutoff held, and writes the row: exact select over the survivors,
+// the tie pass, or the direct path.
 template <int MODE>
-__global__ __launch_bounds__(kNT) void topk_team_select(Params p) {
+__global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
+  constexpr int NT = kSelNT, NW = NT / 64;
   extern __shared__ uint32_t smem[];
   const int lrow = blockIdx.x;
   const int row = p.row0 + lrow;
@@ -941,114 +1138,148 @@ __global__ __launch_bounds__(kNT) void topk_team_select(Params p) {
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
-  uint32_t* start = smem + kSelPrefix;          // 4G + 1 segment starts
-  uint32_t* tstart = start + 4 * G + 1;         // G + 1 tie-list starts
-  uint16_t* skeys = reinterpret_cast<uint16_t*>(smem + kSelStage);
-  uint32_t* sidx = smem + kSelStage + kSelectMax / 2;
+  uint32_t* segc = smem + kLists + kSelSegc;
+  uint32_t* start = smem + kLists + kSelStart;
+  uint32_t* estart = smem + kLists + kSelEstart;
+  uint32_t* tstart = smem + kLists + kSelTstart;
+  uint32_t* stage = smem + kLists + kSelStage;
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
   if (!direct) {
     const uint32_t* slices = p.team + (size_t)lrow * G * kMemberWords;
     const int nvec = (v + 7) >> 3;
-    const int per = (nvec + G - 1) / G;
-    const uint32_t scale = (MODE == TOPK_MODE_BLOCK) ? 1u : 8u;
-    for (int i = tid; i < 512 + kRelBins; i += kNT) smem[i] = 0;
-    // segment sizes -> starts (block-wide inclusive scan; 4 G <= kNT)
-    uint32_t sz = 0, bad = 0;
-    if (tid < 4 * G) {
-      sz = slices[(size_t)(tid >> 2) * kMemberWords + (tid & 3)];
-      bad = sz > (uint32_t)kTeamLCW ? 1u : 0u;
+    const uint32_t per = (uint32_t)((nvec + G - 1) / G);
+    const int nseg = 4 * G;  // <= 256: waves 0..3 hold one segment per lane
+    for (int i = tid; i < 512 + kRelBins; i += NT) smem[i] = 0;
+    uint32_t wc = 0, ec = 0, tc = 0, tcp = 0, bad = 0;
+    if (tid < nseg) {
+      const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
+      const int w = tid & 3;
+      if (hdr[13] & kFlagDirect) {
+        bad = 2u;
+      } else {
+        wc = hdr[w];
+        ec = hdr[4 + w];
+        tc = hdr[8 + w];
+        tcp = min(tc, tie_cap(k));
+        bad = wc > (uint32_t)(kTeamLCW - 1) ? 1u : 0u;
+      }
+      segc[tid] = wc;
     }
-    uint32_t tz = 0, ties = 0;
-    if (tid < G) {
-      ties = slices[(size_t)tid * kMemberWords + 4];
-      tz = min(ties, (uint32_t)k);
-      bad |= slices[(size_t)tid * kMemberWords + 6] ? 2u : 0u;
-    }
-    const uint32_t incl = wave_incl_scan(sz);
-    const uint32_t tincl = wave_incl_scan(tz);
-    const uint32_t eqsum = wave_incl_scan(ties);
-    const unsigned long long anybad = __ballot((bad & 1u) != 0);
-    const unsigned long long anyflag = __ballot((bad & 2u) != 0);
+    const uint32_t iw = wave_incl_scan(wc), ie = wave_incl_scan(ec);
+    const uint32_t it = wave_incl_scan(tcp), itc = wave_incl_scan(tc);
+    const unsigned long long mb = __ballot((bad & 1u) != 0), mf = __ballot((bad & 2u) != 0);
     if (lane == 63) {
-      bc[BC_TMP + wave] = incl;
-      bc[BC_X + wave] = eqsum;
+      bc[BC_TMP + wave] = iw;
+      bc[BC_X + wave] = ie;
+      bc[BC_CGT + wave] = it;
+      bc[BC_CEQ + wave] = itc;
     }
-    if (lane == 0) {
-      bc[BC_CGT + wave] = anybad ? 1u : 0u;
-      bc[BC_CEQ + wave] = anyflag ? 1u : 0u;
-    }
+    if (lane == 0) bc[BC_CNT + wave] = (mb ? 1u : 0u) | (mf ? 2u : 0u);
     __syncthreads();
-    uint32_t off = 0, gt_total = 0, eq_total = 0, flagged = 0, broken = 0;
+    uint32_t ow = 0, oe = 0, ot = 0, E = 0, gt_total = 0, avail = 0, eq_total = 0, flags = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      off += w < wave ? bc[BC_TMP + w] : 0u;
-      gt_total += bc[BC_TMP + w];
-      eq_total += bc[BC_X + w];
-      broken |= bc[BC_CGT + w];
-      flagged |= bc[BC_CEQ + w];
+    for (int w = 0; w < NW; ++w) {
+      const bool lower = w < wave;
+      ow += lower ? bc[BC_TMP + w] : 0u;
+      oe += lower ? bc[BC_X + w] : 0u;
+      ot += lower ? bc[BC_CGT + w] : 0u;
+      E += bc[BC_TMP + w];
+      gt_total += bc[BC_X + w];
+      avail += bc[BC_CGT + w];
+      eq_total += bc[BC_CEQ + w];
+      flags |= bc[BC_CNT + w];
     }
-    if (tid < 4 * G) start[tid + 1] = off + incl;
-    if (tid == 0) start[0] = 0;
-    if (tid < G) tstart[tid + 1] = tincl;  // G <= 64: the first wave holds them all
-    if (tid == 0) tstart[0] = 0;
-    const uint32_t c = slices[5];
+    if (tid < nseg) {
+      start[tid + 1] = ow + iw;
+      estart[tid + 1] = oe + ie;
+      tstart[tid + 1] = ot + it;
+    }
+    if (tid == 0) {
+      start[0] = 0;
+      estart[0] = 0;
+      tstart[0] = 0;
+    }
+    const uint32_t c = slices[12];
     __syncthreads();
-    if (flagged) {
+    const uint32_t gscale = (MODE == TOPK_MODE_BLOCK) ? 1u : 4u;  // entry index units
+    if (flags & 2u) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
-    } else if (broken) {
+    } else if (flags & 1u) {
       direct = true;
       code = TOPK_PATH_DIRECT_OVERFLOW;
     } else if (gt_total + eq_total < (uint32_t)k) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
     } else if (gt_total >= (uint32_t)k) {
-      if (gt_total > (uint32_t)kSelectMax) {
+      if (E > (uint32_t)p.sel_cap) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
       } else {
-        // stage every survivor in LDS: key, row index
-#pragma unroll 8
-        for (uint32_t i = tid; i < gt_total; i += kNT) {
-          const int s = find_segment(start, 4 * G, i);
-          const int g = s >> 2;
-          const uint32_t e =
-              slices[(size_t)g * kMemberWords + kMemberHdr + (s & 3) * kTeamLCW + (i - start[s])];
-          skeys[i] = (uint16_t)(e >> 16);
-          sidx[i] = (uint32_t)(g * per) * scale + (e & 0xFFFFu);
+        // stage every survivor entry in LDS with its row-level index
+        for (int s = wave; s < nseg; s += NW) {
+          const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
+                               (s & 3) * 2 * kTeamLCW;
+          const uint32_t gbase = (uint32_t)(s >> 2) * per * gscale;
+          const uint32_t cs = segc[s], d0 = start[s];
+          for (uint32_t i = lane; i < cs; i += 64) {
+            stage[2 * (d0 + i)] = es[2 * i];
+            stage[2 * (d0 + i) + 1] = es[2 * i + 1] + gbase;
+          }
         }
         __syncthreads();
-        const uint32_t quarter = (gt_total + kWaves - 1) / kWaves;
-        const uint32_t lo = min((uint32_t)wave * quarter, gt_total);
-        const uint32_t hi = min(lo + quarter, gt_total);
-        select_and_write(StageView{skeys + lo, sidx + lo}, hi - lo, c, (uint32_t)k, rel, sh, bc, o);
+        const uint32_t share = (E + NW - 1) / NW;
+        const uint32_t lo = min((uint32_t)wave * share, E);
+        const uint32_t hi = min(lo + share, E);
+        select_and_write<MODE, NW>(EntryView<MODE>{stage + 2 * lo}, hi - lo, c, (uint32_t)k,
+                                   rel, sh, bc, o);
         code = TOPK_PATH_SAMPLED;
       }
     } else {
-      // the k-th key is the cutoff: every survivor above it, then ties
-#pragma unroll 8
-      for (uint32_t i = tid; i < gt_total; i += kNT) {
-        const int s = find_segment(start, 4 * G, i);
-        const int g = s >> 2;
-        const uint32_t e =
-            slices[(size_t)g * kMemberWords + kMemberHdr + (s & 3) * kTeamLCW + (i - start[s])];
-        o.put(i, (uint32_t)(g * per) * scale + (e & 0xFFFFu), e >> 16);
-      }
+      // the k-th key is the cutoff: every key above it, then ties
       const uint32_t take = (uint32_t)k - gt_total;
-      for (uint32_t j = tid; j < take; j += kNT) {
-        const int g = find_segment(tstart, G, j);
-        const uint16_t* tl =
-            reinterpret_cast<const uint16_t*>(slices + (size_t)g * kMemberWords + kMemberHdr +
-                                              4 * kTeamLCW);
-        o.put(gt_total + j, (uint32_t)(g * per) * scale + tl[j - tstart[g]], c);
+      if (avail < take) {
+        direct = true;
+        code = TOPK_PATH_DIRECT_OVERFLOW;
+      } else {
+        for (int s = wave; s < nseg; s += NW) {
+          const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
+                               (s & 3) * 2 * kTeamLCW;
+          const uint32_t gbase = (uint32_t)(s >> 2) * per * gscale;
+          const uint32_t cs = segc[s];
+          uint32_t base = estart[s];
+          for (uint32_t b0 = 0; b0 < cs; b0 += 64) {
+            const uint32_t i = b0 + lane;
+            uint32_t k0 = 0, k1 = 0, id = 0;
+            if (i < cs) {
+              EntryView<MODE>{es}.keys(i, k0, k1);
+              id = es[2 * i + 1] + gbase;
+            }
+            const bool g0 = k0 > c, g1 = k1 > c;
+            const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
+            const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, base));
+            const uint32_t i0 = (MODE == TOPK_MODE_TOKEN) ? 2u * id : id;
+            if (g0) o.put(p0, i0, k0);
+            if (g1) o.put(p0 + (g0 ? 1u : 0u), i0 + 1u, k1);
+            base += popc(mg0) + popc(mg1);
+          }
+        }
+        const uint32_t escale = (MODE == TOPK_MODE_BLOCK) ? 1u : 8u;  // element index units
+        for (uint32_t j = tid; j < take; j += NT) {
+          const int s = find_segment(tstart, nseg, j);
+          const uint16_t* tl = reinterpret_cast<const uint16_t*>(
+                                   slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
+                                   8 * kTeamLCW) + (s & 3) * kTieCapWave;
+          o.put(gt_total + j, (uint32_t)(s >> 2) * per * escale + tl[j - tstart[s]], c);
+        }
+        code = TOPK_PATH_SAMPLED_TIES;
       }
-      code = TOPK_PATH_SAMPLED_TIES;
     }
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE>(src, v, n, k, o, smem + kLists, bc);
+    direct_select<MODE, NT>(src, v, n, k, o, smem + kLists, bc);
   }
   set_path(p, row, code);
 }
@@ -1100,22 +1331,36 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
   return TOPK_OK;
 }
 
-// Survivor slots per wave of the one-workgroup kernel: about 1.3 times the
-// expected survivors of a 16384-logit row plus a margin, capped so that the
-// kernel's LDS stays at 20 KB (eight rows in flight per CU).
-int row_lcw(int k) {
-  const int l = k / 2 + 96;
-  return l > 880 ? 880 : l;
+// Survivor entries per wave of the one-workgroup kernel.  A 16384-logit
+// row with the cutoff rank of sample_rank keeps about 1.2 k + 400 words
+// holding a key above the cutoff; the workgroup holds k + k/4 + 512 of
+// them, spread evenly over its waves, plus 32 per wave for imbalance.
+int row_lcw(int k, int nw) { return (k + k / 4 + 512) / nw + 32; }
+
+size_t row_lds_bytes(int lcw, int nw) {
+  const int lists = nw * (lcw + 1) * 2;
+  return (size_t)(kLists + (lists > kDirectWords ? lists : kDirectWords)) * 4;
 }
 
-size_t row_lds_bytes(int lcw) {
-  const int lists = 4 * lcw > kDirectWords ? 4 * lcw : kDirectWords;
-  return (size_t)(kLists + lists) * 4;
+// Dynamic LDS a workgroup may take on this device (cached per device).
+int device_lds_limit(int dev) {
+  static int cached[64] = {0};
+  if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev];
+  int v = 65536;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    v = 65536;
+  if (dev >= 0 && dev < 64) cached[dev] = v;
+  return v;
 }
 
 template <class K>
-int launch(K kernel, int grid, size_t lds, hipStream_t stream, const Params& p) {
-  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kNT), lds, stream, p);
+int launch(K kernel, int grid, int nt, size_t lds, hipStream_t stream, const Params& p) {
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return fail(TOPK_ERR_HIP, "LDS of %zu bytes: %s", lds, hipGetErrorString(e));
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(nt), lds, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TOPK_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
   return TOPK_OK;
@@ -1164,20 +1409,23 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.path = opt ? opt->path_codes : nullptr;
   p.force_direct = opt ? (opt->force_direct != 0) : 0;
 
+  // one workgroup of 512 threads per row while the row fits its
+  // registers: 2048 vectors (token) or 4096 (block)
   const int nvec_max = (width + 7) / 8;
-  const int cap_wg = kNT * (mode == TOPK_MODE_BLOCK ? kBlockVPT : kTokenVPT);
+  const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kBlockVPT / 2 : kTokenVPT / 2);
   if (nvec_max <= cap_wg) {
     p.rows = rows;
     p.row0 = 0;
-    p.lcw = row_lcw(k);
-    const size_t lds = row_lds_bytes(p.lcw);
+    p.lcw = row_lcw(k, kRowNT / 64);
+    const size_t lds = row_lds_bytes(p.lcw, kRowNT / 64);
     if (mode == TOPK_MODE_BLOCK)
-      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kBlockVPT>, rows, lds, stream, p);
-    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kTokenVPT>, rows, lds, stream, p);
+      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kBlockVPT / 2>, rows, kRowNT, lds, stream, p);
+    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kTokenVPT / 2>, rows, kRowNT, lds, stream, p);
   }
 
   // team path: a filter kernel (G members a row), then a select kernel
-  const int G = (nvec_max + cap_wg - 1) / cap_wg;  // <= 64, so 4 G <= kNT
+  const int cap_team = kTeamNT * (mode == TOPK_MODE_BLOCK ? kBlockVPT : kTokenVPT);
+  const int G = (nvec_max + cap_team - 1) / cap_team;  // <= 64, so 4 G <= 256
   const size_t row_bytes = (size_t)G * kMemberWords * 4;
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
   if ((size_t)batch * row_bytes > kTeamScratchMax) batch = (int)(kTeamScratchMax / row_bytes);
@@ -1187,7 +1435,13 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   if (rc != TOPK_OK) return rc;
   p.G = G;
   p.team = static_cast<uint32_t*>(scratch);
-  const size_t sel_lds = (size_t)kSelWords * 4;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  // stage as many survivor entries as the LDS of one workgroup holds
+  int cap = (device_lds_limit(dev) / 4 - kSelFixed) / 2;
+  cap = cap < kSelectMin ? kSelectMin : (cap > 32768 ? 32768 : cap);
+  p.sel_cap = cap;
+  const size_t sel_lds = (size_t)(kSelFixed + 2 * cap) * 4;
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = (rows - r0) < batch ? (rows - r0) : batch;
     p.row0 = r0;
@@ -1195,11 +1449,13 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     p.xcd_map = nr >= 8 ? 1 : 0;
     const int grid = p.xcd_map ? ((nr + 7) / 8) * 8 * G : nr * G;
     if (mode == TOPK_MODE_BLOCK) {
-      rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kBlockVPT, kBlockSV>, grid, 0, stream, p);
-      if (rc == TOPK_OK) rc = launch(topk_team_select<TOPK_MODE_BLOCK>, nr, sel_lds, stream, p);
+      rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kBlockVPT, kBlockSV>, grid, kTeamNT, 0, stream, p);
+      if (rc == TOPK_OK)
+        rc = launch(topk_team_select<TOPK_MODE_BLOCK>, nr, kSelNT, sel_lds, stream, p);
     } else {
-      rc = launch(topk_team_filter<TOPK_MODE_TOKEN, kTokenVPT, kTokenSV>, grid, 0, stream, p);
-      if (rc == TOPK_OK) rc = launch(topk_team_select<TOPK_MODE_TOKEN>, nr, sel_lds, stream, p);
+      rc = launch(topk_team_filter<TOPK_MODE_TOKEN, kTokenVPT, kTokenSV>, grid, kTeamNT, 0, stream, p);
+      if (rc == TOPK_OK)
+        rc = launch(topk_team_select<TOPK_MODE_TOKEN>, nr, kSelNT, sel_lds, stream, p);
     }
     if (rc != TOPK_OK) return rc;
   }

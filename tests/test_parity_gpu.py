@@ -174,10 +174,11 @@ def test_block_mode_page_transform():
 
 
 def _sampled_positions_wg(nvec):
-    """Positions the one-workgroup token kernel samples: element (j & 7) of
-    the vector in slot j, i.e. vector vid = j * 256 + t, element vid // 256."""
+    """Positions the one-workgroup token kernel samples: logit (j mod 8) of
+    the vector staged in slot j, i.e. logit (vid // 512) mod 8 of vector vid
+    (512-thread workgroups)."""
     vid = np.arange(nvec)
-    return vid * 8 + (vid // 256) % 8
+    return vid * 8 + (vid // 512) % 8
 
 
 def test_crafted_misjudged_row_takes_direct_path():
