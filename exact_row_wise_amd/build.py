@@ -30,6 +30,9 @@ def command(out: str = LIB, extra=()) -> list[str]:
         # no packed FP32 (the path has no floating point; keep the backend from
         # forming packed FP32 ops anywhere)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # every wave-level atomic here is already issued by one lane with the
+        # wave's total; the backend's own aggregation would only add work
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, *extra, "-o", out, SRC,
     ]

@@ -17,13 +17,15 @@
 //     over the sampled keys find it, and every wave reads the bins itself;
 //   * words holding a key above c are compacted, two logits per wave64
 //     ballot step, into the wave's own LDS region (ballot + lane-mask
-//     count, no atomic).  When c is the key of a non-negative value the
-//     test is a signed 16-bit compare of the raw bits, so the key transform
-//     is never applied to the whole row;
+//     count, no atomic).  Survivor words hold signed keys (key - 0x8000 in
+//     each half); when c is the key of a non-negative value the raw word
+//     already serves, so the key transform never touches the whole row;
 //   * the exact k-th key T over the survivors takes one pass of a
 //     1024-bin LDS histogram of (key - c), which gives T itself whenever
-//     T - c <= 1024 (else two 8-bit passes); the indices are then written
-//     from per-wave counts, again without atomics;
+//     T - c <= 1024 (else two 8-bit passes); the write pass takes slots
+//     from one LDS counter pair, one atomic per wave and 64 entries, into
+//     a k-slot LDS staging row that one coalesced pass then copies out,
+//     applying the block table;
 //   * rows whose k-th key equals the cutoff take the tie pass: every key
 //     above c, then the first keys equal to c;
 //   * a misjudged sample (fewer than k keys at or above c) or a survivor
@@ -63,7 +65,8 @@ constexpr int kTokenVPT = 8;             // 16-byte vectors per thread of a toke
 constexpr int kBlockVPT = 16;            // 16-byte vectors per thread of a block member
 constexpr int kTokenSV = 2;              // sample vectors per thread, token teams
 constexpr int kBlockSV = 4;              // sample vectors per thread, block teams
-constexpr int kTeamLCW = 512;            // survivor entries per wave of a team member
+constexpr int kTeamLCW = 512;            // survivor entries per wave region of a member
+constexpr int kSpare = 64;               // region entries past the cap (one ballot step)
 constexpr int kTieCapWave = TOPK_MAX_K / 4 + 64;  // tie indices per wave of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
 constexpr size_t kTeamScratchMax = size_t(256) << 20;
@@ -75,21 +78,26 @@ constexpr uint32_t kKeyNegInf = 0x007Fu; // key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF80u; // key(+inf): the pinned newest block
 constexpr uint32_t kKeyNaN = 0xFFFFu;    // key of the canonical positive NaN
 constexpr uint32_t kNone = 0xFFFFFFFFu;  // empty sample slot
+constexpr int32_t kSNegInf = (int32_t)kKeyNegInf - 0x8000;  // signed key of -inf
+constexpr uint32_t kDeadPair = 0x80008000u;  // two signed keys at the very bottom
 
 // LDS (32-bit words), shared by the one-workgroup and the select kernels
-constexpr int kSampHist = 0;                    // 2 x 256 bins, descending keys
-constexpr int kRelHist = kSampHist + 512;       // kRelBins bins / u16 tie list
-constexpr int kBc = kRelHist + kRelBins;        // 128 words, 16 per per-wave field
-constexpr int kLists = kBc + 128;               // survivor entries / staging / direct path
+constexpr int kBc = 0;                          // 128 words of counters and per-wave fields
+constexpr int kStage = 128;                     // k output slots, overlapping:
+constexpr int kSampHist = kStage;               //   2 x 256 sample bins, descending keys
+constexpr int kRelHist = kStage + 512;          //   kRelBins bins / u16 tie list
+constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
+static_assert(kRelHist + kRelBins <= kLists, "histograms overlap the lists");
 enum {
-  BC_CNT = 0,     // entries per wave
-  BC_ECNT = 16,   // survivor keys per wave
-  BC_CGT = 32,    // keys above T per wave
-  BC_CEQ = 48,    // keys equal to T per wave
+  BC_CNT = 0,     // 16: entries per wave
+  BC_ECNT = 16,   // 16: survivor keys per wave
+  BC_CGT = 32,    // 16: reductions
+  BC_CEQ = 48,    // 16: reductions
   BC_EQ = 64,     // tie-list counter
   BC_C1 = 65, BC_C2 = 66,   // direct-path write counters
-  BC_TMP = 80,    // 16: reductions
-  BC_X = 96       // 16: reductions
+  BC_SLOT = 68,   // 2 (8-byte aligned): output slots taken above T | equal to T
+  BC_X = 80,      // 16: reductions
+  BC_TMP = 96     // 32: reductions, bin searches
 };
 
 // One team member's slice of global scratch (32-bit words):
@@ -115,7 +123,8 @@ struct Params {
   int32_t* out;
   int32_t* path;
   int32_t force_direct;
-  int32_t lcw;         // survivor entries per wave (one-workgroup kernel)
+  int32_t out_vec;     // rows of out may be written as 16-byte vectors
+  int32_t lcw;         // survivor entries per wave before the cap (one-workgroup kernel)
   int32_t G;           // team members per row
   int32_t xcd_map;
   uint32_t* team;      // team scratch: [rows][G][kMemberWords]
@@ -137,6 +146,19 @@ __device__ __forceinline__ uint32_t key1(uint32_t x) {
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Signed keys: key - 0x8000 as a signed 16-bit number, same order as the
+// key.  For a word of two BF16 patterns that is the word with the low 15
+// bits of each negative half inverted (a non-negative half is its own
+// signed key).
+__device__ __forceinline__ uint32_t skey2(uint32_t w) {
+  const s16x2 sm = __builtin_bit_cast(s16x2, w) >> (s16x2){15, 15};
+  return w ^ (__builtin_bit_cast(uint32_t, sm) & 0x7FFF7FFFu);
+}
+
+__device__ __forceinline__ int32_t lo16s(uint32_t x) { return (int32_t)(int16_t)(x & 0xFFFFu); }
+__device__ __forceinline__ int32_t hi16s(uint32_t x) { return (int32_t)x >> 16; }
 
 __device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
@@ -211,6 +233,12 @@ __device__ __forceinline__ uint32_t popc(unsigned long long m) {
   return (uint32_t)__popcll(m);
 }
 
+// True in exactly the lanes whose bit is set in the wave-uniform mask m:
+// lets a ballot taken earlier serve as the branch mask itself.
+__device__ __forceinline__ bool in_mask(unsigned long long m) {
+  return __builtin_amdgcn_inverse_ballot_w64(m);
+}
+
 #define TOPK_DPP(x, ctrl, rmask) \
   ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(x), (ctrl), (rmask), 0xF, false))
 
@@ -228,6 +256,10 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 
 __device__ __forceinline__ uint32_t readlane(uint32_t x, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+__device__ __forceinline__ uint32_t readfirst(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
 
 // One wave over a histogram of 64*B bins whose index 0 holds the largest
@@ -333,25 +365,21 @@ struct Out {
   int32_t shift;         // log2 of the page size
   uint32_t k;            // slots of the row (writes past them are dropped)
   bool block;
+  bool vec;              // out is 16-byte aligned and k a multiple of 4
 
+  // An element index (or -1) as written: through the block table when
+  // there is one (vLLM kimi_k3 indexer, IndexerSelect.emit), -1 kept.
+  __device__ __forceinline__ int32_t map(int32_t x) const {
+    if (!pages) return x;
+    const int32_t i = x < 0 ? 0 : x;
+    const int32_t pg = pages[i >> shift];
+    return x < 0 ? -1 : (pg << shift) | (i & ((1 << shift) - 1));
+  }
   // Element index idx with key `key` into output slot pos: -1 for a -inf
-  // block; otherwise the index, through the block table when there is one
-  // (vLLM kimi_k3 indexer, IndexerSelect.emit).
+  // block, otherwise map(idx).
   __device__ __forceinline__ void put(uint32_t pos, uint32_t idx, uint32_t key) const {
     if (pos >= k) return;
-    int32_t val;
-    if (block && key == kKeyNegInf) {
-      val = -1;
-    } else if (pages) {
-      val = pages[idx >> shift] * (1 << shift) + (int32_t)(idx & ((1u << shift) - 1u));
-    } else {
-      val = (int32_t)idx;
-    }
-    out[pos] = val;
-  }
-  __device__ __forceinline__ int32_t plain(uint32_t idx) const {
-    if (pages) return pages[idx >> shift] * (1 << shift) + (int32_t)(idx & ((1u << shift) - 1u));
-    return (int32_t)idx;
+    out[pos] = (block && key == kKeyNegInf) ? -1 : map((int32_t)idx);
   }
 };
 
@@ -362,7 +390,26 @@ __device__ __forceinline__ Out row_out(const Params& p, int row, bool block) {
   o.shift = p.page_shift;
   o.k = (uint32_t)p.k;
   o.block = block;
+  o.vec = p.out_vec != 0;
   return o;
+}
+
+// The k staged slots of a row to HBM in one coalesced pass (16-byte stores
+// where the row allows), through the block table.  Follows a barrier.
+template <int NT>
+__device__ void flush_out(const int32_t* stage, const Out& o) {
+  if (o.vec) {
+    for (uint32_t e = threadIdx.x * 4u; e < o.k; e += NT * 4u) {
+      int4 v = *reinterpret_cast<const int4*>(stage + e);
+      v.x = o.map(v.x);
+      v.y = o.map(v.y);
+      v.z = o.map(v.z);
+      v.w = o.map(v.w);
+      *reinterpret_cast<int4*>(o.out + e) = v;
+    }
+  } else {
+    for (uint32_t e = threadIdx.x; e < o.k; e += NT) o.out[e] = o.map(stage[e]);
+  }
 }
 
 __device__ __forceinline__ void set_path(const Params& p, int row, int code) {
@@ -373,7 +420,7 @@ __device__ __forceinline__ void set_path(const Params& p, int row, int code) {
 // (decode_topk_cute result definition; kimi_k3 IndexerSelect bypass).
 template <int NT>
 __device__ void write_short_token(const Out& o, int n, int k) {
-  for (int e = threadIdx.x; e < k; e += NT) o.out[e] = e < n ? o.plain((uint32_t)e) : -1;
+  for (int e = threadIdx.x; e < k; e += NT) o.out[e] = o.map(e < n ? e : -1);
 }
 
 // Block rows with n <= k: every block in order, -1 for -inf blocks, the
@@ -527,187 +574,154 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_
   return (b1 << 8) | (255u - i2);
 }
 
-// Survivor compaction of one raw word (two logits): if either key is above
-// the cutoff c, the word and its word index go to this wave's region (two
-// words per entry) at the wave's running count plus its rank among the
-// lanes (ballot + lane-mask count, no atomic).  With POS (c is the key of a
-// non-negative value, craw its raw bits) the test is a signed 16-bit
-// compare of the raw halves; otherwise the halves are keyed first.
-// wcnt (entries) and ecnt (keys above c) are wave-uniform; entries past
-// lcw all land on the spare slot lcw and are detected from wcnt.
-template <bool POS>
-__device__ __forceinline__ void keep_word(uint32_t w, uint32_t widx, uint32_t c, int32_t craw,
-                                          uint32_t* seg, uint32_t lcw, uint32_t& wcnt,
+// Survivor entries: two words each, a word x of two signed keys and the
+// element index of its low half.  Token entries are two neighbouring
+// logits; a block entry holds its block's signed key in the low half and
+// the bottom key in the high half.
+//
+// Compaction of one entry: if either half of x is above the signed cutoff
+// cs, (x, eidx) goes to this wave's region at the wave's running count
+// plus the lane's rank among the kept lanes (ballot + lane-mask count, no
+// atomic).  wcnt (entries) and ecnt (keys above cs) are wave-uniform; once
+// wcnt passes cap the wave stops writing, so a region needs cap + 64
+// entries, and a final wcnt above cap means the row overflowed.
+// The region starts at entry wbase (wave-uniform) of `lists`.
+__device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs, uint32_t* lists,
+                                          uint32_t wbase, uint32_t cap, uint32_t& wcnt,
                                           uint32_t& ecnt) {
-  bool lo, hi;
-  if constexpr (POS) {
-    lo = (int32_t)(int16_t)(w & 0xFFFFu) > craw;
-    hi = (int32_t)(int16_t)(w >> 16) > craw;
-  } else {
-    const uint32_t kk = key2(w);
-    lo = (kk & 0xFFFFu) > c;
-    hi = (kk >> 16) > c;
-  }
-  const unsigned long long mlo = __ballot(lo), mhi = __ballot(hi);
+  const unsigned long long mlo = __ballot(lo16s(x) > cs), mhi = __ballot(hi16s(x) > cs);
   const unsigned long long m = mlo | mhi;
-  const uint32_t pos = min(mbcnt(m, wcnt), lcw);
-  if (lo || hi) {
-    seg[2 * pos] = w;
-    seg[2 * pos + 1] = widx;
+  if (in_mask(wcnt <= cap ? m : 0ull)) {
+    const uint32_t pos = mbcnt(m) + (wbase + wcnt);
+    *reinterpret_cast<uint2*>(lists + 2 * pos) = make_uint2(x, eidx);
   }
   wcnt += popc(m);
   ecnt += popc(mlo) + popc(mhi);
 }
 
-// The same for one block key (one element per entry: key, block index).
-__device__ __forceinline__ void keep_key(uint32_t key, uint32_t idx, uint32_t c, uint32_t* seg,
-                                         uint32_t lcw, uint32_t& wcnt) {
-  const bool gt = key > c;
-  const unsigned long long m = __ballot(gt);
-  const uint32_t pos = min(mbcnt(m, wcnt), lcw);
-  if (gt) {
-    seg[2 * pos] = key;
-    seg[2 * pos + 1] = idx;
-  }
-  wcnt += popc(m);
-}
-
-// Survivor entries: two words each; token entries are (raw word, word
-// index) holding two candidate keys, block entries (key, block index).
-template <int MODE>
-struct EntryView {
-  const uint32_t* e;
-  __device__ __forceinline__ void keys(uint32_t i, uint32_t& k0, uint32_t& k1) const {
-    if constexpr (MODE == TOPK_MODE_TOKEN) {
-      const uint32_t kk = key2(e[2 * i]);
-      k0 = kk & 0xFFFFu;
-      k1 = kk >> 16;
-    } else {
-      k0 = e[2 * i];
-      k1 = 0u;
-    }
-  }
-  __device__ __forceinline__ uint32_t idx(uint32_t i, uint32_t h) const {
-    if constexpr (MODE == TOPK_MODE_TOKEN) return 2u * e[2 * i + 1] + h;
-    return e[2 * i + 1];
-  }
-};
+// Block entries: signed key in the low half, the bottom key above it.
+__device__ __forceinline__ uint32_t block_entry(uint32_t key) { return key ^ kDeadPair; }
 
 // Exact k-th key T over the survivor entries spread over the waves (every
-// candidate key above the cutoff c counts; at least k of them), then the
-// write.  Wave w sees `cnt` entries; `rel` is a zeroed kRelBins histogram
-// and `sh` 512 free words.  The bins of (key - c - 1), largest first, give
-// T exactly unless T - c > kRelBins (then two 8-bit passes over the keys
-// above c + kRelBins).  Keys above T take the slots [0, cgt), the first
-// keys equal to T the slots after, from per-wave counts (one barrier, no
-// atomics).
+// key above the signed cutoff cs counts; at least k of them), then the
+// write into the k staged slots.  Wave w sees `cnt` entries at e; `rel` is
+// a zeroed kRelBins histogram, `sh` 512 free words, bc[BC_SLOT..+1] zero.
+// The bins of (key - cs - 1), largest first, give T exactly unless
+// T > cs + kRelBins (then two 8-bit passes over the keys above that).  The
+// keys above T take the slots [0, cgt) and the first keys equal to T the
+// slots [cgt, k), in the order the wave-level slot atomics hand them out.
+// rel and sh overlap the staging slots.
 template <int MODE, int NW>
-__device__ void select_and_write(EntryView<MODE> v, uint32_t cnt, uint32_t c, uint32_t k,
-                                 uint32_t* rel, uint32_t* sh, uint32_t* bc, const Out& o) {
+__device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t k,
+                                 uint32_t* rel, uint32_t* sh, uint32_t* bc, int32_t* stage) {
   const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
     if (i < cnt) {
-      uint32_t k0, k1;
-      v.keys(i, k0, k1);
-      if (k0 > c) atomicAdd(&rel[(kRelBins - 1) - min(k0 - c - 1u, (uint32_t)(kRelBins - 1))], 1u);
-      if (k1 > c) atomicAdd(&rel[(kRelBins - 1) - min(k1 - c - 1u, (uint32_t)(kRelBins - 1))], 1u);
+      const uint32_t x = e[2 * i];
+      const int32_t s0 = lo16s(x), s1 = hi16s(x);
+      if (s0 > cs) atomicAdd(&rel[max(top - s0, 0)], 1u);
+      if (s1 > cs) atomicAdd(&rel[max(top - s1, 0)], 1u);
     }
   }
   __syncthreads();
   uint32_t ri, above;
   find_block<64 * NW, kRelBins / (64 * NW)>(rel, k, bc + BC_TMP, ri, above);
-  uint32_t T, cgt;
+  int32_t Ts;
+  uint32_t cgt;
   if (ri != 0) {
-    T = c + (uint32_t)kRelBins - ri;
+    Ts = top - (int32_t)ri;
     cgt = above;
   } else {
-    // the k-th key is at least c + kRelBins: 8-bit passes over those keys
-    const uint32_t floor = c + (uint32_t)kRelBins;
+    // the k-th key lies at or above top: 8-bit passes over those keys
     for (int i = threadIdx.x; i < 512; i += 64 * NW) sh[i] = 0;
     __syncthreads();
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
       if (i < cnt) {
-        uint32_t k0, k1;
-        v.keys(i, k0, k1);
-        if (k0 >= floor) atomicAdd(&sh[255u - (k0 >> 8)], 1u);
-        if (k1 >= floor) atomicAdd(&sh[255u - (k1 >> 8)], 1u);
+        const uint32_t x = e[2 * i];
+        const int32_t s0 = lo16s(x), s1 = hi16s(x);
+        if (s0 >= top) atomicAdd(&sh[255 - ((s0 + 0x8000) >> 8)], 1u);
+        if (s1 >= top) atomicAdd(&sh[255 - ((s1 + 0x8000) >> 8)], 1u);
       }
     }
     __syncthreads();
     uint32_t i1, a1, i2, a2;
     find_desc<4>(sh, k, i1, a1);
-    const uint32_t b1 = 255u - i1;
+    const int32_t b1 = 255 - (int32_t)i1;
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
       if (i < cnt) {
-        uint32_t k0, k1;
-        v.keys(i, k0, k1);
-        if (k0 >= floor && (k0 >> 8) == b1) atomicAdd(&sh[256 + 255u - (k0 & 255u)], 1u);
-        if (k1 >= floor && (k1 >> 8) == b1) atomicAdd(&sh[256 + 255u - (k1 & 255u)], 1u);
+        const uint32_t x = e[2 * i];
+        const int32_t s0 = lo16s(x) + 0x8000, s1 = hi16s(x) + 0x8000;
+        if (s0 >= top + 0x8000 && (s0 >> 8) == b1) atomicAdd(&sh[256 + 255 - (s0 & 255)], 1u);
+        if (s1 >= top + 0x8000 && (s1 >> 8) == b1) atomicAdd(&sh[256 + 255 - (s1 & 255)], 1u);
       }
     }
     __syncthreads();
     find_desc<4>(sh + 256, k - a1, i2, a2);
-    T = (b1 << 8) | (255u - i2);
+    Ts = ((b1 << 8) | (255 - (int32_t)i2)) - 0x8000;
     cgt = a1 + a2;
+    __syncthreads();  // every wave has read sh before the slots overwrite it
   }
   const uint32_t take = k - cgt;
-  uint32_t ngt = 0, neq = 0;
+  unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
-    uint32_t k0 = 0, k1 = 0;
-    if (i < cnt) v.keys(i, k0, k1);
-    ngt += popc(__ballot(k0 > T)) + popc(__ballot(k1 > T));
-    neq += popc(__ballot(k0 == T)) + popc(__ballot(k1 == T));
-  }
-  if (lane == 0) {
-    bc[BC_CGT + wave] = ngt;
-    bc[BC_CEQ + wave] = neq;
-  }
-  __syncthreads();
-  uint32_t bgt = 0, beq = 0;
-  for (int w = 0; w < wave; ++w) {
-    bgt += bc[BC_CGT + w];
-    beq += bc[BC_CEQ + w];
-  }
-  for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
-    const uint32_t i = b0 + lane;
-    uint32_t k0 = 0, k1 = 0;
-    if (i < cnt) v.keys(i, k0, k1);
-    const bool g0 = k0 > T, g1 = k1 > T, e0 = k0 == T, e1 = k1 == T;
-    const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
-    const unsigned long long me0 = __ballot(e0), me1 = __ballot(e1);
-    const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, bgt));
-    if (g0) o.put(p0, v.idx(i, 0), k0);
-    if (g1) o.put(p0 + (g0 ? 1u : 0u), v.idx(i, 1), k1);
-    const uint32_t q0 = mbcnt(me1, mbcnt(me0, beq));
-    if (e0 && q0 < take) o.put(cgt + q0, v.idx(i, 0), k0);
-    const uint32_t q1 = q0 + (e0 ? 1u : 0u);
-    if (e1 && q1 < take) o.put(cgt + q1, v.idx(i, 1), k1);
-    bgt += popc(mg0) + popc(mg1);
-    beq += popc(me0) + popc(me1);
+    uint32_t x = kDeadPair, id = 0;
+    if (i < cnt) {
+      x = e[2 * i];
+      id = e[2 * i + 1];
+    }
+    const int32_t s0 = lo16s(x), s1 = hi16s(x);
+    const unsigned long long g0 = __ballot(s0 > Ts), g1 = __ballot(s1 > Ts);
+    const unsigned long long q0 = __ballot(s0 == Ts), q1 = __ballot(s1 == Ts);
+    const uint32_t ng = popc(g0) + popc(g1), nq = popc(q0) + popc(q1);
+    if (ng + nq == 0) continue;
+    unsigned long long base = 0;
+    if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
+    const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
+    int32_t v0 = (int32_t)id, v1 = (int32_t)id + 1;
+    if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
+    if (in_mask(g0)) stage[bg + mbcnt(g0)] = v0;
+    if (in_mask(g1)) stage[bg + popc(g0) + mbcnt(g1)] = v1;
+    if (nq) {
+      const uint32_t p0 = bq + mbcnt(q0);
+      if (in_mask(q0) && p0 < take) stage[cgt + p0] = v0;
+      const uint32_t p1 = bq + popc(q0) + mbcnt(q1);
+      if (in_mask(q1) && p1 < take) stage[cgt + p1] = v1;
+    }
   }
 }
 
-// Every survivor key (above c) of the entries at [base, ...) in order: the
-// tie pass's first part.  Positions come from per-wave key counts.
+// Every survivor key above cs of the entries at e, in order, into slots
+// from `base` on: the tie pass's first part.  Into the staging slots when
+// `stage` is given, else straight out.
 template <int MODE>
-__device__ void write_above(EntryView<MODE> v, uint32_t cnt, uint32_t c, uint32_t base,
-                            const Out& o) {
+__device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t ibase,
+                            uint32_t base, int32_t* stage, const Out& o) {
   const int lane = __lane_id();
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
-    uint32_t k0 = 0, k1 = 0;
-    if (i < cnt) v.keys(i, k0, k1);
-    const bool g0 = k0 > c, g1 = k1 > c;
-    const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
-    const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, base));
-    if (g0) o.put(p0, v.idx(i, 0), k0);
-    if (g1) o.put(p0 + (g0 ? 1u : 0u), v.idx(i, 1), k1);
-    base += popc(mg0) + popc(mg1);
+    uint32_t x = kDeadPair, id = 0;
+    if (i < cnt) {
+      x = e[2 * i];
+      id = e[2 * i + 1] + ibase;
+    }
+    const int32_t s0 = lo16s(x), s1 = hi16s(x);
+    const unsigned long long g0 = __ballot(s0 > cs), g1 = __ballot(s1 > cs);
+    const uint32_t p0 = mbcnt(g0, base), p1 = mbcnt(g1, base + popc(g0));
+    int32_t v0 = (int32_t)id;
+    if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
+    if (stage) {
+      if (in_mask(g0)) stage[p0] = v0;
+      if (in_mask(g1)) stage[p1] = (int32_t)id + 1;
+    } else {
+      if (in_mask(g0)) o.put(p0, id, (uint32_t)(s0 + 0x8000));
+      if (in_mask(g1)) o.put(p1, id + 1, (uint32_t)(s1 + 0x8000));
+    }
+    base += popc(g0) + popc(g1);
   }
 }
 
@@ -754,6 +768,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
   uint32_t* lists = smem + kLists;
+  int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
 
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
@@ -767,8 +782,12 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     const int nvec = (v + 7) >> 3;
     const int jt = (nvec - 1) / NT;   // last vector slot holding row data
     const int rem = nvec - jt * NT;   // vectors in it
-    for (int i = tid; i < 512 + kRelBins; i += NT) smem[i] = 0;  // sample + relative hists
-    if (tid == 0) bc[BC_EQ] = 0;
+    for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;  // sample + relative hists
+    if (tid == 0) {
+      bc[BC_EQ] = 0;
+      bc[BC_SLOT] = 0;
+      bc[BC_SLOT + 1] = 0;
+    }
 
     // -- stage the row: 16-byte loads into VGPRs
     uint4 raw[VPT];
@@ -810,38 +829,42 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     const uint32_t c = sample_cutoff(sk, q, sh);
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
-      // a zero cutoff would admit the zero keys of slots past the length
+      // a zero cutoff would make the zero keys of slots past the length ties
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
     } else {
-      // -- filter + compaction of the words holding a key above the cutoff
-      const uint32_t lcw = (uint32_t)p.lcw;
-      uint32_t* seg = lists + wave * (lcw + 1) * 2;
+      // -- filter + compaction of the entries holding a key above the cutoff
+      const int32_t cs = (int32_t)c - 0x8000;
+      const uint32_t cap = (uint32_t)p.lcw;
+      const uint32_t wbase = readfirst((uint32_t)wave) * (cap + kSpare);
+      uint32_t* seg = lists + 2 * wbase;
       uint32_t wcnt = 0, ecnt = 0;
       if constexpr (MODE == TOPK_MODE_BLOCK) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
-          if (j <= jt) keep_key(kb[j], (uint32_t)slot_vid<NT>(j, jt, rem), c, seg, lcw, wcnt);
-        ecnt = wcnt;
-      } else if (c >= 0x8000u) {
-        const int32_t craw = (int32_t)(c - 0x8000u);
+          if (j <= jt)
+            keep_word(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, lists, wbase,
+                      cap, wcnt, ecnt);
+      } else if (cs >= 0) {
+        // non-negative cutoff: the raw words serve as signed keys
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
           if (j <= jt) {
-            const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+            const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word<true>(word_of(raw[j], q2), w4 + q2, c, craw, seg, lcw, wcnt, ecnt);
+              keep_word(word_of(raw[j], q2), e8 + 2 * q2, cs, lists, wbase, cap, wcnt, ecnt);
           }
         }
       } else {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
           if (j <= jt) {
-            const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+            const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word<false>(word_of(raw[j], q2), w4 + q2, c, 0, seg, lcw, wcnt, ecnt);
+              keep_word(skey2(word_of(raw[j], q2)), e8 + 2 * q2, cs, lists, wbase, cap, wcnt,
+                        ecnt);
           }
         }
       }
@@ -857,15 +880,16 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
         const uint32_t ew = bc[BC_ECNT + w];
         before += w < wave ? ew : 0u;
         gt_total += ew;
-        ovf |= bc[BC_CNT + w] > lcw;
+        ovf |= bc[BC_CNT + w] > cap;
       }
-      const uint32_t nent = min(wcnt, lcw);
       if (ovf) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
       } else if (gt_total >= (uint32_t)k) {
         // the k-th key lies above the cutoff: exact select over the survivors
-        select_and_write<MODE, NW>(EntryView<MODE>{seg}, nent, c, (uint32_t)k, rel, sh, bc, o);
+        select_and_write<MODE, NW>(seg, wcnt, cs, (uint32_t)k, rel, sh, bc, stage);
+        __syncthreads();
+        flush_out<NT>(stage, o);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key can only be the cutoff: collect keys equal to it
@@ -891,7 +915,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
           direct = true;
           code = TOPK_PATH_DIRECT_MISJUDGED;
         } else {
-          write_above<MODE>(EntryView<MODE>{seg}, nent, c, before, o);
+          write_above<MODE>(seg, wcnt, cs, 0u, before, nullptr, o);
           const uint32_t take = (uint32_t)k - gt_total;
           for (uint32_t i = tid; i < take; i += NT) o.put(gt_total + i, ties[i], c);
           code = TOPK_PATH_SAMPLED_TIES;
@@ -909,9 +933,9 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 // ============================================ team of workgroups per row
 // Stage 1: every member of a row's team stages its chunk of the row (the
 // chunks split the valid length), derives the row's cutoff from samples
-// spread over the whole row (the same in every member), and writes the
-// words holding keys above it, and if any, the indices of keys equal to
-// it, to its scratch slice.
+// spread over the whole row (the same in every member), and writes its
+// survivor entries (chunk-local indices) and, if any, the indices of keys
+// equal to the cutoff to its scratch slice.
 template <int MODE, int VPT, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
@@ -1008,7 +1032,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
   const uint32_t c = sample_cutoff(sk, q, sh);
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
-    // a zero cutoff would admit the zero keys of slots past the length:
+    // a zero cutoff would make the zero keys of slots past the length ties:
     // every member sees the same cutoff and flags the row for the direct path
     if (tid == 0) {
       slice[12] = c;
@@ -1017,45 +1041,32 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     return;
   }
 
-  // -- the words above the cutoff go straight to this wave's scratch region
-  uint32_t* seg = slice + kMemberHdr + wave * 2 * kTeamLCW;
-  const uint32_t lcw = kTeamLCW - 1;  // the last entry is the spare slot
+  // -- the entries above the cutoff go straight to this wave's scratch region
+  const int32_t cs = (int32_t)c - 0x8000;
+  uint32_t* seg = slice + kMemberHdr;
+  const uint32_t wbase = readfirst((uint32_t)wave) * kTeamLCW;
+  const uint32_t cap = kTeamLCW - kSpare;
   uint32_t wcnt = 0, ecnt = 0, neq = 0;
   if constexpr (MODE == TOPK_MODE_BLOCK) {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       if (j <= jt) {
-        keep_key(kb[j], (uint32_t)slot_vid<NT>(j, jt, rem), c, seg, lcw, wcnt);
+        keep_word(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, seg, wbase, cap,
+                  wcnt, ecnt);
         neq += popc(__ballot(kb[j] == c));
-      }
-    }
-    ecnt = wcnt;
-  } else if (c >= 0x8000u) {
-    const int32_t craw = (int32_t)(c - 0x8000u);
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (j <= jt) {
-        const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const uint32_t w = word_of(raw[j], q2);
-          keep_word<true>(w, w4 + q2, c, craw, seg, lcw, wcnt, ecnt);
-          neq += popc(__ballot((w & 0xFFFFu) == (uint32_t)craw)) +
-                 popc(__ballot((w >> 16) == (uint32_t)craw));
-        }
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       if (j <= jt) {
-        const uint32_t w4 = (uint32_t)slot_vid<NT>(j, jt, rem) * 4u;
+        const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           const uint32_t w = word_of(raw[j], q2);
-          keep_word<false>(w, w4 + q2, c, 0, seg, lcw, wcnt, ecnt);
-          const uint32_t kk = key2(w);
-          neq += popc(__ballot((kk & 0xFFFFu) == c)) + popc(__ballot((kk >> 16) == c));
+          const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
+          keep_word(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
+          neq += popc(__ballot(lo16s(x) == cs)) + popc(__ballot(hi16s(x) == cs));
         }
       }
     }
@@ -1072,18 +1083,18 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     // second pass: chunk-local indices of keys equal to the cutoff
     uint16_t* tseg =
         reinterpret_cast<uint16_t*>(slice + kMemberHdr + 8 * kTeamLCW) + wave * kTieCapWave;
-    const uint32_t cap = tie_cap(k);
+    const uint32_t tcap = tie_cap(k);
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       if (j <= jt) {
         const int lvid = slot_vid<NT>(j, jt, rem);
         if constexpr (MODE == TOPK_MODE_BLOCK) {
-          keep_tie(kb[j] == c, (uint32_t)lvid, tseg, cap, tcnt);
+          keep_tie(kb[j] == c, (uint32_t)lvid, tseg, tcap, tcnt);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
             keep_tie(key1(half_of(word_of(raw[j], e >> 1), e & 1)) == c,
-                     (uint32_t)(lvid * 8 + e), tseg, cap, tcnt);
+                     (uint32_t)(lvid * 8 + e), tseg, tcap, tcnt);
         }
       }
     }
@@ -1138,19 +1149,26 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
+  int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
   uint32_t* segc = smem + kLists + kSelSegc;
   uint32_t* start = smem + kLists + kSelStart;
   uint32_t* estart = smem + kLists + kSelEstart;
   uint32_t* tstart = smem + kLists + kSelTstart;
-  uint32_t* stage = smem + kLists + kSelStage;
+  uint32_t* ent = smem + kLists + kSelStage;
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
   if (!direct) {
     const uint32_t* slices = p.team + (size_t)lrow * G * kMemberWords;
     const int nvec = (v + 7) >> 3;
     const uint32_t per = (uint32_t)((nvec + G - 1) / G);
+    // chunk starts in element units: 8 logits per vector, one block per vector
+    const uint32_t chunk = per * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
     const int nseg = 4 * G;  // <= 256: waves 0..3 hold one segment per lane
-    for (int i = tid; i < 512 + kRelBins; i += NT) smem[i] = 0;
+    for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;
+    if (tid == 0) {
+      bc[BC_SLOT] = 0;
+      bc[BC_SLOT + 1] = 0;
+    }
     uint32_t wc = 0, ec = 0, tc = 0, tcp = 0, bad = 0;
     if (tid < nseg) {
       const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
@@ -1162,7 +1180,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         ec = hdr[4 + w];
         tc = hdr[8 + w];
         tcp = min(tc, tie_cap(k));
-        bad = wc > (uint32_t)(kTeamLCW - 1) ? 1u : 0u;
+        bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
       }
       segc[tid] = wc;
     }
@@ -1201,8 +1219,8 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       tstart[0] = 0;
     }
     const uint32_t c = slices[12];
+    const int32_t cs = (int32_t)c - 0x8000;
     __syncthreads();
-    const uint32_t gscale = (MODE == TOPK_MODE_BLOCK) ? 1u : 4u;  // entry index units
     if (flags & 2u) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
@@ -1221,19 +1239,21 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         for (int s = wave; s < nseg; s += NW) {
           const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
                                (s & 3) * 2 * kTeamLCW;
-          const uint32_t gbase = (uint32_t)(s >> 2) * per * gscale;
-          const uint32_t cs = segc[s], d0 = start[s];
-          for (uint32_t i = lane; i < cs; i += 64) {
-            stage[2 * (d0 + i)] = es[2 * i];
-            stage[2 * (d0 + i) + 1] = es[2 * i + 1] + gbase;
+          const uint32_t gbase = (uint32_t)(s >> 2) * chunk;
+          const uint32_t cs_ = segc[s], d0 = start[s];
+          for (uint32_t i = lane; i < cs_; i += 64) {
+            const uint2 en = *reinterpret_cast<const uint2*>(es + 2 * i);
+            ent[2 * (d0 + i)] = en.x;
+            ent[2 * (d0 + i) + 1] = en.y + gbase;
           }
         }
         __syncthreads();
         const uint32_t share = (E + NW - 1) / NW;
         const uint32_t lo = min((uint32_t)wave * share, E);
         const uint32_t hi = min(lo + share, E);
-        select_and_write<MODE, NW>(EntryView<MODE>{stage + 2 * lo}, hi - lo, c, (uint32_t)k,
-                                   rel, sh, bc, o);
+        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage);
+        __syncthreads();
+        flush_out<NT>(stage, o);
         code = TOPK_PATH_SAMPLED;
       }
     } else {
@@ -1246,33 +1266,19 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         for (int s = wave; s < nseg; s += NW) {
           const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
                                (s & 3) * 2 * kTeamLCW;
-          const uint32_t gbase = (uint32_t)(s >> 2) * per * gscale;
-          const uint32_t cs = segc[s];
-          uint32_t base = estart[s];
-          for (uint32_t b0 = 0; b0 < cs; b0 += 64) {
-            const uint32_t i = b0 + lane;
-            uint32_t k0 = 0, k1 = 0, id = 0;
-            if (i < cs) {
-              EntryView<MODE>{es}.keys(i, k0, k1);
-              id = es[2 * i + 1] + gbase;
-            }
-            const bool g0 = k0 > c, g1 = k1 > c;
-            const unsigned long long mg0 = __ballot(g0), mg1 = __ballot(g1);
-            const uint32_t p0 = mbcnt(mg1, mbcnt(mg0, base));
-            const uint32_t i0 = (MODE == TOPK_MODE_TOKEN) ? 2u * id : id;
-            if (g0) o.put(p0, i0, k0);
-            if (g1) o.put(p0 + (g0 ? 1u : 0u), i0 + 1u, k1);
-            base += popc(mg0) + popc(mg1);
-          }
+          write_above<MODE>(es, segc[s], cs, (uint32_t)(s >> 2) * chunk, estart[s], stage, o);
         }
-        const uint32_t escale = (MODE == TOPK_MODE_BLOCK) ? 1u : 8u;  // element index units
+        const int32_t tv = (MODE == TOPK_MODE_BLOCK && c == kKeyNegInf) ? -1 : 0;
         for (uint32_t j = tid; j < take; j += NT) {
           const int s = find_segment(tstart, nseg, j);
           const uint16_t* tl = reinterpret_cast<const uint16_t*>(
                                    slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
                                    8 * kTeamLCW) + (s & 3) * kTieCapWave;
-          o.put(gt_total + j, (uint32_t)(s >> 2) * per * escale + tl[j - tstart[s]], c);
+          const int32_t idx = (int32_t)((uint32_t)(s >> 2) * chunk + tl[j - tstart[s]]);
+          stage[gt_total + j] = tv < 0 ? -1 : idx;
         }
+        __syncthreads();
+        flush_out<NT>(stage, o);
         code = TOPK_PATH_SAMPLED_TIES;
       }
     }
@@ -1331,14 +1337,15 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
   return TOPK_OK;
 }
 
-// Survivor entries per wave of the one-workgroup kernel.  A 16384-logit
-// row with the cutoff rank of sample_rank keeps about 1.2 k + 400 words
-// holding a key above the cutoff; the workgroup holds k + k/4 + 512 of
-// them, spread evenly over its waves, plus 32 per wave for imbalance.
+// Survivor entries per wave of the one-workgroup kernel before a wave
+// stops writing (its region holds kSpare more).  A 16384-logit row with
+// the cutoff rank of sample_rank keeps about 1.2 k + 400 entries holding a
+// key above the cutoff; the workgroup takes k + k/4 + 512 of them, spread
+// evenly over its waves, plus 32 per wave for imbalance.
 int row_lcw(int k, int nw) { return (k + k / 4 + 512) / nw + 32; }
 
 size_t row_lds_bytes(int lcw, int nw) {
-  const int lists = nw * (lcw + 1) * 2;
+  const int lists = nw * (lcw + kSpare) * 2;
   return (size_t)(kLists + (lists > kDirectWords ? lists : kDirectWords)) * 4;
 }
 
@@ -1408,6 +1415,7 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.out = out;
   p.path = opt ? opt->path_codes : nullptr;
   p.force_direct = opt ? (opt->force_direct != 0) : 0;
+  p.out_vec = (((uintptr_t)out & 15u) == 0 && (k & 3) == 0) ? 1 : 0;
 
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
