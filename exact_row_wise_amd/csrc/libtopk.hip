@@ -61,13 +61,16 @@ constexpr int kCopies = 8;               // replicated bins of whole-row histogr
 constexpr int kTeamNT = 256;             // filter workgroup size
 constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
-constexpr int kTokenVPT = 8;             // 16-byte vectors per thread of a token member
-constexpr int kBlockVPT = 16;            // 16-byte vectors per thread of a block member
-constexpr int kTokenSV = 2;              // sample vectors per thread, token teams
-constexpr int kBlockSV = 4;              // sample vectors per thread, block teams
+constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
+constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
+constexpr int kTeamTokenVPT = 4;         // 16-byte vectors per thread of a token work item
+constexpr int kTeamBlockVPT = 16;        // 16-byte vectors per thread of a block work item
+constexpr int kTokenSV = 1;              // sample vectors per thread, token cutoff kernel
+constexpr int kBlockSV = 4;              // sample vectors per thread, block cutoff kernel
+constexpr int kMaxItems = 256;           // work items of one row at most (4 per item <= 1024 segments)
 constexpr int kTeamLCW = 512;            // survivor entries per wave region of a member
 constexpr int kSpare = 64;               // region entries past the cap (one ballot step)
-constexpr int kTieCapWave = TOPK_MAX_K / 4 + 64;  // tie indices per wave of a member
+constexpr int kTieLCW = TOPK_MAX_K / 4 + 128;     // tie entries per wave region of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
 constexpr size_t kTeamScratchMax = size_t(256) << 20;
 constexpr int kRelBins = 1024;           // histogram bins of (key - cutoff)
@@ -100,14 +103,21 @@ enum {
   BC_TMP = 96     // 32: reductions, bin searches
 };
 
-// One team member's slice of global scratch (32-bit words):
-//   [0, 4)  survivor entries of each wave     [4, 8)  survivor keys of each wave
-//   [8, 12) keys equal to the cutoff per wave [12] the cutoff  [13] flags
-//   [16, 16 + 8 kTeamLCW) the waves' survivor entries (2 words each)
-//   then the waves' tie lists (kTieCapWave chunk-local u16 indices each)
-constexpr int kMemberHdr = 16;
-constexpr int kMemberWords = kMemberHdr + 4 * 2 * kTeamLCW + 4 * kTieCapWave / 2;
+// One work item's slice of global scratch (32-bit words), per wave w:
+//   [w]      survivor entries            [4 + w]  keys above the cutoff
+//   [8 + w]  tie entries                 [12 + w] keys equal to the cutoff in them
+//   [16 + w] keys equal to the cutoff
+//   [32, 32 + 8 kTeamLCW) the waves' survivor entries (2 words each)
+//   then the waves' tie entries (kTieLCW each, 2 words each)
+constexpr int kMemberHdr = 32;
+constexpr int kMemberWords = kMemberHdr + 4 * 2 * kTeamLCW + 4 * 2 * kTieLCW;
+constexpr int H_WCNT = 0, H_ECNT = 4, H_TW = 8, H_TKEPT = 12, H_NEQ = 16;
 constexpr uint32_t kFlagDirect = 1u;
+static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamTokenVPT - 1) / (kTeamNT * kTeamTokenVPT) <= kMaxItems,
+              "too many token work items per row");
+static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) / (kTeamNT * kTeamBlockVPT) <= kMaxItems,
+              "too many block work items per row");
+static_assert(4 * kMaxItems <= kSelNT, "one select thread per segment");
 
 struct Params {
   const uint16_t* logits;
@@ -125,10 +135,13 @@ struct Params {
   int32_t force_direct;
   int32_t out_vec;     // rows of out may be written as 16-byte vectors
   int32_t lcw;         // survivor entries per wave before the cap (one-workgroup kernel)
-  int32_t G;           // team members per row
-  int32_t xcd_map;
-  uint32_t* team;      // team scratch: [rows][G][kMemberWords]
-  int32_t sel_cap;     // survivor entries the select kernel stages in LDS
+  // team path (rows wider than one workgroup), all in one scratch buffer:
+  uint32_t* team_info;   // [rows][4]: cutoff, flags, first work item, work items
+  uint32_t* team_items;  // [max items]: the row of each work item
+  uint32_t* team_total;  // work items of the launch
+  uint32_t* team_slices; // [max items][kMemberWords]
+  int32_t team_cv;       // 16-byte vectors of one work item
+  int32_t sel_cap;       // survivor entries the select kernel stages in LDS
 };
 
 // ------------------------------------------------------------------ keys
@@ -145,7 +158,6 @@ __device__ __forceinline__ uint32_t key1(uint32_t x) {
   return (x & 0x8000u) ? (x ^ 0xFFFFu) : (x ^ 0x8000u);
 }
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 // Signed keys: key - 0x8000 as a signed 16-bit number, same order as the
@@ -160,26 +172,27 @@ __device__ __forceinline__ uint32_t skey2(uint32_t w) {
 __device__ __forceinline__ int32_t lo16s(uint32_t x) { return (int32_t)(int16_t)(x & 0xFFFFu); }
 __device__ __forceinline__ int32_t hi16s(uint32_t x) { return (int32_t)x >> 16; }
 
-__device__ __forceinline__ uint32_t pk_max(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
+__device__ __forceinline__ uint32_t pk_max_s(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, a),
+                                                                __builtin_bit_cast(s16x2, b)));
 }
-__device__ __forceinline__ uint32_t pk_min(uint32_t a, uint32_t b) {
-  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
-                                                                __builtin_bit_cast(u16x2, b)));
+__device__ __forceinline__ uint32_t pk_min_s(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(s16x2, a),
+                                                                __builtin_bit_cast(s16x2, b)));
 }
 
 // Key of the NaN-propagating maximum of the 8 logits of one 16-byte vector
 // (decode_topk_cute, block_key / max_nan_bf16x2): a NaN of either sign
 // anywhere gives the canonical positive NaN; otherwise the largest key.
-// In key space a NaN is a key above key(+inf) or below key(-inf).
+// Taken over signed keys with packed 16-bit max/min: a NaN is a signed key
+// above that of +inf or below that of -inf.
 __device__ __forceinline__ uint32_t block_key4(uint4 v) {
-  const uint32_t a = key2(v.x), b = key2(v.y), c = key2(v.z), d = key2(v.w);
-  const uint32_t mx = pk_max(pk_max(a, b), pk_max(c, d));
-  const uint32_t mn = pk_min(pk_min(a, b), pk_min(c, d));
-  const uint32_t hi = max(mx & 0xFFFFu, mx >> 16);
-  const uint32_t lo = min(mn & 0xFFFFu, mn >> 16);
-  return (hi > kKeyPosInf || lo < kKeyNegInf) ? kKeyNaN : hi;
+  const uint32_t a = skey2(v.x), b = skey2(v.y), c = skey2(v.z), d = skey2(v.w);
+  const uint32_t mx = pk_max_s(pk_max_s(a, b), pk_max_s(c, d));
+  const uint32_t mn = pk_min_s(pk_min_s(a, b), pk_min_s(c, d));
+  const int32_t hi = max(lo16s(mx), hi16s(mx));
+  const int32_t lo = min(lo16s(mn), hi16s(mn));
+  return (hi > (int32_t)kKeyPosInf - 0x8000 || lo < kSNegInf) ? kKeyNaN : (uint32_t)(hi + 0x8000);
 }
 
 __device__ __forceinline__ uint32_t half_of(uint32_t w, int h) {
@@ -602,6 +615,48 @@ __device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs,
 // Block entries: signed key in the low half, the bottom key above it.
 __device__ __forceinline__ uint32_t block_entry(uint32_t key) { return key ^ kDeadPair; }
 
+// Output slots of the keys above a threshold Ts and of the keys equal to
+// it, from the entries at e: per 64 entries a wave takes its slots with one
+// 64-bit LDS atomic on `slot` (keys above in the low word, equal in the
+// high word).  Keys above take stage[slot], keys equal stage[cgt + slot]
+// while the slot is below `take`.  Block entries of -inf blocks stage -1.
+template <int MODE, bool GT, bool EQ>
+__device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32_t cgt,
+                             uint32_t take, int32_t* stage, unsigned long long* slot) {
+  const int lane = __lane_id();
+  for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
+    const uint32_t i = b0 + lane;
+    uint32_t x = kDeadPair, id = 0;
+    if (i < cnt) {
+      x = e[2 * i];
+      id = e[2 * i + 1];
+    }
+    const int32_t s0 = lo16s(x), s1 = hi16s(x);
+    const unsigned long long g0 = GT ? __ballot(s0 > Ts) : 0ull;
+    const unsigned long long g1 = GT ? __ballot(s1 > Ts) : 0ull;
+    const unsigned long long q0 = EQ ? __ballot(s0 == Ts) : 0ull;
+    const unsigned long long q1 = EQ ? __ballot(s1 == Ts) : 0ull;
+    const uint32_t ng = popc(g0) + popc(g1), nq = popc(q0) + popc(q1);
+    if (ng + nq == 0) continue;
+    unsigned long long base = 0;
+    if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
+    const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
+    int32_t v0 = (int32_t)id;
+    const int32_t v1 = (int32_t)id + 1;
+    if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
+    if (GT && ng) {
+      if (in_mask(g0)) stage[bg + mbcnt(g0)] = v0;
+      if (in_mask(g1)) stage[bg + popc(g0) + mbcnt(g1)] = v1;
+    }
+    if (EQ && nq) {
+      const uint32_t p0 = bq + mbcnt(q0);
+      if (in_mask(q0) && p0 < take) stage[cgt + p0] = v0;
+      const uint32_t p1 = bq + popc(q0) + mbcnt(q1);
+      if (in_mask(q1) && p1 < take) stage[cgt + p1] = v1;
+    }
+  }
+}
+
 // Exact k-th key T over the survivor entries spread over the waves (every
 // key above the signed cutoff cs counts; at least k of them), then the
 // write into the k staged slots.  Wave w sees `cnt` entries at e; `rel` is
@@ -609,8 +664,7 @@ __device__ __forceinline__ uint32_t block_entry(uint32_t key) { return key ^ kDe
 // The bins of (key - cs - 1), largest first, give T exactly unless
 // T > cs + kRelBins (then two 8-bit passes over the keys above that).  The
 // keys above T take the slots [0, cgt) and the first keys equal to T the
-// slots [cgt, k), in the order the wave-level slot atomics hand them out.
-// rel and sh overlap the staging slots.
+// slots [cgt, k).  rel and sh overlap the staging slots.
 template <int MODE, int NW>
 __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t k,
                                  uint32_t* rel, uint32_t* sh, uint32_t* bc, int32_t* stage) {
@@ -665,8 +719,16 @@ __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, ui
     cgt = a1 + a2;
     __syncthreads();  // every wave has read sh before the slots overwrite it
   }
-  const uint32_t take = k - cgt;
-  unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
+  emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt, stage,
+                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT));
+}
+
+// Every survivor key above cs of the entries at e, in order, straight out
+// to the slots from `base` on: the one-workgroup tie pass's first part.
+template <int MODE>
+__device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t base,
+                            const Out& o) {
+  const int lane = __lane_id();
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
     uint32_t x = kDeadPair, id = 0;
@@ -675,52 +737,10 @@ __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, ui
       id = e[2 * i + 1];
     }
     const int32_t s0 = lo16s(x), s1 = hi16s(x);
-    const unsigned long long g0 = __ballot(s0 > Ts), g1 = __ballot(s1 > Ts);
-    const unsigned long long q0 = __ballot(s0 == Ts), q1 = __ballot(s1 == Ts);
-    const uint32_t ng = popc(g0) + popc(g1), nq = popc(q0) + popc(q1);
-    if (ng + nq == 0) continue;
-    unsigned long long base = 0;
-    if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
-    const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
-    int32_t v0 = (int32_t)id, v1 = (int32_t)id + 1;
-    if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
-    if (in_mask(g0)) stage[bg + mbcnt(g0)] = v0;
-    if (in_mask(g1)) stage[bg + popc(g0) + mbcnt(g1)] = v1;
-    if (nq) {
-      const uint32_t p0 = bq + mbcnt(q0);
-      if (in_mask(q0) && p0 < take) stage[cgt + p0] = v0;
-      const uint32_t p1 = bq + popc(q0) + mbcnt(q1);
-      if (in_mask(q1) && p1 < take) stage[cgt + p1] = v1;
-    }
-  }
-}
-
-// Every survivor key above cs of the entries at e, in order, into slots
-// from `base` on: the tie pass's first part.  Into the staging slots when
-// `stage` is given, else straight out.
-template <int MODE>
-__device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t ibase,
-                            uint32_t base, int32_t* stage, const Out& o) {
-  const int lane = __lane_id();
-  for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
-    const uint32_t i = b0 + lane;
-    uint32_t x = kDeadPair, id = 0;
-    if (i < cnt) {
-      x = e[2 * i];
-      id = e[2 * i + 1] + ibase;
-    }
-    const int32_t s0 = lo16s(x), s1 = hi16s(x);
     const unsigned long long g0 = __ballot(s0 > cs), g1 = __ballot(s1 > cs);
     const uint32_t p0 = mbcnt(g0, base), p1 = mbcnt(g1, base + popc(g0));
-    int32_t v0 = (int32_t)id;
-    if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
-    if (stage) {
-      if (in_mask(g0)) stage[p0] = v0;
-      if (in_mask(g1)) stage[p1] = (int32_t)id + 1;
-    } else {
-      if (in_mask(g0)) o.put(p0, id, (uint32_t)(s0 + 0x8000));
-      if (in_mask(g1)) o.put(p1, id + 1, (uint32_t)(s1 + 0x8000));
-    }
+    if (in_mask(g0)) o.put(p0, id, (uint32_t)(s0 + 0x8000));
+    if (in_mask(g1)) o.put(p1, id + 1, (uint32_t)(s1 + 0x8000));
     base += popc(g0) + popc(g1);
   }
 }
@@ -734,20 +754,33 @@ __device__ __forceinline__ void keep_equal_slot(bool eq, uint32_t idx, uint16_t*
   if (eq && slot < cap) list[slot] = (uint16_t)idx;
 }
 
-// Tie collection into this wave's own list at its running count (no atomic).
-__device__ __forceinline__ void keep_tie(bool eq, uint32_t idx, uint16_t* seg, uint32_t cap,
-                                         uint32_t& tcnt) {
-  const unsigned long long m = __ballot(eq);
-  const uint32_t pos = mbcnt(m, tcnt);
-  if (eq && pos < cap) seg[pos] = (uint16_t)idx;
-  tcnt += popc(m);
+// Entries whose key pair holds a key equal to cs go to this wave's tie
+// region the same way (compaction at tbase + tcnt), until tcnt passes
+// tcap.  tw counts the entries written, tkept the equal keys in them, neq
+// every equal key.
+__device__ __forceinline__ void keep_ties(uint32_t x, uint32_t eidx, int32_t cs, uint32_t* tl,
+                                          uint32_t tbase, uint32_t tcap, uint32_t& tcnt,
+                                          uint32_t& tw, uint32_t& tkept, uint32_t& neq) {
+  const unsigned long long elo = __ballot(lo16s(x) == cs), ehi = __ballot(hi16s(x) == cs);
+  const unsigned long long me = elo | ehi;
+  if (me) {
+    const uint32_t ne = popc(elo) + popc(ehi);
+    if (tcnt <= tcap) {
+      if (in_mask(me)) {
+        const uint32_t pos = mbcnt(me) + (tbase + tcnt);
+        *reinterpret_cast<uint2*>(tl + 2 * pos) = make_uint2(x, eidx);
+      }
+      tw += popc(me);
+      tkept += ne;
+    }
+    tcnt += popc(me);
+    neq += ne;
+  }
 }
 
-// Tie indices each wave of a team member keeps: enough for its share of k.
-__device__ __forceinline__ uint32_t tie_cap(int k) {
-  const uint32_t c = (uint32_t)k / 4u + 64u;
-  return c < (uint32_t)kTieCapWave ? c : (uint32_t)kTieCapWave;
-}
+// Tie entries each wave of a team member keeps before it stops: enough for
+// its share of k.
+__device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 64u; }
 
 // ============================================ one workgroup per row
 // Rows whose valid vectors fit NT * VPT: the whole row sits in VGPRs.
@@ -915,7 +948,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
           direct = true;
           code = TOPK_PATH_DIRECT_MISJUDGED;
         } else {
-          write_above<MODE>(seg, wcnt, cs, 0u, before, nullptr, o);
+          write_above<MODE>(seg, wcnt, cs, before, o);
           const uint32_t take = (uint32_t)k - gt_total;
           for (uint32_t i = tid; i < take; i += NT) o.put(gt_total + i, ties[i], c);
           code = TOPK_PATH_SAMPLED_TIES;
@@ -931,28 +964,114 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 }
 
 // ============================================ team of workgroups per row
-// Stage 1: every member of a row's team stages its chunk of the row (the
-// chunks split the valid length), derives the row's cutoff from samples
-// spread over the whole row (the same in every member), and writes its
-// survivor entries (chunk-local indices) and, if any, the indices of keys
-// equal to the cutoff to its scratch slice.
-template <int MODE, int VPT, int SV>
-__global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
+// A row wider than one workgroup is cut into work items of team_cv
+// vectors (the items split the valid length).  Three stream-ordered
+// kernels: the cutoff kernel (one workgroup a row) takes the row's cutoff
+// from samples spread over the row and lays out the work items; the filter
+// kernel (one workgroup an item) compacts the item's entries above and
+// equal to the cutoff into the item's scratch slice; the select kernel
+// (one workgroup a row) finishes the row.  Each kernel reads what the one
+// before it wrote, after the kernel boundary: no workgroup waits for
+// another and no atomic or fence crosses workgroups.
+
+enum { TI_CUT = 0, TI_FLAGS = 1, TI_FIRST = 2, TI_ITEMS = 3 };
+
+// Work items of a row: none when the row is short or goes straight to the
+// direct path.
+template <int MODE>
+__device__ __forceinline__ uint32_t items_of(const Params& p, int row) {
+  const int v = clamp_len(p.valid_len[row], p.width);
+  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
+  if (n <= p.k || p.force_direct) return 0u;
+  const int nvec = (v + 7) >> 3;
+  return (uint32_t)((nvec + p.team_cv - 1) / p.team_cv);
+}
+
+// Stage 1: short rows are written here; every other row gets its cutoff
+// (samples spread over the whole row, as in the one-workgroup kernel) and
+// its work items [first, first + items) of the launch.
+template <int MODE, int SV>
+__global__ __launch_bounds__(kTeamNT) void topk_team_cutoff(Params p) {
   constexpr int NT = kTeamNT;
   __shared__ uint32_t sh[512];
   __shared__ uint32_t bc[128];
-  const int G = p.G;
-  int lrow, member;
-  if (p.xcd_map) {
-    // members of a row share blockIdx % 8, i.e. the same XCD and L2
-    const int b = blockIdx.x, x = b & 7, y = b >> 3;
-    lrow = (y / G) * 8 + x;
-    member = y % G;
-  } else {
-    lrow = blockIdx.x / G;
-    member = blockIdx.x % G;
+  const int lrow = blockIdx.x;
+  const int row = p.row0 + lrow;
+  const int tid = threadIdx.x;
+  const int k = p.k;
+  const int v = clamp_len(p.valid_len[row], p.width);
+  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
+  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  // this row's first work item: the items of the launch's earlier rows
+  uint32_t before = 0;
+  for (int r = tid; r < lrow; r += NT) before += items_of<MODE>(p, p.row0 + r);
+  const uint32_t first = block_sum<NT>(before, bc + BC_TMP);
+  const uint32_t items = items_of<MODE>(p, row);
+  uint32_t* info = p.team_info + (size_t)lrow * 4;
+  for (uint32_t i = tid; i < items; i += NT) p.team_items[first + i] = (uint32_t)lrow;
+  if (lrow == p.rows - 1 && tid == 0) *p.team_total = first + items;
+  if (n <= k) {
+    const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
+    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
+    else write_short_token<NT>(o, n, k);
+    set_path(p, row, TOPK_PATH_SHORT);
+    return;
   }
-  if (lrow >= p.rows) return;
+  uint32_t c = 0u, flags = 0u;
+  if (!p.force_direct) {
+    for (int i = tid; i < 512; i += NT) sh[i] = 0;
+    const int nvec = (v + 7) >> 3;
+    // sample s of ns sits at vector floor((2 s + 1) nvec / (2 ns)), from a 32.32 step
+    const int ns = min(SV * NT, nvec);
+    const uint64_t step = ((uint64_t)nvec << 32) / (uint64_t)(2 * ns);
+    constexpr int NSK = (MODE == TOPK_MODE_BLOCK) ? SV : SV * 8;
+    uint32_t sk[NSK];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      const int s = j * NT + tid;
+      const int vid = s < ns ? (int)(((uint64_t)(2 * s + 1) * step) >> 32) : -1;
+      const uint4 raw = vid >= 0 ? src[vid] : make_uint4(~0u, ~0u, ~0u, ~0u);
+      if constexpr (MODE == TOPK_MODE_BLOCK) {
+        sk[j] = vid < 0 ? kNone : (vid == n - 1 ? kKeyPosInf : block_key4(raw));
+        mine += vid >= 0 ? 1u : 0u;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool ok = vid >= 0 && vid * 8 + e < v;
+          sk[j * 8 + e] = ok ? key1(half_of(word_of(raw, e >> 1), e & 1)) : kNone;
+          mine += ok ? 1u : 0u;
+        }
+      }
+    }
+    const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
+    c = sample_cutoff(sk, sample_rank((uint32_t)k, (uint32_t)n, S), sh);
+    // a zero cutoff would make the zero keys of slots past the length ties
+    if (MODE == TOPK_MODE_TOKEN && c == 0u) flags = kFlagDirect;
+  } else {
+    flags = kFlagDirect;
+  }
+  if (tid == 0) {
+    info[TI_CUT] = c;
+    info[TI_FLAGS] = flags;
+    info[TI_FIRST] = first;
+    info[TI_ITEMS] = items;
+  }
+}
+
+// Stage 2: one workgroup per work item (grid: an upper bound on the items;
+// the rest exit).  Loads the item's vectors, and writes to the item's
+// scratch slice the entries holding a key above the row's cutoff and, in
+// the same pass, those holding a key equal to it (item-local indices).
+// Waves work alone: no LDS, no barrier.
+template <int MODE, int VPT>
+__global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
+  constexpr int NT = kTeamNT;
+  const uint32_t item = blockIdx.x;
+  if (item >= *p.team_total) return;
+  const int lrow = (int)p.team_items[item];
+  const uint32_t* info = p.team_info + (size_t)lrow * 4;
+  if (info[TI_FLAGS] & kFlagDirect) return;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
@@ -961,175 +1080,105 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-
-  if (n <= k) {
-    if (member == 0) {
-      const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
-      if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
-      else write_short_token<NT>(o, n, k);
-      set_path(p, row, TOPK_PATH_SHORT);
-    }
-    return;
-  }
-  if (p.force_direct) return;  // the select stage takes the whole row
-  uint32_t* slice = p.team + ((size_t)lrow * G + member) * kMemberWords;
   const int nvec = (v + 7) >> 3;
-  const int per = (nvec + G - 1) / G;
-  const int vb = min(member * per, nvec);
-  const int ve = min(vb + per, nvec);
-  const int jt = ve > vb ? (ve - vb - 1) / NT : -1;  // last occupied slot
-  const int rem = (ve - vb) - jt * NT;               // vectors in it
-  for (int i = tid; i < 512; i += NT) sh[i] = 0;
-
-  // -- sample loads and chunk loads, all issued before any use
-  const int ns = min(SV * NT, nvec);  // sample vectors, spread over the row
-  uint4 sraw[SV];
-  int spos[SV];
-#pragma unroll
-  for (int j = 0; j < SV; ++j) {
-    const int s = j * NT + tid;
-    spos[j] = s < ns ? (int)(((int64_t)(2 * s + 1) * nvec) / (2 * (int64_t)ns)) : -1;
-    sraw[j] = spos[j] >= 0 ? src[spos[j]] : make_uint4(~0u, ~0u, ~0u, ~0u);
-  }
+  const int vb = (int)(item - info[TI_FIRST]) * p.team_cv;
+  const int ve = min(vb + p.team_cv, nvec);
+  const int jt = (ve - vb - 1) / NT;   // last occupied slot
+  const int rem = (ve - vb) - jt * NT; // vectors in it
   uint4 raw[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int lvid = slot_vid<NT>(j, jt, rem);
     raw[j] = lvid >= 0 ? src[vb + lvid] : make_uint4(~0u, ~0u, ~0u, ~0u);
   }
-
-  // -- sample keys and the cutoff (identical in every member)
-  constexpr int NSK = (MODE == TOPK_MODE_BLOCK) ? SV : SV * 8;
-  uint32_t sk[NSK];
-  uint32_t my_samples = 0;
-#pragma unroll
-  for (int j = 0; j < SV; ++j) {
-    const int vid = spos[j];
-    if constexpr (MODE == TOPK_MODE_BLOCK) {
-      sk[j] = vid < 0 ? kNone : (vid == n - 1 ? kKeyPosInf : block_key4(sraw[j]));
-      my_samples += vid >= 0 ? 1u : 0u;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const bool ok = vid >= 0 && vid * 8 + e < v;
-        sk[j * 8 + e] = ok ? key1(half_of(word_of(sraw[j], e >> 1), e & 1)) : kNone;
-        my_samples += ok ? 1u : 0u;
-      }
-    }
-  }
-  // block keys (and the tail's poison) before the barriers
-  uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
+  const uint32_t c = info[TI_CUT];
+  const int32_t cs = (int32_t)c - 0x8000;
+  uint32_t* slice = p.team_slices + (size_t)item * kMemberWords;
+  uint32_t* seg = slice + kMemberHdr;
+  uint32_t* tl = slice + kMemberHdr + 8 * kTeamLCW;
+  const uint32_t wv = readfirst((uint32_t)wave);
+  const uint32_t wbase = wv * kTeamLCW, tbase = wv * kTieLCW;
+  const uint32_t cap = kTeamLCW - kSpare, tcap = tie_cap(k);
+  uint32_t wcnt = 0, ecnt = 0, tcnt = 0, tw = 0, tkept = 0, neq = 0;
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int lvid = slot_vid<NT>(j, jt, rem);
-    if constexpr (MODE == TOPK_MODE_BLOCK) {
-      kb[j] = lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
-    } else {
-      if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
-    }
-  }
-  const uint32_t S = block_sum<NT>(my_samples, bc + BC_TMP);  // also publishes the zeroed hists
-  const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
-  const uint32_t c = sample_cutoff(sk, q, sh);
-  if (MODE == TOPK_MODE_TOKEN && c == 0u) {
-    // a zero cutoff would make the zero keys of slots past the length ties:
-    // every member sees the same cutoff and flags the row for the direct path
-    if (tid == 0) {
-      slice[12] = c;
-      slice[13] = kFlagDirect;
-    }
-    return;
-  }
-
-  // -- the entries above the cutoff go straight to this wave's scratch region
-  const int32_t cs = (int32_t)c - 0x8000;
-  uint32_t* seg = slice + kMemberHdr;
-  const uint32_t wbase = readfirst((uint32_t)wave) * kTeamLCW;
-  const uint32_t cap = kTeamLCW - kSpare;
-  uint32_t wcnt = 0, ecnt = 0, neq = 0;
-  if constexpr (MODE == TOPK_MODE_BLOCK) {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (j <= jt) {
-        keep_word(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, seg, wbase, cap,
-                  wcnt, ecnt);
-        neq += popc(__ballot(kb[j] == c));
-      }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (j <= jt) {
-        const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
+    if (j <= jt) {
+      const int lvid = slot_vid<NT>(j, jt, rem);
+      if constexpr (MODE == TOPK_MODE_BLOCK) {
+        const uint32_t key =
+            lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
+        const uint32_t x = block_entry(key);
+        keep_word(x, (uint32_t)lvid, cs, seg, wbase, cap, wcnt, ecnt);
+        keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
+      } else {
+        if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
+        const uint32_t e8 = (uint32_t)lvid * 8u;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           const uint32_t w = word_of(raw[j], q2);
           const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
           keep_word(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
-          neq += popc(__ballot(lo16s(x) == cs)) + popc(__ballot(hi16s(x) == cs));
+          keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
         }
       }
     }
   }
   if (lane == 0) {
-    slice[wave] = wcnt;
-    slice[4 + wave] = ecnt;
-    bc[BC_X + wave] = neq;
+    slice[H_WCNT + wave] = wcnt;
+    slice[H_ECNT + wave] = ecnt;
+    slice[H_TW + wave] = tw;
+    slice[H_TKEPT + wave] = tkept;
+    slice[H_NEQ + wave] = neq;
   }
-  __syncthreads();
-  const uint32_t eq_total = bc[BC_X] + bc[BC_X + 1] + bc[BC_X + 2] + bc[BC_X + 3];
-  uint32_t tcnt = 0;
-  if (eq_total) {
-    // second pass: chunk-local indices of keys equal to the cutoff
-    uint16_t* tseg =
-        reinterpret_cast<uint16_t*>(slice + kMemberHdr + 8 * kTeamLCW) + wave * kTieCapWave;
-    const uint32_t tcap = tie_cap(k);
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      if (j <= jt) {
-        const int lvid = slot_vid<NT>(j, jt, rem);
-        if constexpr (MODE == TOPK_MODE_BLOCK) {
-          keep_tie(kb[j] == c, (uint32_t)lvid, tseg, tcap, tcnt);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            keep_tie(key1(half_of(word_of(raw[j], e >> 1), e & 1)) == c,
-                     (uint32_t)(lvid * 8 + e), tseg, tcap, tcnt);
-        }
-      }
-    }
-  }
-  if (lane == 0) slice[8 + wave] = tcnt;
-  if (tid == 0) {
-    slice[12] = c;
-    slice[13] = 0u;
-  }
-}
-
-// Index of the segment holding flattened entry i: the last s with
-// start[s] <= i (start[0] = 0, nseg + 1 entries).
-__device__ __forceinline__ int find_segment(const uint32_t* start, int nseg, uint32_t i) {
-  int lo = 0, hi = nseg;  // start[lo] <= i < start[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (start[mid] <= i) lo = mid;
-    else hi = mid;
-  }
-  return lo;
 }
 
 // LDS of the select kernel past kLists (words)
-constexpr int kSelSegc = 0;          // entries per segment (4 G <= 256)
-constexpr int kSelStart = 256;       // 4 G + 1 entry starts
-constexpr int kSelEstart = 520;      // 4 G + 1 key starts
-constexpr int kSelTstart = 784;      // 4 G + 1 tie starts
-constexpr int kSelStage = 1048;      // staged entries, 2 words each
+constexpr int kSelStart = 0;         // survivor entry starts of the <= 4 kMaxItems segments
+constexpr int kSelTstart = 1024;     // tie entry starts
+constexpr int kSelSegc = 2048;       // survivor entries per segment
+constexpr int kSelTsegc = 3072;      // tie entries per segment
+constexpr int kSelStage = 4096;      // staged entries, 2 words each
 constexpr int kSelFixed = kLists + kSelStage;  // words before the staged entries
 
-// Stage 2: one 1024-thread workgroup per row reads the team's slices
-// (written by the previous kernel, so plain loads see them), checks that
-// the cutoff held, and writes the row: exact select over the survivors,
-// the tie pass, or the direct path.
+// Copies the entries of segments wave, wave + NW, ... (segment s: n_s
+// entries at src_s, chunk-local indices) into LDS at dst[s] with row-level
+// indices.  The first 64 entries of four segments are in flight together.
+template <int NW, class SrcOf, class CntOf>
+__device__ void stage_segments(int nseg, SrcOf src_of, CntOf cnt_of, const uint32_t* dst,
+                               uint32_t chunk, uint32_t* ent) {
+  constexpr int U = 4;
+  const int lane = __lane_id();
+  const int wave = threadIdx.x >> 6;
+  for (int s0 = wave; s0 < nseg; s0 += NW * U) {
+    uint2 en[U];
+    uint32_t cnt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NW;
+      cnt[u] = s < nseg ? cnt_of(s) : 0u;
+      en[u] = (uint32_t)lane < cnt[u] ? *reinterpret_cast<const uint2*>(src_of(s) + 2 * lane)
+                                      : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NW;
+      if ((uint32_t)lane < cnt[u]) {
+        const uint32_t d = dst[s] + lane, g = (uint32_t)(s >> 2) * chunk;
+        *reinterpret_cast<uint2*>(ent + 2 * d) = make_uint2(en[u].x, en[u].y + g);
+      }
+      for (uint32_t i = 64 + lane; i < cnt[u]; i += 64) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src_of(s) + 2 * i);
+        const uint32_t d = dst[s] + i, g = (uint32_t)(s >> 2) * chunk;
+        *reinterpret_cast<uint2*>(ent + 2 * d) = make_uint2(x.x, x.y + g);
+      }
+    }
+  }
+}
+
+// Stage 3: one 1024-thread workgroup per row reads the slices of its work
+// items (written by the previous kernel, so plain loads see them), checks
+// that the cutoff held, and writes the row: exact select over the
+// survivors, the tie pass, or the direct path.
 template <int MODE>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
@@ -1140,147 +1189,129 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   const int lane = __lane_id();
   const int wave = tid >> 6;
   const int k = p.k;
-  const int G = p.G;
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  if (n <= k) return;  // written by the filter stage
+  if (n <= k) return;  // written by the cutoff stage
   const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
   int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
-  uint32_t* segc = smem + kLists + kSelSegc;
   uint32_t* start = smem + kLists + kSelStart;
-  uint32_t* estart = smem + kLists + kSelEstart;
   uint32_t* tstart = smem + kLists + kSelTstart;
+  uint32_t* segc = smem + kLists + kSelSegc;
+  uint32_t* tsegc = smem + kLists + kSelTsegc;
   uint32_t* ent = smem + kLists + kSelStage;
-  bool direct = p.force_direct != 0;
-  int code = TOPK_PATH_DIRECT_FORCED;
+  const uint32_t* info = p.team_info + (size_t)lrow * 4;
+  const uint32_t rflags = info[TI_FLAGS];
+  bool direct = (rflags & kFlagDirect) != 0;
+  int code = p.force_direct ? TOPK_PATH_DIRECT_FORCED : TOPK_PATH_DIRECT_MISJUDGED;
   if (!direct) {
-    const uint32_t* slices = p.team + (size_t)lrow * G * kMemberWords;
-    const int nvec = (v + 7) >> 3;
-    const uint32_t per = (uint32_t)((nvec + G - 1) / G);
-    // chunk starts in element units: 8 logits per vector, one block per vector
-    const uint32_t chunk = per * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
-    const int nseg = 4 * G;  // <= 256: waves 0..3 hold one segment per lane
+    const uint32_t* slices = p.team_slices + (size_t)info[TI_FIRST] * kMemberWords;
+    // item starts in element units: 8 logits per vector, one block per vector
+    const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
+    const int nseg = 4 * (int)info[TI_ITEMS];  // <= 4 kMaxItems = NT: one segment per thread
     for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-    uint32_t wc = 0, ec = 0, tc = 0, tcp = 0, bad = 0;
+    // per segment (item, wave): entry counts, key counts, overflow
+    uint32_t wc = 0, ec = 0, tw = 0, tk = 0, nq = 0, bad = 0;
     if (tid < nseg) {
       const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
       const int w = tid & 3;
-      if (hdr[13] & kFlagDirect) {
-        bad = 2u;
-      } else {
-        wc = hdr[w];
-        ec = hdr[4 + w];
-        tc = hdr[8 + w];
-        tcp = min(tc, tie_cap(k));
-        bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
-      }
-      segc[tid] = wc;
+      wc = hdr[H_WCNT + w];
+      ec = hdr[H_ECNT + w];
+      tw = hdr[H_TW + w];
+      tk = hdr[H_TKEPT + w];
+      nq = hdr[H_NEQ + w];
+      bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
     }
-    const uint32_t iw = wave_incl_scan(wc), ie = wave_incl_scan(ec);
-    const uint32_t it = wave_incl_scan(tcp), itc = wave_incl_scan(tc);
-    const unsigned long long mb = __ballot((bad & 1u) != 0), mf = __ballot((bad & 2u) != 0);
+  const uint32_t iw = wave_incl_scan(wc), it = wave_incl_scan(tw);
+    const uint32_t ie = wave_incl_scan(ec), ik = wave_incl_scan(tk), iq = wave_incl_scan(nq);
+    const unsigned long long mb = __ballot(bad != 0);
     if (lane == 63) {
       bc[BC_TMP + wave] = iw;
+      bc[BC_TMP + 16 + wave] = it;
       bc[BC_X + wave] = ie;
-      bc[BC_CGT + wave] = it;
-      bc[BC_CEQ + wave] = itc;
+      bc[BC_CGT + wave] = ik;
+      bc[BC_CEQ + wave] = iq;
     }
-    if (lane == 0) bc[BC_CNT + wave] = (mb ? 1u : 0u) | (mf ? 2u : 0u);
+    if (lane == 0) bc[BC_CNT + wave] = mb ? 1u : 0u;
     __syncthreads();
-    uint32_t ow = 0, oe = 0, ot = 0, E = 0, gt_total = 0, avail = 0, eq_total = 0, flags = 0;
+    uint32_t ow = 0, ot = 0, E = 0, Et = 0, gt_total = 0, avail = 0, eq_total = 0, flags = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const bool lower = w < wave;
       ow += lower ? bc[BC_TMP + w] : 0u;
-      oe += lower ? bc[BC_X + w] : 0u;
-      ot += lower ? bc[BC_CGT + w] : 0u;
+      ot += lower ? bc[BC_TMP + 16 + w] : 0u;
       E += bc[BC_TMP + w];
+      Et += bc[BC_TMP + 16 + w];
       gt_total += bc[BC_X + w];
       avail += bc[BC_CGT + w];
       eq_total += bc[BC_CEQ + w];
       flags |= bc[BC_CNT + w];
     }
     if (tid < nseg) {
-      start[tid + 1] = ow + iw;
-      estart[tid + 1] = oe + ie;
-      tstart[tid + 1] = ot + it;
+      start[tid] = ow + iw - wc;
+      tstart[tid] = ot + it - tw;
+      segc[tid] = wc;
+      tsegc[tid] = tw;
     }
-    if (tid == 0) {
-      start[0] = 0;
-      estart[0] = 0;
-      tstart[0] = 0;
-    }
-    const uint32_t c = slices[12];
+    const uint32_t c = info[TI_CUT];
     const int32_t cs = (int32_t)c - 0x8000;
     __syncthreads();
-    if (flags & 2u) {
-      direct = true;
-      code = TOPK_PATH_DIRECT_MISJUDGED;
-    } else if (flags & 1u) {
+    const uint32_t cap = (uint32_t)p.sel_cap;
+    const bool sampled = gt_total >= (uint32_t)k;
+    if (flags & 1u) {
       direct = true;
       code = TOPK_PATH_DIRECT_OVERFLOW;
     } else if (gt_total + eq_total < (uint32_t)k) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
-    } else if (gt_total >= (uint32_t)k) {
-      if (E > (uint32_t)p.sel_cap) {
-        direct = true;
-        code = TOPK_PATH_DIRECT_OVERFLOW;
-      } else {
-        // stage every survivor entry in LDS with its row-level index
-        for (int s = wave; s < nseg; s += NW) {
-          const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
-                               (s & 3) * 2 * kTeamLCW;
-          const uint32_t gbase = (uint32_t)(s >> 2) * chunk;
-          const uint32_t cs_ = segc[s], d0 = start[s];
-          for (uint32_t i = lane; i < cs_; i += 64) {
-            const uint2 en = *reinterpret_cast<const uint2*>(es + 2 * i);
-            ent[2 * (d0 + i)] = en.x;
-            ent[2 * (d0 + i) + 1] = en.y + gbase;
-          }
-        }
-        __syncthreads();
-        const uint32_t share = (E + NW - 1) / NW;
-        const uint32_t lo = min((uint32_t)wave * share, E);
-        const uint32_t hi = min(lo + share, E);
-        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage);
-        __syncthreads();
-        flush_out<NT>(stage, o);
-        code = TOPK_PATH_SAMPLED;
-      }
+    } else if (E + (sampled ? 0u : Et) > cap ||
+               (!sampled && avail < (uint32_t)k - gt_total)) {
+      direct = true;
+      code = TOPK_PATH_DIRECT_OVERFLOW;
     } else {
-      // the k-th key is the cutoff: every key above it, then ties
-      const uint32_t take = (uint32_t)k - gt_total;
-      if (avail < take) {
-        direct = true;
-        code = TOPK_PATH_DIRECT_OVERFLOW;
+      // stage the survivor entries (and, for the tie pass, the tie entries
+      // after them) in LDS with row-level indices
+      auto seg_src = [&](int s) {
+        return slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr + (s & 3) * 2 * kTeamLCW;
+      };
+      auto seg_cnt = [&](int s) { return segc[s]; };
+      stage_segments<NW>(nseg, seg_src, seg_cnt, start, chunk, ent);
+      if (!sampled) {
+        auto tie_src = [&](int s) {
+          return slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
+                 (s & 3) * 2 * kTieLCW;
+        };
+        auto tie_cnt = [&](int s) { return tsegc[s]; };
+        stage_segments<NW>(nseg, tie_src, tie_cnt, tstart, chunk, ent + 2 * E);
+      }
+      __syncthreads();
+      const uint32_t share = (E + NW - 1) / NW;
+      const uint32_t lo = min((uint32_t)wave * share, E);
+      const uint32_t hi = min(lo + share, E);
+      unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
+      if (sampled) {
+        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage);
+        code = TOPK_PATH_SAMPLED;
       } else {
-        for (int s = wave; s < nseg; s += NW) {
-          const uint32_t* es = slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
-                               (s & 3) * 2 * kTeamLCW;
-          write_above<MODE>(es, segc[s], cs, (uint32_t)(s >> 2) * chunk, estart[s], stage, o);
-        }
-        const int32_t tv = (MODE == TOPK_MODE_BLOCK && c == kKeyNegInf) ? -1 : 0;
-        for (uint32_t j = tid; j < take; j += NT) {
-          const int s = find_segment(tstart, nseg, j);
-          const uint16_t* tl = reinterpret_cast<const uint16_t*>(
-                                   slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr +
-                                   8 * kTeamLCW) + (s & 3) * kTieCapWave;
-          const int32_t idx = (int32_t)((uint32_t)(s >> 2) * chunk + tl[j - tstart[s]]);
-          stage[gt_total + j] = tv < 0 ? -1 : idx;
-        }
-        __syncthreads();
-        flush_out<NT>(stage, o);
+        // the k-th key is the cutoff: every key above it, then the first ties
+        const uint32_t take = (uint32_t)k - gt_total;
+        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take, stage, slot);
+        const uint32_t tshare = (Et + NW - 1) / NW;
+        const uint32_t tlo = min((uint32_t)wave * tshare, Et);
+        const uint32_t thi = min(tlo + tshare, Et);
+        emit_entries<MODE, false, true>(ent + 2 * (E + tlo), thi - tlo, cs, gt_total, take,
+                                        stage, slot);
         code = TOPK_PATH_SAMPLED_TIES;
       }
+      __syncthreads();
+      flush_out<NT>(stage, o);
     }
   }
   if (direct) {
@@ -1309,9 +1340,9 @@ struct Scratch {
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
-// Team scratch: one slice of kMemberWords words per (row, member) of a
-// launch.  Every word the select kernel reads is written by the filter
-// kernel of the same call, so nothing needs zeroing between calls.
+// Team scratch, one buffer per (device, stream).  Every word a team kernel
+// reads was written by an earlier kernel of the same call, so nothing needs
+// zeroing between calls.
 int get_scratch(hipStream_t stream, size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -1420,29 +1451,41 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
   const int nvec_max = (width + 7) / 8;
-  const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kBlockVPT / 2 : kTokenVPT / 2);
+  const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kRowBlockVPT : kRowTokenVPT);
   if (nvec_max <= cap_wg) {
     p.rows = rows;
     p.row0 = 0;
     p.lcw = row_lcw(k, kRowNT / 64);
     const size_t lds = row_lds_bytes(p.lcw, kRowNT / 64);
     if (mode == TOPK_MODE_BLOCK)
-      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kBlockVPT / 2>, rows, kRowNT, lds, stream, p);
-    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kTokenVPT / 2>, rows, kRowNT, lds, stream, p);
+      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT>, rows, kRowNT, lds,
+                    stream, p);
+    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT>, rows, kRowNT, lds,
+                  stream, p);
   }
 
-  // team path: a filter kernel (G members a row), then a select kernel
-  const int cap_team = kTeamNT * (mode == TOPK_MODE_BLOCK ? kBlockVPT : kTokenVPT);
-  const int G = (nvec_max + cap_team - 1) / cap_team;  // <= 64, so 4 G <= 256
-  const size_t row_bytes = (size_t)G * kMemberWords * 4;
+  // team path: cutoff kernel, filter kernel (one workgroup per work item),
+  // select kernel.  Scratch per launch: row info, the row of every work
+  // item, the item count, then one slice per work item.
+  const int cv = kTeamNT * (mode == TOPK_MODE_BLOCK ? kTeamBlockVPT : kTeamTokenVPT);
+  const int max_items_row = (nvec_max + cv - 1) / cv;  // <= kMaxItems
+  const size_t row_bytes = (size_t)max_items_row * ((size_t)kMemberWords + 1) * 4 + 16;
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
   if ((size_t)batch * row_bytes > kTeamScratchMax) batch = (int)(kTeamScratchMax / row_bytes);
   if (batch < 1) batch = 1;
+  const size_t max_items = (size_t)batch * max_items_row;
+  const size_t off_items = (size_t)batch * 4;
+  const size_t off_total = (off_items + max_items + 63) / 64 * 64;
+  const size_t off_slices = off_total + 64;
   void* scratch = nullptr;
-  int rc = get_scratch(stream, (size_t)batch * row_bytes, &scratch);
+  int rc = get_scratch(stream, (off_slices + max_items * kMemberWords) * 4, &scratch);
   if (rc != TOPK_OK) return rc;
-  p.G = G;
-  p.team = static_cast<uint32_t*>(scratch);
+  uint32_t* sw = static_cast<uint32_t*>(scratch);
+  p.team_info = sw;
+  p.team_items = sw + off_items;
+  p.team_total = sw + off_total;
+  p.team_slices = sw + off_slices;
+  p.team_cv = cv;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   // stage as many survivor entries as the LDS of one workgroup holds
@@ -1454,14 +1497,17 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     const int nr = (rows - r0) < batch ? (rows - r0) : batch;
     p.row0 = r0;
     p.rows = nr;
-    p.xcd_map = nr >= 8 ? 1 : 0;
-    const int grid = p.xcd_map ? ((nr + 7) / 8) * 8 * G : nr * G;
+    const int grid = nr * max_items_row;
     if (mode == TOPK_MODE_BLOCK) {
-      rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kBlockVPT, kBlockSV>, grid, kTeamNT, 0, stream, p);
+      rc = launch(topk_team_cutoff<TOPK_MODE_BLOCK, kBlockSV>, nr, kTeamNT, 0, stream, p);
+      if (rc == TOPK_OK)
+        rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kTeamBlockVPT>, grid, kTeamNT, 0, stream, p);
       if (rc == TOPK_OK)
         rc = launch(topk_team_select<TOPK_MODE_BLOCK>, nr, kSelNT, sel_lds, stream, p);
     } else {
-      rc = launch(topk_team_filter<TOPK_MODE_TOKEN, kTokenVPT, kTokenSV>, grid, kTeamNT, 0, stream, p);
+      rc = launch(topk_team_cutoff<TOPK_MODE_TOKEN, kTokenSV>, nr, kTeamNT, 0, stream, p);
+      if (rc == TOPK_OK)
+        rc = launch(topk_team_filter<TOPK_MODE_TOKEN, kTeamTokenVPT>, grid, kTeamNT, 0, stream, p);
       if (rc == TOPK_OK)
         rc = launch(topk_team_select<TOPK_MODE_TOKEN>, nr, kSelNT, sel_lds, stream, p);
     }
