@@ -73,9 +73,10 @@ constexpr int kSpare = 64;               // region entries past the cap (one bal
 constexpr int kTieLCW = TOPK_MAX_K / 4 + 128;     // tie entries per wave region of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
 constexpr size_t kTeamScratchMax = size_t(256) << 20;
-constexpr int kRelBins = 1024;           // histogram bins of (key - cutoff)
+constexpr int kRelBins = 1024;           // histogram bins of (key - cutoff): 16 per lane
 constexpr int kSelectMin = 6144;         // staged survivor entries with 64 KB of LDS
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
+constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
 
 constexpr uint32_t kKeyNegInf = 0x007Fu; // key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF80u; // key(+inf): the pinned newest block
@@ -87,7 +88,7 @@ constexpr uint32_t kDeadPair = 0x80008000u;  // two signed keys at the very bott
 // LDS (32-bit words), shared by the one-workgroup and the select kernels
 constexpr int kBc = 0;                          // 128 words of counters and per-wave fields
 constexpr int kStage = 128;                     // k output slots, overlapping:
-constexpr int kSampHist = kStage;               //   2 x 256 sample bins, descending keys
+constexpr int kSampHist = kStage;               //   256 low-byte sample bins / 2 x 256 bins
 constexpr int kRelHist = kStage + 512;          //   kRelBins bins / u16 tie list
 constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
 static_assert(kRelHist + kRelBins <= kLists, "histograms overlap the lists");
@@ -135,6 +136,7 @@ struct Params {
   int32_t force_direct;
   int32_t out_vec;     // rows of out may be written as 16-byte vectors
   int32_t lcw;         // survivor entries per wave before the cap (one-workgroup kernel)
+  int32_t page_lds;    // LDS word offset of a row's block-table copy (one-workgroup kernel), or 0
   // team path (rows wider than one workgroup), all in one scratch buffer:
   uint32_t* team_info;   // [rows][4]: cutoff, flags, first work item, work items
   uint32_t* team_items;  // [max items]: the row of each work item
@@ -275,74 +277,83 @@ __device__ __forceinline__ uint32_t readfirst(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
 }
 
-// One wave over a histogram of 64*B bins whose index 0 holds the largest
-// keys: the first bin where the running count reaches `need`, and the count
-// before it (decode_topk_cute, select_bin).  Every lane gets the answer.
-template <int B>
+// One wave over a 256-bin histogram (16-byte aligned) whose index 0 holds
+// the largest keys: the first bin where the running count reaches `need`,
+// and the count before it (decode_topk_cute, select_bin).  A lane holds 4
+// bins; the lane that crosses `need` is found with one ballot, and the bin
+// inside it with scalar code.  Every lane gets the answer.
 __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, uint32_t& bin,
                                           uint32_t& above) {
   const int lane = __lane_id();
-  uint32_t h[B];
-  uint32_t s = 0;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    h[b] = hist[lane * B + b];
-    s += h[b];
-  }
+  const uint4 h = *reinterpret_cast<const uint4*>(hist + lane * 4);
+  const uint32_t s = h.x + h.y + h.z + h.w;
   const uint32_t incl = wave_incl_scan(s);
   const unsigned long long m = __ballot(incl >= need);
   const int L = m ? (__ffsll(m) - 1) : 63;
-  uint32_t acc = incl - s, pos = B - 1;
-  bool found = false;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const bool hit = !found && acc + h[b] >= need;
-    pos = hit ? (uint32_t)b : pos;
-    found = found || hit;
-    acc += found ? 0u : h[b];
+  uint32_t acc = readlane(incl - s, L);
+  const uint32_t h0 = readlane(h.x, L), h1 = readlane(h.y, L), h2 = readlane(h.z, L);
+  uint32_t pos = 3;
+  if (acc + h0 >= need) {
+    pos = 0;
+  } else if (acc + h0 + h1 >= need) {
+    pos = 1;
+    acc += h0;
+  } else if (acc + h0 + h1 + h2 >= need) {
+    pos = 2;
+    acc += h0 + h1;
+  } else {
+    acc += h0 + h1 + h2;
   }
-  bin = readlane((uint32_t)lane * B + pos, L);
-  above = readlane(acc, L);
+  bin = (uint32_t)L * 4u + pos;
+  above = acc;
 }
 
-// Workgroup-wide version for a histogram of BPT*NT bins, index 0 holding
-// the largest keys: each thread scans BPT consecutive bins, one barrier
-// joins the waves, and the thread holding the answer broadcasts it through
-// tmp (NT/64 + 2 words, free until the caller's next barrier).
-template <int NT, int BPT>
-__device__ __forceinline__ void find_block(const uint32_t* hist, uint32_t need, uint32_t* tmp,
-                                           uint32_t& bin, uint32_t& above) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t h[BPT];
-  uint32_t s = 0;
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) {
-    h[b] = hist[tid * BPT + b];
-    s += h[b];
-  }
+// One wave over a 1024-bin histogram (16-byte aligned), index 0 holding
+// the largest keys: as find_desc with 16 bins a lane; the lane's group of
+// 4 bins, then the bin, are found with scalar code.  `total` is the
+// histogram's sum; bin and above are meaningful when need <= total.
+__device__ __forceinline__ void find_desc16(const uint32_t* hist, uint32_t need, uint32_t& bin,
+                                            uint32_t& above, uint32_t& total) {
+  const int lane = __lane_id();
+  const uint4* h = reinterpret_cast<const uint4*>(hist + lane * 16);
+  const uint4 a = h[0], b = h[1], c = h[2], d = h[3];
+  const uint32_t g0 = a.x + a.y + a.z + a.w, g1 = b.x + b.y + b.z + b.w;
+  const uint32_t g2 = c.x + c.y + c.z + c.w, g3 = d.x + d.y + d.z + d.w;
+  const uint32_t s = g0 + g1 + g2 + g3;
   const uint32_t incl = wave_incl_scan(s);
-  if (lane == 63) tmp[wave] = incl;
-  __syncthreads();
-  uint32_t acc = incl - s;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) acc += w < wave ? tmp[w] : 0u;
-  if (acc < need && need <= acc + s) {
-    uint32_t pos = BPT - 1;
-    bool found = false;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const bool hit = !found && acc + h[b] >= need;
-      pos = hit ? (uint32_t)b : pos;
-      found = found || hit;
-      acc += found ? 0u : h[b];
-    }
-    tmp[NW] = (uint32_t)tid * BPT + pos;
-    tmp[NW + 1] = acc;
+  total = readlane(incl, 63);
+  const unsigned long long m = __ballot(incl >= need);
+  const int L = m ? (__ffsll(m) - 1) : 63;
+  uint32_t acc = readlane(incl - s, L);
+  const uint32_t s0 = readlane(g0, L), s1 = readlane(g1, L), s2 = readlane(g2, L);
+  uint32_t grp = 3;
+  if (acc + s0 >= need) {
+    grp = 0;
+  } else if (acc + s0 + s1 >= need) {
+    grp = 1;
+    acc += s0;
+  } else if (acc + s0 + s1 + s2 >= need) {
+    grp = 2;
+    acc += s0 + s1;
+  } else {
+    acc += s0 + s1 + s2;
   }
-  __syncthreads();
-  bin = tmp[NW];
-  above = tmp[NW + 1];
+  const uint4 e = *reinterpret_cast<const uint4*>(hist + L * 16 + grp * 4);
+  const uint32_t e0 = readfirst(e.x), e1 = readfirst(e.y), e2 = readfirst(e.z);
+  uint32_t pos = 3;
+  if (acc + e0 >= need) {
+    pos = 0;
+  } else if (acc + e0 + e1 >= need) {
+    pos = 1;
+    acc += e0;
+  } else if (acc + e0 + e1 + e2 >= need) {
+    pos = 2;
+    acc += e0 + e1;
+  } else {
+    acc += e0 + e1 + e2;
+  }
+  bin = (uint32_t)L * 16u + grp * 4u + pos;
+  above = acc;
 }
 
 // Sum over the workgroup (every thread gets the total).
@@ -408,20 +419,27 @@ __device__ __forceinline__ Out row_out(const Params& p, int row, bool block) {
 }
 
 // The k staged slots of a row to HBM in one coalesced pass (16-byte stores
-// where the row allows), through the block table.  Follows a barrier.
+// where the row allows), through the block table: the row's copy in LDS
+// when `lpages` is given, else the table in global memory.  Follows a
+// barrier.
 template <int NT>
-__device__ void flush_out(const int32_t* stage, const Out& o) {
+__device__ void flush_out(const int32_t* stage, const Out& o, const int32_t* lpages = nullptr) {
+  auto map = [&](int32_t x) -> int32_t {
+    if (!lpages) return o.map(x);
+    const int32_t i = x < 0 ? 0 : x;
+    return x < 0 ? -1 : (lpages[i >> o.shift] << o.shift) | (i & ((1 << o.shift) - 1));
+  };
   if (o.vec) {
     for (uint32_t e = threadIdx.x * 4u; e < o.k; e += NT * 4u) {
       int4 v = *reinterpret_cast<const int4*>(stage + e);
-      v.x = o.map(v.x);
-      v.y = o.map(v.y);
-      v.z = o.map(v.z);
-      v.w = o.map(v.w);
+      v.x = map(v.x);
+      v.y = map(v.y);
+      v.z = map(v.z);
+      v.w = map(v.w);
       *reinterpret_cast<int4*>(o.out + e) = v;
     }
   } else {
-    for (uint32_t e = threadIdx.x; e < o.k; e += NT) o.out[e] = o.map(stage[e]);
+    for (uint32_t e = threadIdx.x; e < o.k; e += NT) o.out[e] = map(stage[e]);
   }
 }
 
@@ -506,7 +524,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& 
     }
     __syncthreads();
     uint32_t bin, above;
-    find_desc<4>(sums, pass == 0 ? (uint32_t)k : (uint32_t)k - a1, bin, above);
+    find_desc(sums, pass == 0 ? (uint32_t)k : (uint32_t)k - a1, bin, above);
     if (pass == 0) {
       b1 = 255u - bin;
       a1 = above;
@@ -550,40 +568,46 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out& 
 // sample plus a margin of ~4.5 standard deviations and a constant, so that
 // fewer than k keys at or above the cutoff is a rare event (the row then
 // falls back to the direct path; exactness never depends on this choice).
-__device__ __forceinline__ uint32_t isqrt32(uint32_t x) {
-  uint32_t r = 0;
-  for (uint32_t b = 1u << 15; b; b >>= 1) {
-    const uint32_t t = r | b;
-    if (t * t <= x) r = t;
-  }
-  return r;
-}
-
 __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t S) {
   if (S >= n) return k;  // every element sampled: the cutoff is the k-th key
-  const uint32_t q0 = (uint32_t)(((uint64_t)k * S) / n);
-  const uint32_t q = q0 + (9u * isqrt32(q0) + 1u) / 2u + 8u;
+  const uint32_t q0 = (k * S) / n;  // k <= 2048 and S <= 4096: no overflow
+  // the margin's square root in single precision: it sizes the work only
+  const uint32_t q = q0 + (uint32_t)(4.5f * __builtin_sqrtf((float)q0)) + 9u;
   return q < S ? q : S;
 }
 
 // The q-th largest of the samples (kNone marks an empty slot): two 8-bit
-// radix passes over one zeroed 2 x 256-bin histogram, each wave finding
-// the bins itself (decode_topk_cute, radix_select over the samples).
-template <int NSK>
-__device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_t* sh) {
+// radix passes (decode_topk_cute, radix_select over the samples).  The
+// high-byte pass counts into kCopies replicated bins (lane mod 8) at h8
+// (256 kCopies words, zeroed), since sampled keys of smooth data crowd a
+// few high bytes and same-word LDS atomics serialize; 256 threads then sum
+// the copies into h8 + 256 kCopies (256 words).  The low-byte pass counts
+// into sh (256 words, zeroed).  Every wave finds the bins itself.
+template <int NSK, int NT>
+__device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_t* h8,
+                                  uint32_t* sh) {
+  static_assert(NT >= 256, "one thread per high-byte bin");
+  const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
   for (int i = 0; i < NSK; ++i)
-    if (sk[i] != kNone) atomicAdd(&sh[255u - (sk[i] >> 8)], 1u);
+    if (sk[i] != kNone) atomicAdd(&h8[(255u - (sk[i] >> 8)) * kCopies + copy], 1u);
+  __syncthreads();
+  uint32_t* sums = h8 + 256 * kCopies;
+  if (threadIdx.x < 256) {
+    const uint4 a = *reinterpret_cast<const uint4*>(h8 + threadIdx.x * kCopies);
+    const uint4 b = *reinterpret_cast<const uint4*>(h8 + threadIdx.x * kCopies + 4);
+    sums[threadIdx.x] = a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w;
+  }
   __syncthreads();
   uint32_t i1, a1;
-  find_desc<4>(sh, q, i1, a1);
+  find_desc(sums, q, i1, a1);
   const uint32_t b1 = 255u - i1;
 #pragma unroll
   for (int i = 0; i < NSK; ++i)
-    if (sk[i] != kNone && (sk[i] >> 8) == b1) atomicAdd(&sh[256 + 255u - (sk[i] & 255u)], 1u);
+    if (sk[i] != kNone && (sk[i] >> 8) == b1) atomicAdd(&sh[255u - (sk[i] & 255u)], 1u);
   __syncthreads();
   uint32_t i2, a2;
-  find_desc<4>(sh + 256, q - a1, i2, a2);
+  find_desc(sh, q - a1, i2, a2);
   return (b1 << 8) | (255u - i2);
 }
 
@@ -595,10 +619,12 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_
 // Compaction of one entry: if either half of x is above the signed cutoff
 // cs, (x, eidx) goes to this wave's region at the wave's running count
 // plus the lane's rank among the kept lanes (ballot + lane-mask count, no
-// atomic).  wcnt (entries) and ecnt (keys above cs) are wave-uniform; once
-// wcnt passes cap the wave stops writing, so a region needs cap + 64
-// entries, and a final wcnt above cap means the row overflowed.
+// atomic).  wcnt (entries) and ecnt (keys above cs, when counted) are
+// wave-uniform; once wcnt passes cap the wave stops writing, so a region
+// needs cap + 64 entries, and a final wcnt above cap means the row
+// overflowed.
 // The region starts at entry wbase (wave-uniform) of `lists`.
+template <bool COUNT_KEYS>
 __device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs, uint32_t* lists,
                                           uint32_t wbase, uint32_t cap, uint32_t& wcnt,
                                           uint32_t& ecnt) {
@@ -609,7 +635,7 @@ __device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs,
     *reinterpret_cast<uint2*>(lists + 2 * pos) = make_uint2(x, eidx);
   }
   wcnt += popc(m);
-  ecnt += popc(mlo) + popc(mhi);
+  if (COUNT_KEYS) ecnt += popc(mlo) + popc(mhi);
 }
 
 // Block entries: signed key in the low half, the bottom key above it.
@@ -657,17 +683,22 @@ __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32
   }
 }
 
-// Exact k-th key T over the survivor entries spread over the waves (every
-// key above the signed cutoff cs counts; at least k of them), then the
-// write into the k staged slots.  Wave w sees `cnt` entries at e; `rel` is
-// a zeroed kRelBins histogram, `sh` 512 free words, bc[BC_SLOT..+1] zero.
-// The bins of (key - cs - 1), largest first, give T exactly unless
+enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
+
+// Exact k-th key T over the survivor entries spread over the waves, then
+// the write into the k staged slots.  Wave w sees `cnt` entries at e; `rel`
+// is a zeroed kRelBins histogram, `sh` 512 free words, bc[BC_SLOT..+1]
+// zero.  The bins of (key - cs - 1), largest first, give T exactly unless
 // T > cs + kRelBins (then two 8-bit passes over the keys above that).  The
 // keys above T take the slots [0, cgt) and the first keys equal to T the
 // slots [cgt, k).  rel and sh overlap the staging slots.
+// Returns SEL_OVERFLOW when a wave's published entry count bc[BC_CNT + w]
+// passed `cap` (checked after the histogram barrier), SEL_TIES when fewer
+// than k keys lie above cs (nothing written then), else SEL_DONE.
 template <int MODE, int NW>
-__device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t k,
-                                 uint32_t* rel, uint32_t* sh, uint32_t* bc, int32_t* stage) {
+__device__ int select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t k,
+                                uint32_t* rel, uint32_t* sh, uint32_t* bc, int32_t* stage,
+                                uint32_t cap) {
   const int lane = __lane_id();
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
@@ -680,13 +711,19 @@ __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, ui
     }
   }
   __syncthreads();
-  uint32_t ri, above;
-  find_block<64 * NW, kRelBins / (64 * NW)>(rel, k, bc + BC_TMP, ri, above);
+  bool ovf = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) ovf |= bc[BC_CNT + w] > cap;
+  if (ovf) return SEL_OVERFLOW;
+  uint32_t ri, above, total;
+  find_desc16(rel, k, ri, above, total);
+  if (total < k) return SEL_TIES;
   int32_t Ts;
   uint32_t cgt;
   if (ri != 0) {
     Ts = top - (int32_t)ri;
     cgt = above;
+    __syncthreads();  // every wave has read rel before the slots overwrite it
   } else {
     // the k-th key lies at or above top: 8-bit passes over those keys
     for (int i = threadIdx.x; i < 512; i += 64 * NW) sh[i] = 0;
@@ -702,7 +739,7 @@ __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, ui
     }
     __syncthreads();
     uint32_t i1, a1, i2, a2;
-    find_desc<4>(sh, k, i1, a1);
+    find_desc(sh, k, i1, a1);
     const int32_t b1 = 255 - (int32_t)i1;
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
@@ -714,13 +751,25 @@ __device__ void select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, ui
       }
     }
     __syncthreads();
-    find_desc<4>(sh + 256, k - a1, i2, a2);
+    find_desc(sh + 256, k - a1, i2, a2);
     Ts = ((b1 << 8) | (255 - (int32_t)i2)) - 0x8000;
     cgt = a1 + a2;
     __syncthreads();  // every wave has read sh before the slots overwrite it
   }
   emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt, stage,
                                  reinterpret_cast<unsigned long long*>(bc + BC_SLOT));
+  return SEL_DONE;
+}
+
+// Keys above cs in the entries at e (wave-uniform count).
+__device__ __forceinline__ uint32_t count_above(const uint32_t* e, uint32_t cnt, int32_t cs) {
+  uint32_t c = 0;
+  for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
+    const uint32_t i = b0 + __lane_id();
+    const uint32_t x = i < cnt ? e[2 * i] : kDeadPair;
+    c += popc(__ballot(lo16s(x) > cs)) + popc(__ballot(hi16s(x) > cs));
+  }
+  return c;
 }
 
 // Every survivor key above cs of the entries at e, in order, straight out
@@ -802,6 +851,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   uint32_t* bc = smem + kBc;
   uint32_t* lists = smem + kLists;
   int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
+  int32_t* lpages =
+      (p.page_lds && o.pages) ? reinterpret_cast<int32_t*>(smem + p.page_lds) : nullptr;
 
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
@@ -816,6 +867,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     const int jt = (nvec - 1) / NT;   // last vector slot holding row data
     const int rem = nvec - jt * NT;   // vectors in it
     for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;  // sample + relative hists
+    for (int i = tid; i < 256 * kCopies; i += NT) lists[i] = 0; // replicated sample bins
     if (tid == 0) {
       bc[BC_EQ] = 0;
       bc[BC_SLOT] = 0;
@@ -828,6 +880,15 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     for (int j = 0; j < VPT; ++j) {
       const int vid = slot_vid<NT>(j, jt, rem);
       raw[j] = vid >= 0 ? src[vid] : make_uint4(~0u, ~0u, ~0u, ~0u);
+    }
+    // the row's block-table entries ride along, for an LDS copy
+    constexpr int PPT = kPageLdsMax / NT;
+    int32_t pgv[PPT];
+    const int npg = lpages ? (v + (1 << p.page_shift) - 1) >> p.page_shift : 0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int i = j * NT + tid;
+      pgv[j] = i < npg ? o.pages[i] : 0;
     }
     // sampled slots: every slot in token mode (one logit of every vector),
     // every SE-th slot in block mode (at most 2048 block keys)
@@ -857,9 +918,14 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
         S += (uint32_t)(j < jt ? NT : (j == jt ? rem : 0));
       }
     }
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const int i = j * NT + tid;
+      if (i < npg) lpages[i] = pgv[j];
+    }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
-    __syncthreads();  // histograms zeroed
-    const uint32_t c = sample_cutoff(sk, q, sh);
+    __syncthreads();  // histograms zeroed, block-table copy complete
+    const uint32_t c = sample_cutoff<NSK, NT>(sk, q, lists, sh);
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
       // a zero cutoff would make the zero keys of slots past the length ties
@@ -876,8 +942,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
           if (j <= jt)
-            keep_word(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, lists, wbase,
-                      cap, wcnt, ecnt);
+            keep_word<false>(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, lists,
+                             wbase, cap, wcnt, ecnt);
       } else if (cs >= 0) {
         // non-negative cutoff: the raw words serve as signed keys
 #pragma unroll
@@ -886,7 +952,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
             const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word(word_of(raw[j], q2), e8 + 2 * q2, cs, lists, wbase, cap, wcnt, ecnt);
+              keep_word<false>(word_of(raw[j], q2), e8 + 2 * q2, cs, lists, wbase, cap, wcnt,
+                               ecnt);
           }
         }
       } else {
@@ -896,35 +963,35 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
             const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word(skey2(word_of(raw[j], q2)), e8 + 2 * q2, cs, lists, wbase, cap, wcnt,
-                        ecnt);
+              keep_word<false>(skey2(word_of(raw[j], q2)), e8 + 2 * q2, cs, lists, wbase, cap,
+                               wcnt, ecnt);
           }
         }
       }
-      if (lane == 0) {
-        bc[BC_CNT + wave] = wcnt;
-        bc[BC_ECNT + wave] = ecnt;
-      }
-      __syncthreads();
-      uint32_t gt_total = 0, before = 0;
-      bool ovf = false;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t ew = bc[BC_ECNT + w];
-        before += w < wave ? ew : 0u;
-        gt_total += ew;
-        ovf |= bc[BC_CNT + w] > cap;
-      }
-      if (ovf) {
+      if (lane == 0) bc[BC_CNT + wave] = wcnt;
+      // exact select over the survivors; its histogram barrier also publishes
+      // the entry counts (overflow) and the count of keys above the cutoff
+      const int st = select_and_write<MODE, NW>(seg, min(wcnt, cap), cs, (uint32_t)k, rel, sh,
+                                                bc, stage, cap);
+      if (st == SEL_OVERFLOW) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
-      } else if (gt_total >= (uint32_t)k) {
-        // the k-th key lies above the cutoff: exact select over the survivors
-        select_and_write<MODE, NW>(seg, wcnt, cs, (uint32_t)k, rel, sh, bc, stage);
+      } else if (st == SEL_DONE) {
         __syncthreads();
-        flush_out<NT>(stage, o);
+        flush_out<NT>(stage, o, lpages);
         code = TOPK_PATH_SAMPLED;
       } else {
+        // fewer than k keys above the cutoff: per-wave counts for the slots
+        const uint32_t ew = count_above(seg, wcnt, cs);  // every lane takes part
+        if (lane == 0) bc[BC_ECNT + wave] = ew;
+        __syncthreads();
+        uint32_t gt_total = 0, before = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t ew = bc[BC_ECNT + w];
+          before += w < wave ? ew : 0u;
+          gt_total += ew;
+        }
         // the k-th key can only be the cutoff: collect keys equal to it
         uint16_t* ties = reinterpret_cast<uint16_t*>(rel);  // room for 2 kRelBins >= k
 #pragma unroll
@@ -993,7 +1060,8 @@ __device__ __forceinline__ uint32_t items_of(const Params& p, int row) {
 template <int MODE, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_cutoff(Params p) {
   constexpr int NT = kTeamNT;
-  __shared__ uint32_t sh[512];
+  __shared__ __align__(16) uint32_t sh[512];
+  __shared__ __align__(16) uint32_t h8[256 * kCopies + 256];
   __shared__ uint32_t bc[128];
   const int lrow = blockIdx.x;
   const int row = p.row0 + lrow;
@@ -1020,6 +1088,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_cutoff(Params p) {
   uint32_t c = 0u, flags = 0u;
   if (!p.force_direct) {
     for (int i = tid; i < 512; i += NT) sh[i] = 0;
+    for (int i = tid; i < 256 * kCopies; i += NT) h8[i] = 0;
     const int nvec = (v + 7) >> 3;
     // sample s of ns sits at vector floor((2 s + 1) nvec / (2 ns)), from a 32.32 step
     const int ns = min(SV * NT, nvec);
@@ -1045,7 +1114,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_cutoff(Params p) {
       }
     }
     const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
-    c = sample_cutoff(sk, sample_rank((uint32_t)k, (uint32_t)n, S), sh);
+    c = sample_cutoff<NSK, NT>(sk, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
     // a zero cutoff would make the zero keys of slots past the length ties
     if (MODE == TOPK_MODE_TOKEN && c == 0u) flags = kFlagDirect;
   } else {
@@ -1108,7 +1177,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
         const uint32_t key =
             lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         const uint32_t x = block_entry(key);
-        keep_word(x, (uint32_t)lvid, cs, seg, wbase, cap, wcnt, ecnt);
+        keep_word<true>(x, (uint32_t)lvid, cs, seg, wbase, cap, wcnt, ecnt);
         keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
       } else {
         if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
@@ -1117,7 +1186,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
         for (int q2 = 0; q2 < 4; ++q2) {
           const uint32_t w = word_of(raw[j], q2);
           const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
-          keep_word(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
+          keep_word<true>(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
           keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
         }
       }
@@ -1297,7 +1366,8 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       const uint32_t hi = min(lo + share, E);
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
       if (sampled) {
-        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage);
+        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage,
+                                   0xFFFFFFFFu);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key is the cutoff: every key above it, then the first ties
@@ -1456,7 +1526,12 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     p.rows = rows;
     p.row0 = 0;
     p.lcw = row_lcw(k, kRowNT / 64);
-    const size_t lds = row_lds_bytes(p.lcw, kRowNT / 64);
+    size_t lds = row_lds_bytes(p.lcw, kRowNT / 64);
+    if (bt && ((int64_t)width + bt->page_size - 1) / bt->page_size <= kPageLdsMax) {
+      // the rows' block-table entries get an LDS copy after everything else
+      p.page_lds = (int32_t)(lds / 4);
+      lds += (size_t)kPageLdsMax * 4;
+    }
     if (mode == TOPK_MODE_BLOCK)
       return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT>, rows, kRowNT, lds,
                     stream, p);
