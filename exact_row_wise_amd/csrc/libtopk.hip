@@ -63,11 +63,10 @@ constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
-constexpr int kTeamTokenVPT = 4;         // 16-byte vectors per thread of a token work item
 constexpr int kTeamBlockVPT = 16;        // 16-byte vectors per thread of a block work item
 constexpr int kTokenSV = 1;              // sample vectors per thread, token cutoff kernel
 constexpr int kBlockSV = 4;              // sample vectors per thread, block cutoff kernel
-constexpr int kMaxItems = 256;           // work items of one row at most (4 per item <= 1024 segments)
+constexpr int kMaxMembers = 64;          // members of a row at most (4 segments each <= 256)
 constexpr int kTeamLCW = 512;            // survivor entries per wave region of a member
 constexpr int kSpare = 64;               // region entries past the cap (one ballot step)
 constexpr int kTieLCW = TOPK_MAX_K / 4 + 128;     // tie entries per wave region of a member
@@ -104,21 +103,21 @@ enum {
   BC_TMP = 96     // 32: reductions, bin searches
 };
 
-// One work item's slice of global scratch (32-bit words), per wave w:
+// One team member's slice of global scratch (32-bit words), per wave w:
 //   [w]      survivor entries            [4 + w]  keys above the cutoff
 //   [8 + w]  tie entries                 [12 + w] keys equal to the cutoff in them
-//   [16 + w] keys equal to the cutoff
+//   [16 + w] keys equal to the cutoff    [20] the cutoff  [21] flags
 //   [32, 32 + 8 kTeamLCW) the waves' survivor entries (2 words each)
 //   then the waves' tie entries (kTieLCW each, 2 words each)
 constexpr int kMemberHdr = 32;
 constexpr int kMemberWords = kMemberHdr + 4 * 2 * kTeamLCW + 4 * 2 * kTieLCW;
-constexpr int H_WCNT = 0, H_ECNT = 4, H_TW = 8, H_TKEPT = 12, H_NEQ = 16;
+constexpr int H_WCNT = 0, H_ECNT = 4, H_TW = 8, H_TKEPT = 12, H_NEQ = 16, H_CUT = 20, H_FLAGS = 21;
 constexpr uint32_t kFlagDirect = 1u;
-static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamTokenVPT - 1) / (kTeamNT * kTeamTokenVPT) <= kMaxItems,
-              "too many token work items per row");
-static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) / (kTeamNT * kTeamBlockVPT) <= kMaxItems,
-              "too many block work items per row");
-static_assert(4 * kMaxItems <= kSelNT, "one select thread per segment");
+static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * 8 - 1) / (kTeamNT * 8) <= kMaxMembers,
+              "too many token members per row");
+static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) / (kTeamNT * kTeamBlockVPT) <=
+                  kMaxMembers, "too many block members per row");
+static_assert(4 * kMaxMembers <= kSelNT, "one select thread per segment");
 
 struct Params {
   const uint16_t* logits;
@@ -138,11 +137,9 @@ struct Params {
   int32_t lcw;         // survivor entries per wave before the cap (one-workgroup kernel)
   int32_t page_lds;    // LDS word offset of a row's block-table copy (one-workgroup kernel), or 0
   // team path (rows wider than one workgroup), all in one scratch buffer:
-  uint32_t* team_info;   // [rows][4]: cutoff, flags, first work item, work items
-  uint32_t* team_items;  // [max items]: the row of each work item
-  uint32_t* team_total;  // work items of the launch
-  uint32_t* team_slices; // [max items][kMemberWords]
-  int32_t team_cv;       // 16-byte vectors of one work item
+  int32_t G;             // team members per row (for the widest row)
+  int32_t team_cv;       // 16-byte vectors of one member
+  uint32_t* team_slices; // [rows][G][kMemberWords]
   int32_t sel_cap;       // survivor entries the select kernel stages in LDS
 };
 
@@ -423,7 +420,7 @@ __device__ __forceinline__ Out row_out(const Params& p, int row, bool block) {
 // when `lpages` is given, else the table in global memory.  Follows a
 // barrier.
 template <int NT>
-__device__ void flush_out(const int32_t* stage, const Out& o, const int32_t* lpages = nullptr) {
+__device__ void flush_out(const int32_t* stage, const Out o, const int32_t* lpages = nullptr) {
   auto map = [&](int32_t x) -> int32_t {
     if (!lpages) return o.map(x);
     const int32_t i = x < 0 ? 0 : x;
@@ -450,14 +447,14 @@ __device__ __forceinline__ void set_path(const Params& p, int row, int code) {
 // Token rows with n <= k: 0..n-1 then -1, no logits read
 // (decode_topk_cute result definition; kimi_k3 IndexerSelect bypass).
 template <int NT>
-__device__ void write_short_token(const Out& o, int n, int k) {
+__device__ void write_short_token(const Out o, int n, int k) {
   for (int e = threadIdx.x; e < k; e += NT) o.out[e] = o.map(e < n ? e : -1);
 }
 
 // Block rows with n <= k: every block in order, -1 for -inf blocks, the
 // newest pinned at +inf, then -1 padding.
 template <int NT>
-__device__ void write_short_block(const Out& o, const uint4* src, int n, int k) {
+__device__ void write_short_block(const Out o, const uint4* src, int n, int k) {
   for (int b = threadIdx.x; b < k; b += NT) {
     if (b < n) {
       const uint32_t key = (b == n - 1) ? kKeyPosInf : block_key4(src[b]);
@@ -476,7 +473,7 @@ __device__ void write_short_block(const Out& o, const uint4* src, int n, int k) 
 // when the sampled cutoff misjudged the row, or on request.  n > k.
 // `region` holds kDirectWords words of LDS.
 template <int MODE, int NT>
-__device__ void direct_select(const uint4* src, int v, int n, int k, const Out& o,
+__device__ void direct_select(const uint4* src, int v, int n, int k, const Out o,
                               uint32_t* region, uint32_t* bc) {
   const int tid = threadIdx.x;
   const int copy = __lane_id() & (kCopies - 1);
@@ -776,7 +773,7 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* e, uint32_t cnt,
 // to the slots from `base` on: the one-workgroup tie pass's first part.
 template <int MODE>
 __device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t base,
-                            const Out& o) {
+                            const Out o) {
   const int lane = __lane_id();
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
@@ -1031,116 +1028,30 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 }
 
 // ============================================ team of workgroups per row
-// A row wider than one workgroup is cut into work items of team_cv
-// vectors (the items split the valid length).  Three stream-ordered
-// kernels: the cutoff kernel (one workgroup a row) takes the row's cutoff
-// from samples spread over the row and lays out the work items; the filter
-// kernel (one workgroup an item) compacts the item's entries above and
-// equal to the cutoff into the item's scratch slice; the select kernel
-// (one workgroup a row) finishes the row.  Each kernel reads what the one
-// before it wrote, after the kernel boundary: no workgroup waits for
-// another and no atomic or fence crosses workgroups.
+// A row wider than one workgroup is split over member workgroups of fixed
+// chunks of its valid length (G per row in the grid, for the widest row); a
+// second kernel, one workgroup per row, finishes it after the kernel
+// boundary.  The members of a row share
+// blockIdx % 8, so they run on one XCD and the row's samples, loaded by
+// every member, come from that XCD's L2 after the first.
 
-enum { TI_CUT = 0, TI_FLAGS = 1, TI_FIRST = 2, TI_ITEMS = 3 };
-
-// Work items of a row: none when the row is short or goes straight to the
-// direct path.
-template <int MODE>
-__device__ __forceinline__ uint32_t items_of(const Params& p, int row) {
-  const int v = clamp_len(p.valid_len[row], p.width);
-  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  if (n <= p.k || p.force_direct) return 0u;
-  const int nvec = (v + 7) >> 3;
-  return (uint32_t)((nvec + p.team_cv - 1) / p.team_cv);
-}
-
-// Stage 1: short rows are written here; every other row gets its cutoff
-// (samples spread over the whole row, as in the one-workgroup kernel) and
-// its work items [first, first + items) of the launch.
-template <int MODE, int SV>
-__global__ __launch_bounds__(kTeamNT) void topk_team_cutoff(Params p) {
+// Stage 1: every member loads the row's samples (spread over the whole
+// row; the same in every member) and then its chunk of NT * VPT vectors
+// (members past the row's valid length exit at once), derives the row's
+// cutoff while its chunk is still in flight, and writes to its scratch
+// slice the entries holding a key above the cutoff and, in the same pass,
+// those holding a key equal to it (chunk-local indices).  Short rows and
+// rows sent straight to the direct path are left to stage 2.
+template <int MODE, int VPT, int SV>
+__global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
   __shared__ __align__(16) uint32_t sh[512];
   __shared__ __align__(16) uint32_t h8[256 * kCopies + 256];
   __shared__ uint32_t bc[128];
-  const int lrow = blockIdx.x;
-  const int row = p.row0 + lrow;
-  const int tid = threadIdx.x;
-  const int k = p.k;
-  const int v = clamp_len(p.valid_len[row], p.width);
-  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-  // this row's first work item: the items of the launch's earlier rows
-  uint32_t before = 0;
-  for (int r = tid; r < lrow; r += NT) before += items_of<MODE>(p, p.row0 + r);
-  const uint32_t first = block_sum<NT>(before, bc + BC_TMP);
-  const uint32_t items = items_of<MODE>(p, row);
-  uint32_t* info = p.team_info + (size_t)lrow * 4;
-  for (uint32_t i = tid; i < items; i += NT) p.team_items[first + i] = (uint32_t)lrow;
-  if (lrow == p.rows - 1 && tid == 0) *p.team_total = first + items;
-  if (n <= k) {
-    const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
-    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
-    else write_short_token<NT>(o, n, k);
-    set_path(p, row, TOPK_PATH_SHORT);
-    return;
-  }
-  uint32_t c = 0u, flags = 0u;
-  if (!p.force_direct) {
-    for (int i = tid; i < 512; i += NT) sh[i] = 0;
-    for (int i = tid; i < 256 * kCopies; i += NT) h8[i] = 0;
-    const int nvec = (v + 7) >> 3;
-    // sample s of ns sits at vector floor((2 s + 1) nvec / (2 ns)), from a 32.32 step
-    const int ns = min(SV * NT, nvec);
-    const uint64_t step = ((uint64_t)nvec << 32) / (uint64_t)(2 * ns);
-    constexpr int NSK = (MODE == TOPK_MODE_BLOCK) ? SV : SV * 8;
-    uint32_t sk[NSK];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int j = 0; j < SV; ++j) {
-      const int s = j * NT + tid;
-      const int vid = s < ns ? (int)(((uint64_t)(2 * s + 1) * step) >> 32) : -1;
-      const uint4 raw = vid >= 0 ? src[vid] : make_uint4(~0u, ~0u, ~0u, ~0u);
-      if constexpr (MODE == TOPK_MODE_BLOCK) {
-        sk[j] = vid < 0 ? kNone : (vid == n - 1 ? kKeyPosInf : block_key4(raw));
-        mine += vid >= 0 ? 1u : 0u;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool ok = vid >= 0 && vid * 8 + e < v;
-          sk[j * 8 + e] = ok ? key1(half_of(word_of(raw, e >> 1), e & 1)) : kNone;
-          mine += ok ? 1u : 0u;
-        }
-      }
-    }
-    const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
-    c = sample_cutoff<NSK, NT>(sk, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
-    // a zero cutoff would make the zero keys of slots past the length ties
-    if (MODE == TOPK_MODE_TOKEN && c == 0u) flags = kFlagDirect;
-  } else {
-    flags = kFlagDirect;
-  }
-  if (tid == 0) {
-    info[TI_CUT] = c;
-    info[TI_FLAGS] = flags;
-    info[TI_FIRST] = first;
-    info[TI_ITEMS] = items;
-  }
-}
-
-// Stage 2: one workgroup per work item (grid: an upper bound on the items;
-// the rest exit).  Loads the item's vectors, and writes to the item's
-// scratch slice the entries holding a key above the row's cutoff and, in
-// the same pass, those holding a key equal to it (item-local indices).
-// Waves work alone: no LDS, no barrier.
-template <int MODE, int VPT>
-__global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
-  constexpr int NT = kTeamNT;
-  const uint32_t item = blockIdx.x;
-  if (item >= *p.team_total) return;
-  const int lrow = (int)p.team_items[item];
-  const uint32_t* info = p.team_info + (size_t)lrow * 4;
-  if (info[TI_FLAGS] & kFlagDirect) return;
+  const int G = p.G;
+  const int b = blockIdx.x, xg = b & 7, yg = b >> 3;
+  const int lrow = (yg / G) * 8 + xg, member = yg % G;
+  if (lrow >= p.rows) return;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
@@ -1148,21 +1059,79 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const int k = p.k;
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
+  if (n <= k || p.force_direct) return;
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  // members take NT * VPT vectors each; those past the row's length exit
   const int nvec = (v + 7) >> 3;
-  const int vb = (int)(item - info[TI_FIRST]) * p.team_cv;
-  const int ve = min(vb + p.team_cv, nvec);
+  const int vb = member * NT * VPT;
+  if (vb >= nvec) return;
+  const int ve = min(vb + NT * VPT, nvec);
   const int jt = (ve - vb - 1) / NT;   // last occupied slot
   const int rem = (ve - vb) - jt * NT; // vectors in it
+  for (int i = tid; i < 512; i += NT) sh[i] = 0;
+  for (int i = tid; i < 256 * kCopies; i += NT) h8[i] = 0;
+
+  // -- sample loads, then chunk loads.  The samples are the same in every
+  // member of the row: every vector of a short row; otherwise SV * NT / 8
+  // runs of 8 consecutive vectors (one 128-byte line each), run r starting
+  // at line floor((2 r + 1) lines / (2 runs)) (a 32.32 step), so that the
+  // row's members share few lines.
+  const int ns = min(SV * NT, nvec);
+  const int nl = nvec >> 3, runs = SV * NT / 8;
+  const uint64_t step = nvec > SV * NT ? ((uint64_t)nl << 32) / (uint64_t)(2 * runs) : 0;
+  uint4 sraw[SV];
+  int spos[SV];
+#pragma unroll
+  for (int j = 0; j < SV; ++j) {
+    const int si = j * NT + tid;
+    if (nvec <= SV * NT) {
+      spos[j] = si < ns ? si : -1;
+    } else {
+      const int r = si >> 3;
+      spos[j] = (int)((((uint64_t)(2 * r + 1) * step) >> 32) << 3) + (si & 7);
+    }
+    sraw[j] = spos[j] >= 0 ? src[spos[j]] : make_uint4(~0u, ~0u, ~0u, ~0u);
+  }
   uint4 raw[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     const int lvid = slot_vid<NT>(j, jt, rem);
     raw[j] = lvid >= 0 ? src[vb + lvid] : make_uint4(~0u, ~0u, ~0u, ~0u);
   }
-  const uint32_t c = info[TI_CUT];
+  // -- the cutoff, identical in every member, while the chunk arrives
+  constexpr int NSK = (MODE == TOPK_MODE_BLOCK) ? SV : SV * 8;
+  uint32_t sk[NSK];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < SV; ++j) {
+    const int vid = spos[j];
+    if constexpr (MODE == TOPK_MODE_BLOCK) {
+      sk[j] = vid < 0 ? kNone : (vid == n - 1 ? kKeyPosInf : block_key4(sraw[j]));
+      mine += vid >= 0 ? 1u : 0u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool ok = vid >= 0 && vid * 8 + e < v;
+        sk[j * 8 + e] = ok ? key1(half_of(word_of(sraw[j], e >> 1), e & 1)) : kNone;
+        mine += ok ? 1u : 0u;
+      }
+    }
+  }
+  const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
+  const uint32_t c = sample_cutoff<NSK, NT>(sk, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
+  uint32_t* slice = p.team_slices + ((size_t)lrow * G + member) * kMemberWords;
+  if (MODE == TOPK_MODE_TOKEN && c == 0u) {
+    // a zero cutoff would make the zero keys of slots past the length ties:
+    // every member sees the same cutoff and flags the row for the direct path
+    if (tid == 0) {
+      slice[H_CUT] = c;
+      slice[H_FLAGS] = kFlagDirect;
+    }
+    return;
+  }
+
+  // -- entries above / equal to the cutoff straight to this wave's regions
   const int32_t cs = (int32_t)c - 0x8000;
-  uint32_t* slice = p.team_slices + (size_t)item * kMemberWords;
   uint32_t* seg = slice + kMemberHdr;
   uint32_t* tl = slice + kMemberHdr + 8 * kTeamLCW;
   const uint32_t wv = readfirst((uint32_t)wave);
@@ -1199,10 +1168,14 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     slice[H_TKEPT + wave] = tkept;
     slice[H_NEQ + wave] = neq;
   }
+  if (tid == 0) {
+    slice[H_CUT] = c;
+    slice[H_FLAGS] = 0u;
+  }
 }
 
 // LDS of the select kernel past kLists (words)
-constexpr int kSelStart = 0;         // survivor entry starts of the <= 4 kMaxItems segments
+constexpr int kSelStart = 0;         // survivor entry starts of the <= 4 kMaxMembers segments
 constexpr int kSelTstart = 1024;     // tie entry starts
 constexpr int kSelSegc = 2048;       // survivor entries per segment
 constexpr int kSelTsegc = 3072;      // tie entries per segment
@@ -1260,9 +1233,14 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   const int k = p.k;
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  if (n <= k) return;  // written by the cutoff stage
   const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  if (n <= k) {
+    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
+    else write_short_token<NT>(o, n, k);
+    set_path(p, row, TOPK_PATH_SHORT);
+    return;
+  }
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
@@ -1272,15 +1250,20 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   uint32_t* segc = smem + kLists + kSelSegc;
   uint32_t* tsegc = smem + kLists + kSelTsegc;
   uint32_t* ent = smem + kLists + kSelStage;
-  const uint32_t* info = p.team_info + (size_t)lrow * 4;
-  const uint32_t rflags = info[TI_FLAGS];
-  bool direct = (rflags & kFlagDirect) != 0;
-  int code = p.force_direct ? TOPK_PATH_DIRECT_FORCED : TOPK_PATH_DIRECT_MISJUDGED;
+  const int G = p.G;
+  const uint32_t* slices = p.team_slices + (size_t)lrow * G * kMemberWords;
+  bool direct = p.force_direct != 0;
+  int code = TOPK_PATH_DIRECT_FORCED;
+  if (!direct && (slices[H_FLAGS] & kFlagDirect)) {
+    direct = true;
+    code = TOPK_PATH_DIRECT_MISJUDGED;
+  }
   if (!direct) {
-    const uint32_t* slices = p.team_slices + (size_t)info[TI_FIRST] * kMemberWords;
-    // item starts in element units: 8 logits per vector, one block per vector
+    const int nvec = (v + 7) >> 3;
+    const int gr = (nvec + p.team_cv - 1) / p.team_cv;  // members of this row
+    // chunk starts in element units: 8 logits per vector, one block per vector
     const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
-    const int nseg = 4 * (int)info[TI_ITEMS];  // <= 4 kMaxItems = NT: one segment per thread
+    const int nseg = 4 * gr;  // <= 4 kMaxMembers <= NT: one segment per thread
     for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
@@ -1329,7 +1312,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       segc[tid] = wc;
       tsegc[tid] = tw;
     }
-    const uint32_t c = info[TI_CUT];
+    const uint32_t c = slices[H_CUT];
     const int32_t cs = (int32_t)c - 0x8000;
     __syncthreads();
     const uint32_t cap = (uint32_t)p.sel_cap;
@@ -1539,28 +1522,22 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
                   stream, p);
   }
 
-  // team path: cutoff kernel, filter kernel (one workgroup per work item),
-  // select kernel.  Scratch per launch: row info, the row of every work
-  // item, the item count, then one slice per work item.
-  const int cv = kTeamNT * (mode == TOPK_MODE_BLOCK ? kTeamBlockVPT : kTeamTokenVPT);
-  const int max_items_row = (nvec_max + cv - 1) / cv;  // <= kMaxItems
-  const size_t row_bytes = (size_t)max_items_row * ((size_t)kMemberWords + 1) * 4 + 16;
+  // team path: G members per row (filter kernel), then one workgroup per
+  // row (select kernel).  Scratch: one slice per member of a launch's rows.
+  const int vpt = mode == TOPK_MODE_BLOCK ? kTeamBlockVPT
+                                          : (nvec_max <= kMaxMembers * kTeamNT * 4 ? 4 : 8);
+  const int cv = kTeamNT * vpt;
+  const int G = (nvec_max + cv - 1) / cv;  // <= kMaxMembers
+  const size_t row_bytes = (size_t)G * kMemberWords * 4;
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
   if ((size_t)batch * row_bytes > kTeamScratchMax) batch = (int)(kTeamScratchMax / row_bytes);
-  if (batch < 1) batch = 1;
-  const size_t max_items = (size_t)batch * max_items_row;
-  const size_t off_items = (size_t)batch * 4;
-  const size_t off_total = (off_items + max_items + 63) / 64 * 64;
-  const size_t off_slices = off_total + 64;
+  batch = batch < 8 ? 8 : batch / 8 * 8;  // whole groups of 8 rows (one per XCD)
   void* scratch = nullptr;
-  int rc = get_scratch(stream, (off_slices + max_items * kMemberWords) * 4, &scratch);
+  int rc = get_scratch(stream, (size_t)batch * row_bytes, &scratch);
   if (rc != TOPK_OK) return rc;
-  uint32_t* sw = static_cast<uint32_t*>(scratch);
-  p.team_info = sw;
-  p.team_items = sw + off_items;
-  p.team_total = sw + off_total;
-  p.team_slices = sw + off_slices;
+  p.G = G;
   p.team_cv = cv;
+  p.team_slices = static_cast<uint32_t*>(scratch);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   // stage as many survivor entries as the LDS of one workgroup holds
@@ -1572,18 +1549,18 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     const int nr = (rows - r0) < batch ? (rows - r0) : batch;
     p.row0 = r0;
     p.rows = nr;
-    const int grid = nr * max_items_row;
-    if (mode == TOPK_MODE_BLOCK) {
-      rc = launch(topk_team_cutoff<TOPK_MODE_BLOCK, kBlockSV>, nr, kTeamNT, 0, stream, p);
-      if (rc == TOPK_OK)
-        rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kTeamBlockVPT>, grid, kTeamNT, 0, stream, p);
-      if (rc == TOPK_OK)
+    const int grid = (nr + 7) / 8 * 8 * G;
+    if (mode == TOPK_MODE_BLOCK)
+      rc = launch(topk_team_filter<TOPK_MODE_BLOCK, kTeamBlockVPT, kBlockSV>, grid, kTeamNT, 0,
+                  stream, p);
+    else if (vpt == 4)
+      rc = launch(topk_team_filter<TOPK_MODE_TOKEN, 4, kTokenSV>, grid, kTeamNT, 0, stream, p);
+    else
+      rc = launch(topk_team_filter<TOPK_MODE_TOKEN, 8, kTokenSV>, grid, kTeamNT, 0, stream, p);
+    if (rc == TOPK_OK) {
+      if (mode == TOPK_MODE_BLOCK)
         rc = launch(topk_team_select<TOPK_MODE_BLOCK>, nr, kSelNT, sel_lds, stream, p);
-    } else {
-      rc = launch(topk_team_cutoff<TOPK_MODE_TOKEN, kTokenSV>, nr, kTeamNT, 0, stream, p);
-      if (rc == TOPK_OK)
-        rc = launch(topk_team_filter<TOPK_MODE_TOKEN, kTeamTokenVPT>, grid, kTeamNT, 0, stream, p);
-      if (rc == TOPK_OK)
+      else
         rc = launch(topk_team_select<TOPK_MODE_TOKEN>, nr, kSelNT, sel_lds, stream, p);
     }
     if (rc != TOPK_OK) return rc;
