@@ -1182,45 +1182,12 @@ constexpr int kSelTsegc = 3072;      // tie entries per segment
 constexpr int kSelStage = 4096;      // staged entries, 2 words each
 constexpr int kSelFixed = kLists + kSelStage;  // words before the staged entries
 
-// Copies the entries of segments wave, wave + NW, ... (segment s: n_s
-// entries at src_s, chunk-local indices) into LDS at dst[s] with row-level
-// indices.  The first 64 entries of four segments are in flight together.
-template <int NW, class SrcOf, class CntOf>
-__device__ void stage_segments(int nseg, SrcOf src_of, CntOf cnt_of, const uint32_t* dst,
-                               uint32_t chunk, uint32_t* ent) {
-  constexpr int U = 4;
-  const int lane = __lane_id();
-  const int wave = threadIdx.x >> 6;
-  for (int s0 = wave; s0 < nseg; s0 += NW * U) {
-    uint2 en[U];
-    uint32_t cnt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * NW;
-      cnt[u] = s < nseg ? cnt_of(s) : 0u;
-      en[u] = (uint32_t)lane < cnt[u] ? *reinterpret_cast<const uint2*>(src_of(s) + 2 * lane)
-                                      : make_uint2(0u, 0u);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int s = s0 + u * NW;
-      if ((uint32_t)lane < cnt[u]) {
-        const uint32_t d = dst[s] + lane, g = (uint32_t)(s >> 2) * chunk;
-        *reinterpret_cast<uint2*>(ent + 2 * d) = make_uint2(en[u].x, en[u].y + g);
-      }
-      for (uint32_t i = 64 + lane; i < cnt[u]; i += 64) {
-        const uint2 x = *reinterpret_cast<const uint2*>(src_of(s) + 2 * i);
-        const uint32_t d = dst[s] + i, g = (uint32_t)(s >> 2) * chunk;
-        *reinterpret_cast<uint2*>(ent + 2 * d) = make_uint2(x.x, x.y + g);
-      }
-    }
-  }
-}
-
-// Stage 3: one 1024-thread workgroup per row reads the slices of its work
-// items (written by the previous kernel, so plain loads see them), checks
-// that the cutoff held, and writes the row: exact select over the
-// survivors, the tie pass, or the direct path.
+// Stage 2: one 1024-thread workgroup per row writes short rows, and
+// otherwise reads the slices of the row's members (written by the previous
+// kernel, so plain loads see them; the first 64 entries of each segment are
+// loaded together with the headers), checks that the cutoff held, and
+// writes the row: exact select over the survivors, the tie pass, or the
+// direct path.
 template <int MODE>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
@@ -1269,7 +1236,26 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-    // per segment (item, wave): entry counts, key counts, overflow
+    auto seg_src = [&](int s2) {
+      return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + (s2 & 3) * 2 * kTeamLCW;
+    };
+    // the first 64 entries of segments wave, wave + NW, ... (up to kPre of
+    // them) are loaded with the headers, before their counts are known
+    auto tie_src = [&](int s2) {
+      return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
+             (s2 & 3) * 2 * kTieLCW;
+    };
+    constexpr int kPre = 8;
+    uint2 pre[kPre], tpre[kPre];  // the same for the tie entries
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int s2 = wave + u * NW;
+      pre[u] = s2 < nseg ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
+                         : make_uint2(kDeadPair, 0u);
+      tpre[u] = s2 < nseg ? *reinterpret_cast<const uint2*>(tie_src(s2) + 2 * lane)
+                          : make_uint2(kDeadPair, 0u);
+    }
+    // per segment (member, wave): entry counts, key counts, overflow
     uint32_t wc = 0, ec = 0, tw = 0, tk = 0, nq = 0, bad = 0;
     if (tid < nseg) {
       const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
@@ -1293,19 +1279,16 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     }
     if (lane == 0) bc[BC_CNT + wave] = mb ? 1u : 0u;
     __syncthreads();
-    uint32_t ow = 0, ot = 0, E = 0, Et = 0, gt_total = 0, avail = 0, eq_total = 0, flags = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const bool lower = w < wave;
-      ow += lower ? bc[BC_TMP + w] : 0u;
-      ot += lower ? bc[BC_TMP + 16 + w] : 0u;
-      E += bc[BC_TMP + w];
-      Et += bc[BC_TMP + 16 + w];
-      gt_total += bc[BC_X + w];
-      avail += bc[BC_CGT + w];
-      eq_total += bc[BC_CEQ + w];
-      flags |= bc[BC_CNT + w];
-    }
+    // lane w < NW holds wave w's sums; scans across those lanes
+    const bool lw = lane < NW;
+    const uint32_t aw = lw ? bc[BC_TMP + lane] : 0u, at = lw ? bc[BC_TMP + 16 + lane] : 0u;
+    const uint32_t sw_ = wave_incl_scan(aw), st_ = wave_incl_scan(at);
+    const uint32_t ow = readlane(sw_ - aw, wave), ot = readlane(st_ - at, wave);
+    const uint32_t E = readlane(sw_, 63), Et = readlane(st_, 63);
+    const uint32_t gt_total = readlane(wave_incl_scan(lw ? bc[BC_X + lane] : 0u), 63);
+    const uint32_t avail = readlane(wave_incl_scan(lw ? bc[BC_CGT + lane] : 0u), 63);
+    const uint32_t eq_total = readlane(wave_incl_scan(lw ? bc[BC_CEQ + lane] : 0u), 63);
+    const uint32_t flags = __ballot(lw && bc[BC_CNT + lane] != 0u) ? 1u : 0u;
     if (tid < nseg) {
       start[tid] = ow + iw - wc;
       tstart[tid] = ot + it - tw;
@@ -1329,19 +1312,46 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       code = TOPK_PATH_DIRECT_OVERFLOW;
     } else {
       // stage the survivor entries (and, for the tie pass, the tie entries
-      // after them) in LDS with row-level indices
-      auto seg_src = [&](int s) {
-        return slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr + (s & 3) * 2 * kTeamLCW;
-      };
-      auto seg_cnt = [&](int s) { return segc[s]; };
-      stage_segments<NW>(nseg, seg_src, seg_cnt, start, chunk, ent);
+      // after them) in LDS with row-level indices: the preloaded chunks
+      // first, then whatever they did not cover
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const int s2 = wave + u * NW;
+        if (s2 < nseg && (uint32_t)lane < segc[s2]) {
+          const uint32_t d = start[s2] + lane;
+          *reinterpret_cast<uint2*>(ent + 2 * d) =
+              make_uint2(pre[u].x, pre[u].y + (uint32_t)(s2 >> 2) * chunk);
+        }
+      }
+      for (int s2 = wave; s2 < nseg; s2 += NW) {
+        const uint32_t from = s2 < kPre * NW ? 64u : 0u;
+        const uint32_t* es = seg_src(s2);
+        const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
+        for (uint32_t i = from + lane; i < segc[s2]; i += 64) {
+          const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
+          *reinterpret_cast<uint2*>(ent + 2 * (start[s2] + i)) = make_uint2(x.x, x.y + g);
+        }
+      }
       if (!sampled) {
-        auto tie_src = [&](int s) {
-          return slices + (size_t)(s >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
-                 (s & 3) * 2 * kTieLCW;
-        };
-        auto tie_cnt = [&](int s) { return tsegc[s]; };
-        stage_segments<NW>(nseg, tie_src, tie_cnt, tstart, chunk, ent + 2 * E);
+        uint32_t* tent = ent + 2 * E;
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+          const int s2 = wave + u * NW;
+          if (s2 < nseg && (uint32_t)lane < tsegc[s2]) {
+            const uint32_t d = tstart[s2] + lane;
+            *reinterpret_cast<uint2*>(tent + 2 * d) =
+                make_uint2(tpre[u].x, tpre[u].y + (uint32_t)(s2 >> 2) * chunk);
+          }
+        }
+        for (int s2 = wave; s2 < nseg; s2 += NW) {
+          const uint32_t from = s2 < kPre * NW ? 64u : 0u;
+          const uint32_t* es = tie_src(s2);
+          const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
+          for (uint32_t i = from + lane; i < tsegc[s2]; i += 64) {
+            const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
+            *reinterpret_cast<uint2*>(tent + 2 * (tstart[s2] + i)) = make_uint2(x.x, x.y + g);
+          }
+        }
       }
       __syncthreads();
       const uint32_t share = (E + NW - 1) / NW;
