@@ -63,7 +63,7 @@ constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
-constexpr int kTeamBlockVPT = 16;        // 16-byte vectors per thread of a block work item
+constexpr int kTeamBlockVPT = 12;        // 16-byte vectors per thread of a block work item
 constexpr int kTokenSV = 1;              // sample vectors per thread, token cutoff kernel
 constexpr int kBlockSV = 4;              // sample vectors per thread, block cutoff kernel
 constexpr int kMaxMembers = 64;          // members of a row at most (4 segments each <= 256)
@@ -86,11 +86,12 @@ constexpr uint32_t kDeadPair = 0x80008000u;  // two signed keys at the very bott
 
 // LDS (32-bit words), shared by the one-workgroup and the select kernels
 constexpr int kBc = 0;                          // 128 words of counters and per-wave fields
-constexpr int kStage = 128;                     // k output slots, overlapping:
+constexpr int kEmitDummy = 128;                 // 64 words: one per lane for stores that drop
+constexpr int kStage = 192;                     // k output slots, overlapping:
 constexpr int kSampHist = kStage;               //   256 low-byte sample bins / 2 x 256 bins
-constexpr int kRelHist = kStage + 512;          //   kRelBins bins / u16 tie list
+constexpr int kRelHist = kStage + 512;          //   kRelBins bins + 64 spill bins / u16 ties
 constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
-static_assert(kRelHist + kRelBins <= kLists, "histograms overlap the lists");
+static_assert(kRelHist + kRelBins + 64 <= kLists, "histograms overlap the lists");
 enum {
   BC_CNT = 0,     // 16: entries per wave
   BC_ECNT = 16,   // 16: survivor keys per wave
@@ -236,6 +237,30 @@ __device__ __forceinline__ int slot_vid(int j, int jt, int rem) {
 }
 
 // ----------------------------------------------------------- wave tools
+// Byte address in LDS of a pointer into shared memory (the low half of its
+// generic address), computed once into a scalar register (left alone, the
+// compiler recomputes the conversion's null test at every use).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  uint32_t a = (uint32_t)reinterpret_cast<uintptr_t>(p);
+  asm("" : "+s"(a));
+  return a;
+}
+// Lanes of m take a, the others b: one vector select (the compiler would
+// otherwise turn some of these into exec-mask branches).
+__device__ __forceinline__ uint32_t pick(unsigned long long m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
+  return r;
+}
+// Stores at LDS byte address a (a plain 32-bit address, so that address
+// arithmetic stays in single vector ops): one word, or the pair (lo, hi).
+__device__ __forceinline__ void lds_store(uint32_t a, int32_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) int32_t*>(a) = v;
+}
+__device__ __forceinline__ void lds_store2(uint32_t a, uint32_t lo, uint32_t hi) {
+  *reinterpret_cast<__attribute__((address_space(3))) unsigned long long*>(a) =
+      ((unsigned long long)hi << 32) | lo;
+}
 __device__ __forceinline__ uint32_t mbcnt(unsigned long long m, uint32_t add = 0u) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, add));
@@ -567,27 +592,32 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
 // falls back to the direct path; exactness never depends on this choice).
 __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t S) {
   if (S >= n) return k;  // every element sampled: the cutoff is the k-th key
-  const uint32_t q0 = (k * S) / n;  // k <= 2048 and S <= 4096: no overflow
-  // the margin's square root in single precision: it sizes the work only
-  const uint32_t q = q0 + (uint32_t)(4.5f * __builtin_sqrtf((float)q0)) + 9u;
+  // k S / n and the margin's square root in single precision with the
+  // hardware's approximate reciprocal and root: they size the work only
+  const float f0 = (float)(k * S) * __builtin_amdgcn_rcpf((float)n);
+  const uint32_t q = (uint32_t)(f0 + 4.5f * __builtin_amdgcn_sqrtf(f0)) + 9u;
   return q < S ? q : S;
 }
 
-// The q-th largest of the samples (kNone marks an empty slot): two 8-bit
-// radix passes (decode_topk_cute, radix_select over the samples).  The
-// high-byte pass counts into kCopies replicated bins (lane mod 8) at h8
-// (256 kCopies words, zeroed), since sampled keys of smooth data crowd a
-// few high bytes and same-word LDS atomics serialize; 256 threads then sum
-// the copies into h8 + 256 kCopies (256 words).  The low-byte pass counts
-// into sh (256 words, zeroed).  Every wave finds the bins itself.
+// The q-th largest of the samples (kNone marks an empty slot; the first
+// `lead` samples are known not to be empty): two 8-bit radix passes
+// (decode_topk_cute, radix_select over the samples).  The high-byte pass
+// counts into kCopies replicated bins (lane mod 8) at h8 (256 kCopies
+// words, zeroed), since sampled keys of smooth data crowd a few high bytes
+// and same-word LDS atomics serialize; 256 threads then sum the copies into
+// h8 + 256 kCopies (256 words).  The low-byte pass counts into sh (256
+// words, zeroed; a sample outside the chosen high byte counts into the
+// lane's own word of sh[256, 320) instead).  Every wave finds the bins
+// itself.
 template <int NSK, int NT>
-__device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_t* h8,
+__device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
                                   uint32_t* sh) {
   static_assert(NT >= 256, "one thread per high-byte bin");
   const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
-  for (int i = 0; i < NSK; ++i)
-    if (sk[i] != kNone) atomicAdd(&h8[(255u - (sk[i] >> 8)) * kCopies + copy], 1u);
+  for (int i = 0; i < NSK; ++i) {
+    if (i < lead || sk[i] != kNone) atomicAdd(&h8[(255u - (sk[i] >> 8)) * kCopies + copy], 1u);
+  }
   __syncthreads();
   uint32_t* sums = h8 + 256 * kCopies;
   if (threadIdx.x < 256) {
@@ -599,9 +629,12 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], uint32_t q, uint32_
   uint32_t i1, a1;
   find_desc(sums, q, i1, a1);
   const uint32_t b1 = 255u - i1;
+  const uint32_t spill = 256u + __lane_id();
 #pragma unroll
-  for (int i = 0; i < NSK; ++i)
-    if (sk[i] != kNone && (sk[i] >> 8) == b1) atomicAdd(&sh[255u - (sk[i] & 255u)], 1u);
+  for (int i = 0; i < NSK; ++i) {
+    const uint32_t x = sk[i];  // an empty slot's high byte is never b1
+    atomicAdd(&sh[pick(__ballot((x >> 8) == b1), 255u - (x & 255u), spill)], 1u);
+  }
   __syncthreads();
   uint32_t i2, a2;
   find_desc(sh, q - a1, i2, a2);
@@ -635,47 +668,81 @@ __device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs,
   if (COUNT_KEYS) ecnt += popc(mlo) + popc(mhi);
 }
 
+// The same into LDS without touching the exec mask (fewer scalar
+// instructions): one test per entry on the larger of its two keys, and
+// every lane stores, a lane without a key above cs into its own slot of a
+// dummy area (LDS byte address `dummy`).  at is the LDS byte address of
+// the wave's next entry (wave-uniform); stores stop advancing at lim, so a
+// region needs 64 entries past lim, and a final at above lim means the row
+// overflowed.
+__device__ __forceinline__ void keep_word_lds(uint32_t x, uint32_t eidx, int32_t cs, uint32_t lim,
+                                              uint32_t dummy, uint32_t& at) {
+  const unsigned long long m = __ballot(max(lo16s(x), hi16s(x)) > cs);
+  // lane rank * 8 + the first free entry's address in one shift-add (left
+  // to itself the compiler adds first and shifts after the select)
+  uint32_t a;
+  asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(a) : "v"(mbcnt(m)), "s"(min(at, lim)));
+  lds_store2(pick(m, a, dummy), x, eidx);
+  asm("s_lshl3_add_u32 %0, %1, %2" : "=s"(at) : "s"(popc(m)), "s"(at));  // at += 8 * kept
+}
+
 // Block entries: signed key in the low half, the bottom key above it.
 __device__ __forceinline__ uint32_t block_entry(uint32_t key) { return key ^ kDeadPair; }
 
+// x clamped to [0, hi] (hi >= 0) in one vector op.
+__device__ __forceinline__ int32_t clamp0(int32_t x, int32_t hi) {
+  int32_t r;
+  asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "v"(hi));
+  return r;
+}
+// a = b + 4 * r in one vector op (b wave-uniform).
+__device__ __forceinline__ uint32_t shl2_add(uint32_t r, uint32_t b) {
+  uint32_t a;
+  asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(a) : "v"(r), "s"(b));
+  return a;
+}
+
+// Entry lists handed to the passes below are padded: the entries from cnt
+// up to the next multiple of 64 exist and hold dead pairs (both keys at
+// the bottom), so a pass reads whole 64-entry chunks with no bounds test.
+//
 // Output slots of the keys above a threshold Ts and of the keys equal to
 // it, from the entries at e: per 64 entries a wave takes its slots with one
 // 64-bit LDS atomic on `slot` (keys above in the low word, equal in the
-// high word).  Keys above take stage[slot], keys equal stage[cgt + slot]
-// while the slot is below `take`.  Block entries of -inf blocks stage -1.
+// high word).  Keys above take staging slot `slot`, keys equal slot
+// cgt + `slot` while that is below `take` (the slots are the words from LDS
+// byte address st on).  Block entries of -inf blocks stage -1.  Lanes with
+// nothing to write store to their own word at LDS byte address `dummy`
+// instead of leaving the store.
 template <int MODE, bool GT, bool EQ>
 __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32_t cgt,
-                             uint32_t take, int32_t* stage, unsigned long long* slot) {
+                             uint32_t take, uint32_t st, unsigned long long* slot,
+                             uint32_t dummy) {
   const int lane = __lane_id();
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
-    const uint32_t i = b0 + lane;
-    uint32_t x = kDeadPair, id = 0;
-    if (i < cnt) {
-      x = e[2 * i];
-      id = e[2 * i + 1];
-    }
-    const int32_t s0 = lo16s(x), s1 = hi16s(x);
+    const uint2 en = *reinterpret_cast<const uint2*>(e + 2 * (b0 + lane));
+    const int32_t s0 = lo16s(en.x), s1 = hi16s(en.x);
     const unsigned long long g0 = GT ? __ballot(s0 > Ts) : 0ull;
     const unsigned long long g1 = GT ? __ballot(s1 > Ts) : 0ull;
     const unsigned long long q0 = EQ ? __ballot(s0 == Ts) : 0ull;
     const unsigned long long q1 = EQ ? __ballot(s1 == Ts) : 0ull;
-    const uint32_t ng = popc(g0) + popc(g1), nq = popc(q0) + popc(q1);
-    if (ng + nq == 0) continue;
+    const uint32_t ng0 = popc(g0), nq0 = popc(q0);
+    const uint32_t ng = ng0 + popc(g1), nq = nq0 + popc(q1);
     unsigned long long base = 0;
     if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
     const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
-    int32_t v0 = (int32_t)id;
-    const int32_t v1 = (int32_t)id + 1;
+    int32_t v0 = (int32_t)en.y;
+    const int32_t v1 = (int32_t)en.y + 1;
     if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
-    if (GT && ng) {
-      if (in_mask(g0)) stage[bg + mbcnt(g0)] = v0;
-      if (in_mask(g1)) stage[bg + popc(g0) + mbcnt(g1)] = v1;
+    if (GT) {
+      lds_store(pick(g0, shl2_add(mbcnt(g0), st + 4u * bg), dummy), v0);
+      lds_store(pick(g1, shl2_add(mbcnt(g1), st + 4u * (bg + ng0)), dummy), v1);
     }
-    if (EQ && nq) {
-      const uint32_t p0 = bq + mbcnt(q0);
-      if (in_mask(q0) && p0 < take) stage[cgt + p0] = v0;
-      const uint32_t p1 = bq + popc(q0) + mbcnt(q1);
-      if (in_mask(q1) && p1 < take) stage[cgt + p1] = v1;
+    if (EQ && nq) {  // keys equal to Ts are few: most chunks skip this
+      const uint32_t p0 = mbcnt(q0, bq), p1 = mbcnt(q1, bq + nq0);
+      const uint32_t qb = st + 4u * cgt;
+      lds_store(pick(q0 & __ballot(p0 < take), shl2_add(p0, qb), dummy), v0);
+      lds_store(pick(q1 & __ballot(p1 < take), shl2_add(p1, qb), dummy), v1);
     }
   }
 }
@@ -693,25 +760,21 @@ enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
 // passed `cap` (checked after the histogram barrier), SEL_TIES when fewer
 // than k keys lie above cs (nothing written then), else SEL_DONE.
 template <int MODE, int NW>
-__device__ int select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t k,
-                                uint32_t* rel, uint32_t* sh, uint32_t* bc, int32_t* stage,
-                                uint32_t cap) {
+__device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, int32_t cs,
+                                uint32_t k, uint32_t* __restrict__ rel, uint32_t* sh,
+                                uint32_t* bc, uint32_t lds0, uint32_t cap) {
   const int lane = __lane_id();
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
+  // keys at or below cs (top - s >= kRelBins) count into the lane's own
+  // bin past the histogram, or into one of the 63 below it
+  const int32_t spill = kRelBins + lane;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
-    const uint32_t i = b0 + lane;
-    if (i < cnt) {
-      const uint32_t x = e[2 * i];
-      const int32_t s0 = lo16s(x), s1 = hi16s(x);
-      if (s0 > cs) atomicAdd(&rel[max(top - s0, 0)], 1u);
-      if (s1 > cs) atomicAdd(&rel[max(top - s1, 0)], 1u);
-    }
+    const uint32_t x = e[2 * (b0 + lane)];
+    atomicAdd(&rel[clamp0(top - lo16s(x), spill)], 1u);
+    atomicAdd(&rel[clamp0(top - hi16s(x), spill)], 1u);
   }
   __syncthreads();
-  bool ovf = false;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) ovf |= bc[BC_CNT + w] > cap;
-  if (ovf) return SEL_OVERFLOW;
+  if (__ballot(lane < NW && bc[BC_CNT + lane] > cap)) return SEL_OVERFLOW;
   uint32_t ri, above, total;
   find_desc16(rel, k, ri, above, total);
   if (total < k) return SEL_TIES;
@@ -753,8 +816,9 @@ __device__ int select_and_write(const uint32_t* e, uint32_t cnt, int32_t cs, uin
     cgt = a1 + a2;
     __syncthreads();  // every wave has read sh before the slots overwrite it
   }
-  emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt, stage,
-                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT));
+  emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt, lds0 + 4u * kStage,
+                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT),
+                                 lds0 + 4u * (kEmitDummy + lane));
   return SEL_DONE;
 }
 
@@ -830,10 +894,12 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 
 // ============================================ one workgroup per row
 // Rows whose valid vectors fit NT * VPT: the whole row sits in VGPRs.
+
 template <int MODE, int NT, int VPT>
 __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   constexpr int NW = NT / 64;
   extern __shared__ uint32_t smem[];
+  const uint32_t lds0 = lds_addr(smem);
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
@@ -863,14 +929,17 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     const int nvec = (v + 7) >> 3;
     const int jt = (nvec - 1) / NT;   // last vector slot holding row data
     const int rem = nvec - jt * NT;   // vectors in it
-    for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;  // sample + relative hists
-    for (int i = tid; i < 256 * kCopies; i += NT) lists[i] = 0; // replicated sample bins
+    // zero the sample and relative histograms and the replicated sample bins
+    const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int i = tid; i < (512 + kRelBins) / 4; i += NT) reinterpret_cast<uint4*>(sh)[i] = z4;
+#pragma unroll
+    for (int i = tid; i < 256 * kCopies / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
     if (tid == 0) {
       bc[BC_EQ] = 0;
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-
     // -- stage the row: 16-byte loads into VGPRs
     uint4 raw[VPT];
 #pragma unroll
@@ -902,13 +971,24 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
         kb[j] = vid >= 0 ? (vid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         s = vid >= 0 ? kb[j] : kNone;
       } else {
-        if (j == jt) poison_tail(raw[j], vid >= 0 ? clamp8(v - 8 * vid) : 0);
-        // sample: logit j mod 8 (that is, (vid / NT) mod 8) of the vector,
-        // logit 0 if that one is past the length
+        // sample: logit j mod 8 (that is, (vid / NT) mod 8) of the vector.
+        // Slots before jt hold whole vectors; in slot jt, with a length
+        // that is not a multiple of 8, the row's last vector is cut: its
+        // logits past the length become the bottom key, and its sample is
+        // logit 0 when logit j mod 8 is past the length.
         const int es = j & 7;
         const uint32_t se = key1(half_of(word_of(raw[j], es >> 1), es & 1));
-        const uint32_t s0 = key1(raw[j].x & 0xFFFFu);
-        s = vid >= 0 ? ((vid * 8 + es < v) ? se : s0) : kNone;
+        if (j < jt) {
+          s = se;
+        } else if (j == jt) {
+          if (v & 7) {
+            poison_tail(raw[j], vid >= 0 ? clamp8(v - 8 * vid) : 0);
+            const uint32_t s0 = key1(raw[j].x & 0xFFFFu);
+            s = vid >= 0 ? ((vid * 8 + es < v) ? se : s0) : kNone;
+          } else {
+            s = vid >= 0 ? se : kNone;
+          }
+        }
       }
       if (j % SE == 0) {
         sk[j / SE] = s;
@@ -922,7 +1002,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
     __syncthreads();  // histograms zeroed, block-table copy complete
-    const uint32_t c = sample_cutoff<NSK, NT>(sk, q, lists, sh);
+    const uint32_t c = sample_cutoff<NSK, NT>(sk, (jt + SE - 1) / SE, q, lists, sh);
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
       // a zero cutoff would make the zero keys of slots past the length ties
@@ -934,13 +1014,17 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       const uint32_t cap = (uint32_t)p.lcw;
       const uint32_t wbase = readfirst((uint32_t)wave) * (cap + kSpare);
       uint32_t* seg = lists + 2 * wbase;
-      uint32_t wcnt = 0, ecnt = 0;
+      // LDS byte addresses: the wave's next entry, its cap, the lane's dummy
+      const uint32_t first = lds0 + 4u * (kLists + 2u * wbase);
+      const uint32_t lim = first + cap * 8u;
+      uint32_t at = first;
+      const uint32_t dummy = lds0 + 4u * (kLists + 2u * (NW * (cap + kSpare) + lane));
       if constexpr (MODE == TOPK_MODE_BLOCK) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j)
           if (j <= jt)
-            keep_word<false>(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, lists,
-                             wbase, cap, wcnt, ecnt);
+            keep_word_lds(block_entry(kb[j]), (uint32_t)slot_vid<NT>(j, jt, rem), cs, lim, dummy,
+                          at);
       } else if (cs >= 0) {
         // non-negative cutoff: the raw words serve as signed keys
 #pragma unroll
@@ -949,8 +1033,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
             const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word<false>(word_of(raw[j], q2), e8 + 2 * q2, cs, lists, wbase, cap, wcnt,
-                               ecnt);
+              keep_word_lds(word_of(raw[j], q2), e8 + 2 * q2, cs, lim, dummy, at);
           }
         }
       } else {
@@ -960,16 +1043,18 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
             const uint32_t e8 = (uint32_t)slot_vid<NT>(j, jt, rem) * 8u;
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2)
-              keep_word<false>(skey2(word_of(raw[j], q2)), e8 + 2 * q2, cs, lists, wbase, cap,
-                               wcnt, ecnt);
+              keep_word_lds(skey2(word_of(raw[j], q2)), e8 + 2 * q2, cs, lim, dummy, at);
           }
         }
       }
+      const uint32_t wcnt = (at - first) / 8u;
       if (lane == 0) bc[BC_CNT + wave] = wcnt;
+      // dead entries after the wave's last (the passes read whole chunks)
+      lds_store2(min(at, lim) + 8u * lane, kDeadPair, 0u);
       // exact select over the survivors; its histogram barrier also publishes
       // the entry counts (overflow) and the count of keys above the cutoff
       const int st = select_and_write<MODE, NW>(seg, min(wcnt, cap), cs, (uint32_t)k, rel, sh,
-                                                bc, stage, cap);
+                                                bc, lds0, cap);
       if (st == SEL_OVERFLOW) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
@@ -996,7 +1081,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
           if (j <= jt) {
             const int vid = slot_vid<NT>(j, jt, rem);
             if constexpr (MODE == TOPK_MODE_BLOCK) {
-              keep_equal_slot(kb[j] == c, (uint32_t)vid, ties, (uint32_t)k, &bc[BC_EQ]);
+              keep_equal_slot(vid >= 0 && kb[j] == c, (uint32_t)vid, ties, (uint32_t)k,
+                              &bc[BC_EQ]);
             } else {
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
@@ -1026,6 +1112,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   }
   set_path(p, row, code);
 }
+
+
 
 // ============================================ team of workgroups per row
 // A row wider than one workgroup is split over member workgroups of fixed
@@ -1118,7 +1206,8 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     }
   }
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
-  const uint32_t c = sample_cutoff<NSK, NT>(sk, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
+  const uint32_t c =
+      sample_cutoff<NSK, NT>(sk, 0, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
   uint32_t* slice = p.team_slices + ((size_t)lrow * G + member) * kMemberWords;
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
     // a zero cutoff would make the zero keys of slots past the length ties:
@@ -1192,6 +1281,7 @@ template <int MODE>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
   extern __shared__ uint32_t smem[];
+  const uint32_t lds0 = lds_addr(smem);
   const int lrow = blockIdx.x;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
@@ -1306,7 +1396,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     } else if (gt_total + eq_total < (uint32_t)k) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
-    } else if (E + (sampled ? 0u : Et) > cap ||
+    } else if (E + 64u + (sampled ? 0u : Et + 64u) > cap ||
                (!sampled && avail < (uint32_t)k - gt_total)) {
       direct = true;
       code = TOPK_PATH_DIRECT_OVERFLOW;
@@ -1333,7 +1423,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         }
       }
       if (!sampled) {
-        uint32_t* tent = ent + 2 * E;
+        uint32_t* tent = ent + 2 * (E + 64);
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
           const int s2 = wave + u * NW;
@@ -1353,24 +1443,34 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
           }
         }
       }
+      // dead entries after the survivors and after the ties
+      if (tid < 64) {
+        *reinterpret_cast<uint2*>(ent + 2 * (E + tid)) = make_uint2(kDeadPair, 0u);
+        if (!sampled)
+          *reinterpret_cast<uint2*>(ent + 2 * (E + 64 + Et + tid)) = make_uint2(kDeadPair, 0u);
+      }
       __syncthreads();
-      const uint32_t share = (E + NW - 1) / NW;
+      // each wave takes whole 64-entry chunks: only the last share ends in
+      // the padding
+      const uint32_t share = ((E + 64 * NW - 1) / (64 * NW)) * 64;
       const uint32_t lo = min((uint32_t)wave * share, E);
       const uint32_t hi = min(lo + share, E);
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
+      const uint32_t dummy = lds0 + 4u * (kEmitDummy + lane);
       if (sampled) {
-        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, stage,
+        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, lds0,
                                    0xFFFFFFFFu);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key is the cutoff: every key above it, then the first ties
         const uint32_t take = (uint32_t)k - gt_total;
-        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take, stage, slot);
-        const uint32_t tshare = (Et + NW - 1) / NW;
+        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take,
+                                        lds0 + 4u * kStage, slot, dummy);
+        const uint32_t tshare = ((Et + 64 * NW - 1) / (64 * NW)) * 64;
         const uint32_t tlo = min((uint32_t)wave * tshare, Et);
         const uint32_t thi = min(tlo + tshare, Et);
-        emit_entries<MODE, false, true>(ent + 2 * (E + tlo), thi - tlo, cs, gt_total, take,
-                                        stage, slot);
+        emit_entries<MODE, false, true>(ent + 2 * (E + 64 + tlo), thi - tlo, cs, gt_total, take,
+                                        lds0 + 4u * kStage, slot, dummy);
         code = TOPK_PATH_SAMPLED_TIES;
       }
       __syncthreads();
@@ -1439,7 +1539,7 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
 int row_lcw(int k, int nw) { return (k + k / 4 + 512) / nw + 32; }
 
 size_t row_lds_bytes(int lcw, int nw) {
-  const int lists = nw * (lcw + kSpare) * 2;
+  const int lists = nw * (lcw + kSpare) * 2 + 2 * 64;  // regions, then the dummy area
   return (size_t)(kLists + (lists > kDirectWords ? lists : kDirectWords)) * 4;
 }
 
