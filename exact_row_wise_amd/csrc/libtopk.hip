@@ -58,6 +58,8 @@
 namespace {
 
 constexpr int kCopies = 8;               // replicated bins of whole-row histograms
+constexpr int kCopyStride = 260;         // words between the copies of a replicated sample bin
+constexpr int kSampBins = kCopies * kCopyStride;  // words of the replicated sample bins
 constexpr int kTeamNT = 256;             // filter workgroup size
 constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
@@ -604,11 +606,12 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t
 // (decode_topk_cute, radix_select over the samples).  The high-byte pass
 // counts into kCopies replicated bins (lane mod 8) at h8 (256 kCopies
 // words, zeroed), since sampled keys of smooth data crowd a few high bytes
-// and same-word LDS atomics serialize; 256 threads then sum the copies into
-// h8 + 256 kCopies (256 words).  The low-byte pass counts into sh (256
-// words, zeroed; a sample outside the chosen high byte counts into the
-// lane's own word of sh[256, 320) instead).  Every wave finds the bins
-// itself.
+// and same-word LDS atomics serialize (copy c of bin b at word
+// c kCopyStride + b: the copies of a bin lie in distinct banks); 256
+// threads then sum the copies into h8 + kSampBins (256 words).  The
+// low-byte pass counts into sh (256 words, zeroed;
+// a sample outside the chosen high byte counts into the lane's own word of
+// sh[256, 320) instead).  Every wave finds the bins itself.
 template <int NSK, int NT>
 __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
                                   uint32_t* sh) {
@@ -616,14 +619,15 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
   const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
   for (int i = 0; i < NSK; ++i) {
-    if (i < lead || sk[i] != kNone) atomicAdd(&h8[(255u - (sk[i] >> 8)) * kCopies + copy], 1u);
+    if (i < lead || sk[i] != kNone) atomicAdd(&h8[copy * kCopyStride + 255u - (sk[i] >> 8)], 1u);
   }
   __syncthreads();
-  uint32_t* sums = h8 + 256 * kCopies;
+  uint32_t* sums = h8 + kSampBins;
   if (threadIdx.x < 256) {
-    const uint4 a = *reinterpret_cast<const uint4*>(h8 + threadIdx.x * kCopies);
-    const uint4 b = *reinterpret_cast<const uint4*>(h8 + threadIdx.x * kCopies + 4);
-    sums[threadIdx.x] = a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w;
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) t += h8[c * kCopyStride + threadIdx.x];
+    sums[threadIdx.x] = t;
   }
   __syncthreads();
   uint32_t i1, a1;
@@ -934,7 +938,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 #pragma unroll
     for (int i = tid; i < (512 + kRelBins) / 4; i += NT) reinterpret_cast<uint4*>(sh)[i] = z4;
 #pragma unroll
-    for (int i = tid; i < 256 * kCopies / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
+    for (int i = tid; i < kSampBins / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
     if (tid == 0) {
       bc[BC_EQ] = 0;
       bc[BC_SLOT] = 0;
@@ -1134,7 +1138,7 @@ template <int MODE, int VPT, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
   __shared__ __align__(16) uint32_t sh[512];
-  __shared__ __align__(16) uint32_t h8[256 * kCopies + 256];
+  __shared__ __align__(16) uint32_t h8[kSampBins + 256];
   __shared__ uint32_t bc[128];
   const int G = p.G;
   const int b = blockIdx.x, xg = b & 7, yg = b >> 3;
@@ -1157,7 +1161,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const int jt = (ve - vb - 1) / NT;   // last occupied slot
   const int rem = (ve - vb) - jt * NT; // vectors in it
   for (int i = tid; i < 512; i += NT) sh[i] = 0;
-  for (int i = tid; i < 256 * kCopies; i += NT) h8[i] = 0;
+  for (int i = tid; i < kSampBins; i += NT) h8[i] = 0;
 
   // -- sample loads, then chunk loads.  The samples are the same in every
   // member of the row: every vector of a short row; otherwise SV * NT / 8
@@ -1554,12 +1558,28 @@ int device_lds_limit(int dev) {
   return v;
 }
 
+// Raise a kernel's dynamic LDS limit to `lds` bytes once per device (not at
+// every call, so that calls also work under stream capture).
+int allow_lds(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, size_t> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> g(mu);
+  size_t& have = done[{dev, kernel}];
+  if (have >= lds) return TOPK_OK;
+  const hipError_t e =
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return fail(TOPK_ERR_HIP, "LDS of %zu bytes: %s", lds, hipGetErrorString(e));
+  have = lds;
+  return TOPK_OK;
+}
+
 template <class K>
 int launch(K kernel, int grid, int nt, size_t lds, hipStream_t stream, const Params& p) {
   if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return fail(TOPK_ERR_HIP, "LDS of %zu bytes: %s", lds, hipGetErrorString(e));
+    const int rc = allow_lds(reinterpret_cast<const void*>(kernel), lds);
+    if (rc != TOPK_OK) return rc;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(nt), lds, stream, p);
   const hipError_t e = hipGetLastError();
