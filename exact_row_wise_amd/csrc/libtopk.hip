@@ -20,9 +20,10 @@
 //     count, no atomic).  Survivor words hold signed keys (key - 0x8000 in
 //     each half); when c is the key of a non-negative value the raw word
 //     already serves, so the key transform never touches the whole row;
-//   * the exact k-th key T over the survivors takes one pass of a
-//     1024-bin LDS histogram of (key - c), which gives T itself whenever
-//     T - c <= 1024 (else two 8-bit passes); the write pass takes slots
+//   * the exact k-th key T over the survivors takes one pass of a 256-bin
+//     LDS histogram of (key - c), kept in 4 copies (lane mod 4) so that the
+//     many equal keys near c seldom meet on one word, which gives T itself
+//     whenever T - c < 256 (else two 8-bit passes); the write pass takes slots
 //     from one LDS counter pair, one atomic per wave and 64 entries, into
 //     a k-slot LDS staging row that one coalesced pass then copies out,
 //     applying the block table;
@@ -74,7 +75,10 @@ constexpr int kSpare = 64;               // region entries past the cap (one bal
 constexpr int kTieLCW = TOPK_MAX_K / 4 + 128;     // tie entries per wave region of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
 constexpr size_t kTeamScratchMax = size_t(256) << 20;
-constexpr int kRelBins = 1024;           // histogram bins of (key - cutoff): 16 per lane
+constexpr int kRelBins = 256;            // histogram bins of (key - cutoff): 4 per lane
+constexpr int kRelCopies = 4;            // copies of those bins (lane mod 4)
+constexpr int kRelStride = 276;          // words per copy: the bins, then per-lane spill words
+constexpr int kRelWords = kRelCopies * kRelStride;
 constexpr int kSelectMin = 6144;         // staged survivor entries with 64 KB of LDS
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
@@ -91,9 +95,11 @@ constexpr int kBc = 0;                          // 128 words of counters and per
 constexpr int kEmitDummy = 128;                 // 64 words: one per lane for stores that drop
 constexpr int kStage = 192;                     // k output slots, overlapping:
 constexpr int kSampHist = kStage;               //   256 low-byte sample bins / 2 x 256 bins
-constexpr int kRelHist = kStage + 512;          //   kRelBins bins + 64 spill bins / u16 ties
+constexpr int kRelHist = kStage + 512;          //   kRelWords of relative bins / u16 ties
 constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
-static_assert(kRelHist + kRelBins + 64 <= kLists, "histograms overlap the lists");
+static_assert(kRelHist + kRelWords <= kLists, "histograms overlap the lists");
+static_assert(kRelBins + 16 <= kRelStride && (kRelStride * 4) % 16 == 0, "relative bin copies");
+static_assert(2 * kRelWords >= TOPK_MAX_K, "the u16 tie list fits the relative bins");
 enum {
   BC_CNT = 0,     // 16: entries per wave
   BC_ECNT = 16,   // 16: survivor keys per wave
@@ -332,51 +338,41 @@ __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, u
   above = acc;
 }
 
-// One wave over a 1024-bin histogram (16-byte aligned), index 0 holding
-// the largest keys: as find_desc with 16 bins a lane; the lane's group of
-// 4 bins, then the bin, are found with scalar code.  `total` is the
-// histogram's sum; bin and above are meaningful when need <= total.
-__device__ __forceinline__ void find_desc16(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                            uint32_t& above, uint32_t& total) {
+// One wave over the kRelCopies copies of a 256-bin histogram (copy c at
+// hist + c kRelStride, 16-byte aligned), index 0 holding the largest keys:
+// as find_desc over the summed copies, with `total` the count of all bins.
+__device__ __forceinline__ void find_rel(const uint32_t* hist, uint32_t need, uint32_t& bin,
+                                         uint32_t& above, uint32_t& total) {
   const int lane = __lane_id();
-  const uint4* h = reinterpret_cast<const uint4*>(hist + lane * 16);
-  const uint4 a = h[0], b = h[1], c = h[2], d = h[3];
-  const uint32_t g0 = a.x + a.y + a.z + a.w, g1 = b.x + b.y + b.z + b.w;
-  const uint32_t g2 = c.x + c.y + c.z + c.w, g3 = d.x + d.y + d.z + d.w;
-  const uint32_t s = g0 + g1 + g2 + g3;
+  uint4 h = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int c = 0; c < kRelCopies; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(hist + c * kRelStride + lane * 4);
+    h.x += u.x;
+    h.y += u.y;
+    h.z += u.z;
+    h.w += u.w;
+  }
+  const uint32_t s = h.x + h.y + h.z + h.w;
   const uint32_t incl = wave_incl_scan(s);
   total = readlane(incl, 63);
   const unsigned long long m = __ballot(incl >= need);
   const int L = m ? (__ffsll(m) - 1) : 63;
   uint32_t acc = readlane(incl - s, L);
-  const uint32_t s0 = readlane(g0, L), s1 = readlane(g1, L), s2 = readlane(g2, L);
-  uint32_t grp = 3;
-  if (acc + s0 >= need) {
-    grp = 0;
-  } else if (acc + s0 + s1 >= need) {
-    grp = 1;
-    acc += s0;
-  } else if (acc + s0 + s1 + s2 >= need) {
-    grp = 2;
-    acc += s0 + s1;
-  } else {
-    acc += s0 + s1 + s2;
-  }
-  const uint4 e = *reinterpret_cast<const uint4*>(hist + L * 16 + grp * 4);
-  const uint32_t e0 = readfirst(e.x), e1 = readfirst(e.y), e2 = readfirst(e.z);
+  const uint32_t h0 = readlane(h.x, L), h1 = readlane(h.y, L), h2 = readlane(h.z, L);
   uint32_t pos = 3;
-  if (acc + e0 >= need) {
+  if (acc + h0 >= need) {
     pos = 0;
-  } else if (acc + e0 + e1 >= need) {
+  } else if (acc + h0 + h1 >= need) {
     pos = 1;
-    acc += e0;
-  } else if (acc + e0 + e1 + e2 >= need) {
+    acc += h0;
+  } else if (acc + h0 + h1 + h2 >= need) {
     pos = 2;
-    acc += e0 + e1;
+    acc += h0 + h1;
   } else {
-    acc += e0 + e1 + e2;
+    acc += h0 + h1 + h2;
   }
-  bin = (uint32_t)L * 16u + grp * 4u + pos;
+  bin = (uint32_t)L * 4u + pos;
   above = acc;
 }
 
@@ -755,9 +751,12 @@ enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
 
 // Exact k-th key T over the survivor entries spread over the waves, then
 // the write into the k staged slots.  Wave w sees `cnt` entries at e; `rel`
-// is a zeroed kRelBins histogram, `sh` 512 free words, bc[BC_SLOT..+1]
-// zero.  The bins of (key - cs - 1), largest first, give T exactly unless
-// T > cs + kRelBins (then two 8-bit passes over the keys above that).  The
+// is kRelWords zeroed words (kRelCopies copies of a kRelBins histogram,
+// the copy chosen by lane mod 4 so that lanes with equal keys rarely hit
+// one word, each copy followed by the spill words of its lanes), `sh` 512
+// free words, bc[BC_SLOT..+1] zero.  The bins of (key - cs - 1), largest
+// first, give T exactly unless T >= cs + kRelBins (then two 8-bit passes
+// over the keys above that).  The
 // keys above T take the slots [0, cgt) and the first keys equal to T the
 // slots [cgt, k).  rel and sh overlap the staging slots.
 // Returns SEL_OVERFLOW when a wave's published entry count bc[BC_CNT + w]
@@ -770,17 +769,18 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
   const int lane = __lane_id();
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   // keys at or below cs (top - s >= kRelBins) count into the lane's own
-  // bin past the histogram, or into one of the 63 below it
-  const int32_t spill = kRelBins + lane;
+  // spill word after its copy's bins, or into one of the 15 below it
+  uint32_t* const relc = rel + (lane & (kRelCopies - 1)) * kRelStride;
+  const int32_t spill = kRelBins + (lane >> 2);
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t x = e[2 * (b0 + lane)];
-    atomicAdd(&rel[clamp0(top - lo16s(x), spill)], 1u);
-    atomicAdd(&rel[clamp0(top - hi16s(x), spill)], 1u);
+    atomicAdd(&relc[clamp0(top - lo16s(x), spill)], 1u);
+    atomicAdd(&relc[clamp0(top - hi16s(x), spill)], 1u);
   }
   __syncthreads();
   if (__ballot(lane < NW && bc[BC_CNT + lane] > cap)) return SEL_OVERFLOW;
   uint32_t ri, above, total;
-  find_desc16(rel, k, ri, above, total);
+  find_rel(rel, k, ri, above, total);
   if (total < k) return SEL_TIES;
   int32_t Ts;
   uint32_t cgt;
@@ -936,7 +936,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     // zero the sample and relative histograms and the replicated sample bins
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int i = tid; i < (512 + kRelBins) / 4; i += NT) reinterpret_cast<uint4*>(sh)[i] = z4;
+    for (int i = tid; i < (512 + kRelWords) / 4; i += NT) reinterpret_cast<uint4*>(sh)[i] = z4;
 #pragma unroll
     for (int i = tid; i < kSampBins / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
     if (tid == 0) {
@@ -1079,7 +1079,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
           gt_total += ew;
         }
         // the k-th key can only be the cutoff: collect keys equal to it
-        uint16_t* ties = reinterpret_cast<uint16_t*>(rel);  // room for 2 kRelBins >= k
+        uint16_t* ties = reinterpret_cast<uint16_t*>(rel);  // room for 2 kRelWords >= k
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
           if (j <= jt) {
@@ -1325,7 +1325,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     // chunk starts in element units: 8 logits per vector, one block per vector
     const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
     const int nseg = 4 * gr;  // <= 4 kMaxMembers <= NT: one segment per thread
-    for (int i = tid; i < 512 + kRelBins; i += NT) sh[i] = 0;
+    for (int i = tid; i < 512 + kRelWords; i += NT) sh[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
