@@ -79,6 +79,7 @@ constexpr int kRelBins = 256;            // histogram bins of (key - cutoff): 4 
 constexpr int kRelCopies = 4;            // copies of those bins (lane mod 4)
 constexpr int kRelStride = 276;          // words per copy: the bins, then per-lane spill words
 constexpr int kRelWords = kRelCopies * kRelStride;
+constexpr int kRowLoCopies = 2;           // copies of the low-byte sample bins, one-workgroup kernel
 constexpr int kSelectMin = 6144;         // staged survivor entries with 64 KB of LDS
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
@@ -94,8 +95,10 @@ constexpr uint32_t kDeadPair = 0x80008000u;  // two signed keys at the very bott
 constexpr int kBc = 0;                          // 128 words of counters and per-wave fields
 constexpr int kEmitDummy = 128;                 // 64 words: one per lane for stores that drop
 constexpr int kStage = 192;                     // k output slots, overlapping:
-constexpr int kSampHist = kStage;               //   256 low-byte sample bins / 2 x 256 bins
-constexpr int kRelHist = kStage + 512;          //   kRelWords of relative bins / u16 ties
+constexpr int kSampHist = kStage;               //   low-byte sample bins / 2 x 256 fallback bins
+constexpr int kRelHist = kStage + 552;          //   kRelWords of relative bins / u16 ties
+static_assert(kRowLoCopies * kRelStride <= kRelHist - kSampHist && kRelHist - kSampHist >= 512,
+              "low-byte sample bins, fallback bins");
 constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
 static_assert(kRelHist + kRelWords <= kLists, "histograms overlap the lists");
 static_assert(kRelBins + 16 <= kRelStride && (kRelStride * 4) % 16 == 0, "relative bin copies");
@@ -338,16 +341,17 @@ __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, u
   above = acc;
 }
 
-// One wave over the kRelCopies copies of a 256-bin histogram (copy c at
-// hist + c kRelStride, 16-byte aligned), index 0 holding the largest keys:
-// as find_desc over the summed copies, with `total` the count of all bins.
-__device__ __forceinline__ void find_rel(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                         uint32_t& above, uint32_t& total) {
+// One wave over C copies of a 256-bin histogram (copy c at hist + c STRIDE,
+// 16-byte aligned), index 0 holding the largest keys: as find_desc over the
+// summed copies, with `total` the count of all bins.
+template <int C, int STRIDE>
+__device__ __forceinline__ void find_copies(const uint32_t* hist, uint32_t need, uint32_t& bin,
+                                            uint32_t& above, uint32_t& total) {
   const int lane = __lane_id();
   uint4 h = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-  for (int c = 0; c < kRelCopies; ++c) {
-    const uint4 u = *reinterpret_cast<const uint4*>(hist + c * kRelStride + lane * 4);
+  for (int c = 0; c < C; ++c) {
+    const uint4 u = *reinterpret_cast<const uint4*>(hist + c * STRIDE + lane * 4);
     h.x += u.x;
     h.y += u.y;
     h.z += u.z;
@@ -604,13 +608,15 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t
 // words, zeroed), since sampled keys of smooth data crowd a few high bytes
 // and same-word LDS atomics serialize (copy c of bin b at word
 // c kCopyStride + b: the copies of a bin lie in distinct banks); 256
-// threads then sum the copies into h8 + kSampBins (256 words).  The
-// low-byte pass counts into sh (256 words, zeroed;
-// a sample outside the chosen high byte counts into the lane's own word of
-// sh[256, 320) instead).  Every wave finds the bins itself.
-template <int NSK, int NT>
+// threads then sum the copies into h8 + kSampBins (256 words; h8 holds
+// kSampBins + 256 words, zeroed but for the sums).  The low-byte pass
+// counts into LC copies (lane mod LC) at lo8, each kRelStride words, laid
+// out as the relative histogram (LC kRelStride words, zeroed; a sample
+// outside the chosen high byte counts into a spill word of its lane).
+// Every wave finds the bins itself.
+template <int NSK, int NT, int LC>
 __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
-                                  uint32_t* sh) {
+                                  uint32_t* lo8) {
   static_assert(NT >= 256, "one thread per high-byte bin");
   const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
@@ -629,15 +635,16 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
   uint32_t i1, a1;
   find_desc(sums, q, i1, a1);
   const uint32_t b1 = 255u - i1;
-  const uint32_t spill = 256u + __lane_id();
+  uint32_t* const loc = lo8 + (__lane_id() % LC) * kRelStride;
+  const uint32_t spill = 256u + ((__lane_id() / LC) & 15);
 #pragma unroll
   for (int i = 0; i < NSK; ++i) {
     const uint32_t x = sk[i];  // an empty slot's high byte is never b1
-    atomicAdd(&sh[pick(__ballot((x >> 8) == b1), 255u - (x & 255u), spill)], 1u);
+    atomicAdd(&loc[pick(__ballot((x >> 8) == b1), 255u - (x & 255u), spill)], 1u);
   }
   __syncthreads();
-  uint32_t i2, a2;
-  find_desc(sh, q - a1, i2, a2);
+  uint32_t i2, a2, t2;
+  find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2);
   return (b1 << 8) | (255u - i2);
 }
 
@@ -780,7 +787,7 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
   __syncthreads();
   if (__ballot(lane < NW && bc[BC_CNT + lane] > cap)) return SEL_OVERFLOW;
   uint32_t ri, above, total;
-  find_rel(rel, k, ri, above, total);
+  find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total);
   if (total < k) return SEL_TIES;
   int32_t Ts;
   uint32_t cgt;
@@ -936,7 +943,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     // zero the sample and relative histograms and the replicated sample bins
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-    for (int i = tid; i < (512 + kRelWords) / 4; i += NT) reinterpret_cast<uint4*>(sh)[i] = z4;
+    for (int i = tid; i < (kRelHist - kSampHist + kRelWords) / 4; i += NT)
+      reinterpret_cast<uint4*>(sh)[i] = z4;
 #pragma unroll
     for (int i = tid; i < kSampBins / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
     if (tid == 0) {
@@ -1006,7 +1014,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
     __syncthreads();  // histograms zeroed, block-table copy complete
-    const uint32_t c = sample_cutoff<NSK, NT>(sk, (jt + SE - 1) / SE, q, lists, sh);
+    const uint32_t c = sample_cutoff<NSK, NT, kRowLoCopies>(sk, (jt + SE - 1) / SE, q, lists, sh);
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
       // a zero cutoff would make the zero keys of slots past the length ties
@@ -1137,8 +1145,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 template <int MODE, int VPT, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
-  __shared__ __align__(16) uint32_t sh[512];
-  __shared__ __align__(16) uint32_t h8[kSampBins + 256];
+  __shared__ __align__(16) uint32_t h8[kSampBins + 256 + kRelWords];
   __shared__ uint32_t bc[128];
   const int G = p.G;
   const int b = blockIdx.x, xg = b & 7, yg = b >> 3;
@@ -1160,8 +1167,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const int ve = min(vb + NT * VPT, nvec);
   const int jt = (ve - vb - 1) / NT;   // last occupied slot
   const int rem = (ve - vb) - jt * NT; // vectors in it
-  for (int i = tid; i < 512; i += NT) sh[i] = 0;
-  for (int i = tid; i < kSampBins; i += NT) h8[i] = 0;
+  for (int i = tid; i < kSampBins + 256 + kRelWords; i += NT) h8[i] = 0;
 
   // -- sample loads, then chunk loads.  The samples are the same in every
   // member of the row: every vector of a short row; otherwise SV * NT / 8
@@ -1211,7 +1217,8 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   }
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
   const uint32_t c =
-      sample_cutoff<NSK, NT>(sk, 0, sample_rank((uint32_t)k, (uint32_t)n, S), h8, sh);
+      sample_cutoff<NSK, NT, kRelCopies>(sk, 0, sample_rank((uint32_t)k, (uint32_t)n, S), h8,
+                                         h8 + kSampBins + 256);
   uint32_t* slice = p.team_slices + ((size_t)lrow * G + member) * kMemberWords;
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
     // a zero cutoff would make the zero keys of slots past the length ties:
@@ -1325,7 +1332,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     // chunk starts in element units: 8 logits per vector, one block per vector
     const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
     const int nseg = 4 * gr;  // <= 4 kMaxMembers <= NT: one segment per thread
-    for (int i = tid; i < 512 + kRelWords; i += NT) sh[i] = 0;
+    for (int i = tid; i < kRelHist - kSampHist + kRelWords; i += NT) sh[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
@@ -1544,7 +1551,9 @@ int row_lcw(int k, int nw) { return (k + k / 4 + 512) / nw + 32; }
 
 size_t row_lds_bytes(int lcw, int nw) {
   const int lists = nw * (lcw + kSpare) * 2 + 2 * 64;  // regions, then the dummy area
-  return (size_t)(kLists + (lists > kDirectWords ? lists : kDirectWords)) * 4;
+  int words = lists > kDirectWords ? lists : kDirectWords;
+  if (words < kSampBins + 256) words = kSampBins + 256;  // the sample bins and their sums
+  return (size_t)(kLists + words) * 4;
 }
 
 // Dynamic LDS a workgroup may take on this device (cached per device).
