@@ -23,10 +23,10 @@
 //   * the exact k-th key T over the survivors takes one pass of a 256-bin
 //     LDS histogram of (key - c), kept in 4 copies (lane mod 4) so that the
 //     many equal keys near c seldom meet on one word, which gives T itself
-//     whenever T - c < 256 (else two 8-bit passes); the write pass takes slots
-//     from one LDS counter pair, one atomic per wave and 64 entries, into
-//     a k-slot LDS staging row that one coalesced pass then copies out,
-//     applying the block table;
+//     whenever T - c < 256 (else two 8-bit passes); the write pass takes
+//     output slots from one LDS counter pair, one atomic per wave and 64
+//     entries, and writes each index straight to the row's output through
+//     the block table (an LDS copy of the row's entries where it fits);
 //   * rows whose k-th key equals the cutoff take the tie pass: every key
 //     above c, then the first keys equal to c;
 //   * a misjudged sample (fewer than k keys at or above c) or a survivor
@@ -93,14 +93,13 @@ constexpr uint32_t kDeadPair = 0x80008000u;  // two signed keys at the very bott
 
 // LDS (32-bit words), shared by the one-workgroup and the select kernels
 constexpr int kBc = 0;                          // 128 words of counters and per-wave fields
-constexpr int kEmitDummy = 128;                 // 64 words: one per lane for stores that drop
-constexpr int kStage = 192;                     // k output slots, overlapping:
-constexpr int kSampHist = kStage;               //   low-byte sample bins / 2 x 256 fallback bins
-constexpr int kRelHist = kStage + 552;          //   kRelWords of relative bins / u16 ties
+constexpr int kHists = 128;                     // histograms:
+constexpr int kSampHist = kHists;               //   low-byte sample bins / 2 x 256 fallback bins
+constexpr int kRelHist = kHists + 552;          //   kRelWords of relative bins / u16 ties
 static_assert(kRowLoCopies * kRelStride <= kRelHist - kSampHist && kRelHist - kSampHist >= 512,
               "low-byte sample bins, fallback bins");
-constexpr int kLists = kStage + TOPK_MAX_K;     // survivor entries / direct path
-static_assert(kRelHist + kRelWords <= kLists, "histograms overlap the lists");
+constexpr int kLists = kRelHist + kRelWords;    // survivor entries / direct path
+static_assert(kLists % 4 == 0, "16-byte aligned lists");
 static_assert(kRelBins + 16 <= kRelStride && (kRelStride * 4) % 16 == 0, "relative bin copies");
 static_assert(2 * kRelWords >= TOPK_MAX_K, "the u16 tie list fits the relative bins");
 enum {
@@ -145,7 +144,6 @@ struct Params {
   int32_t* out;
   int32_t* path;
   int32_t force_direct;
-  int32_t out_vec;     // rows of out may be written as 16-byte vectors
   int32_t lcw;         // survivor entries per wave before the cap (one-workgroup kernel)
   int32_t page_lds;    // LDS word offset of a row's block-table copy (one-workgroup kernel), or 0
   // team path (rows wider than one workgroup), all in one scratch buffer:
@@ -263,11 +261,8 @@ __device__ __forceinline__ uint32_t pick(unsigned long long m, uint32_t a, uint3
   asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(m));
   return r;
 }
-// Stores at LDS byte address a (a plain 32-bit address, so that address
-// arithmetic stays in single vector ops): one word, or the pair (lo, hi).
-__device__ __forceinline__ void lds_store(uint32_t a, int32_t v) {
-  *reinterpret_cast<__attribute__((address_space(3))) int32_t*>(a) = v;
-}
+// Store of the pair (lo, hi) at LDS byte address a (a plain 32-bit
+// address, so that address arithmetic stays in single vector ops).
 __device__ __forceinline__ void lds_store2(uint32_t a, uint32_t lo, uint32_t hi) {
   *reinterpret_cast<__attribute__((address_space(3))) unsigned long long*>(a) =
       ((unsigned long long)hi << 32) | lo;
@@ -413,7 +408,6 @@ struct Out {
   int32_t shift;         // log2 of the page size
   uint32_t k;            // slots of the row (writes past them are dropped)
   bool block;
-  bool vec;              // out is 16-byte aligned and k a multiple of 4
 
   // An element index (or -1) as written: through the block table when
   // there is one (vLLM kimi_k3 indexer, IndexerSelect.emit), -1 kept.
@@ -438,33 +432,15 @@ __device__ __forceinline__ Out row_out(const Params& p, int row, bool block) {
   o.shift = p.page_shift;
   o.k = (uint32_t)p.k;
   o.block = block;
-  o.vec = p.out_vec != 0;
   return o;
 }
 
-// The k staged slots of a row to HBM in one coalesced pass (16-byte stores
-// where the row allows), through the block table: the row's copy in LDS
-// when `lpages` is given, else the table in global memory.  Follows a
-// barrier.
-template <int NT>
-__device__ void flush_out(const int32_t* stage, const Out o, const int32_t* lpages = nullptr) {
-  auto map = [&](int32_t x) -> int32_t {
-    if (!lpages) return o.map(x);
-    const int32_t i = x < 0 ? 0 : x;
-    return x < 0 ? -1 : (lpages[i >> o.shift] << o.shift) | (i & ((1 << o.shift) - 1));
-  };
-  if (o.vec) {
-    for (uint32_t e = threadIdx.x * 4u; e < o.k; e += NT * 4u) {
-      int4 v = *reinterpret_cast<const int4*>(stage + e);
-      v.x = map(v.x);
-      v.y = map(v.y);
-      v.z = map(v.z);
-      v.w = map(v.w);
-      *reinterpret_cast<int4*>(o.out + e) = v;
-    }
-  } else {
-    for (uint32_t e = threadIdx.x; e < o.k; e += NT) o.out[e] = map(stage[e]);
-  }
+// An element index (or -1) as written, through the block table: the row's
+// copy in LDS when `lpages` is given, else the table in global memory.
+__device__ __forceinline__ int32_t map_out(const Out& o, const int32_t* lpages, int32_t x) {
+  if (!lpages) return o.map(x);
+  const int32_t i = x < 0 ? 0 : x;
+  return x < 0 ? -1 : (lpages[i >> o.shift] << o.shift) | (i & ((1 << o.shift) - 1));
 }
 
 __device__ __forceinline__ void set_path(const Params& p, int row, int code) {
@@ -702,12 +678,6 @@ __device__ __forceinline__ int32_t clamp0(int32_t x, int32_t hi) {
   asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "v"(hi));
   return r;
 }
-// a = b + 4 * r in one vector op (b wave-uniform).
-__device__ __forceinline__ uint32_t shl2_add(uint32_t r, uint32_t b) {
-  uint32_t a;
-  asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(a) : "v"(r), "s"(b));
-  return a;
-}
 
 // Entry lists handed to the passes below are padded: the entries from cnt
 // up to the next multiple of 64 exist and hold dead pairs (both keys at
@@ -716,16 +686,16 @@ __device__ __forceinline__ uint32_t shl2_add(uint32_t r, uint32_t b) {
 // Output slots of the keys above a threshold Ts and of the keys equal to
 // it, from the entries at e: per 64 entries a wave takes its slots with one
 // 64-bit LDS atomic on `slot` (keys above in the low word, equal in the
-// high word).  Keys above take staging slot `slot`, keys equal slot
-// cgt + `slot` while that is below `take` (the slots are the words from LDS
-// byte address st on).  Block entries of -inf blocks stage -1.  Lanes with
-// nothing to write store to their own word at LDS byte address `dummy`
-// instead of leaving the store.
+// high word).  Keys above take output slot `slot`, keys equal slot
+// cgt + `slot` while that is below `take`; each is written straight to the
+// row's output (through the block table, `lpages` its LDS copy or null).
+// Block entries of -inf blocks write -1.
 template <int MODE, bool GT, bool EQ>
 __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32_t cgt,
-                             uint32_t take, uint32_t st, unsigned long long* slot,
-                             uint32_t dummy) {
+                             uint32_t take, unsigned long long* slot, const Out o,
+                             const int32_t* lpages) {
   const int lane = __lane_id();
+  int32_t* const out = o.out;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint2 en = *reinterpret_cast<const uint2*>(e + 2 * (b0 + lane));
     const int32_t s0 = lo16s(en.x), s1 = hi16s(en.x);
@@ -739,17 +709,20 @@ __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32
     if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
     const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
     int32_t v0 = (int32_t)en.y;
-    const int32_t v1 = (int32_t)en.y + 1;
+    int32_t v1 = (int32_t)en.y + 1;
     if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
+    if (o.pages) {
+      v0 = map_out(o, lpages, v0);
+      v1 = map_out(o, lpages, v1);
+    }
     if (GT) {
-      lds_store(pick(g0, shl2_add(mbcnt(g0), st + 4u * bg), dummy), v0);
-      lds_store(pick(g1, shl2_add(mbcnt(g1), st + 4u * (bg + ng0)), dummy), v1);
+      if (in_mask(g0)) out[bg + mbcnt(g0)] = v0;
+      if (in_mask(g1)) out[bg + ng0 + mbcnt(g1)] = v1;
     }
     if (EQ && nq) {  // keys equal to Ts are few: most chunks skip this
       const uint32_t p0 = mbcnt(q0, bq), p1 = mbcnt(q1, bq + nq0);
-      const uint32_t qb = st + 4u * cgt;
-      lds_store(pick(q0 & __ballot(p0 < take), shl2_add(p0, qb), dummy), v0);
-      lds_store(pick(q1 & __ballot(p1 < take), shl2_add(p1, qb), dummy), v1);
+      if (in_mask(q0) && p0 < take) out[cgt + p0] = v0;
+      if (in_mask(q1) && p1 < take) out[cgt + p1] = v1;
     }
   }
 }
@@ -757,7 +730,8 @@ __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32
 enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
 
 // Exact k-th key T over the survivor entries spread over the waves, then
-// the write into the k staged slots.  Wave w sees `cnt` entries at e; `rel`
+// the write of the row's k outputs (o, through the block table, `lpages`
+// its LDS copy or null).  Wave w sees `cnt` entries at e; `rel`
 // is kRelWords zeroed words (kRelCopies copies of a kRelBins histogram,
 // the copy chosen by lane mod 4 so that lanes with equal keys rarely hit
 // one word, each copy followed by the spill words of its lanes), `sh` 512
@@ -765,14 +739,15 @@ enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
 // first, give T exactly unless T >= cs + kRelBins (then two 8-bit passes
 // over the keys above that).  The
 // keys above T take the slots [0, cgt) and the first keys equal to T the
-// slots [cgt, k).  rel and sh overlap the staging slots.
+// slots [cgt, k).
 // Returns SEL_OVERFLOW when a wave's published entry count bc[BC_CNT + w]
 // passed `cap` (checked after the histogram barrier), SEL_TIES when fewer
 // than k keys lie above cs (nothing written then), else SEL_DONE.
 template <int MODE, int NW>
 __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, int32_t cs,
                                 uint32_t k, uint32_t* __restrict__ rel, uint32_t* sh,
-                                uint32_t* bc, uint32_t lds0, uint32_t cap) {
+                                uint32_t* bc, uint32_t cap, const Out o,
+                                const int32_t* lpages) {
   const int lane = __lane_id();
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   // keys at or below cs (top - s >= kRelBins) count into the lane's own
@@ -794,7 +769,6 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
   if (ri != 0) {
     Ts = top - (int32_t)ri;
     cgt = above;
-    __syncthreads();  // every wave has read rel before the slots overwrite it
   } else {
     // the k-th key lies at or above top: 8-bit passes over those keys
     for (int i = threadIdx.x; i < 512; i += 64 * NW) sh[i] = 0;
@@ -825,11 +799,9 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
     find_desc(sh + 256, k - a1, i2, a2);
     Ts = ((b1 << 8) | (255 - (int32_t)i2)) - 0x8000;
     cgt = a1 + a2;
-    __syncthreads();  // every wave has read sh before the slots overwrite it
   }
-  emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt, lds0 + 4u * kStage,
-                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT),
-                                 lds0 + 4u * (kEmitDummy + lane));
+  emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt,
+                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT), o, lpages);
   return SEL_DONE;
 }
 
@@ -924,7 +896,6 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
   uint32_t* lists = smem + kLists;
-  int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
   int32_t* lpages =
       (p.page_lds && o.pages) ? reinterpret_cast<int32_t*>(smem + p.page_lds) : nullptr;
 
@@ -1066,13 +1037,11 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       // exact select over the survivors; its histogram barrier also publishes
       // the entry counts (overflow) and the count of keys above the cutoff
       const int st = select_and_write<MODE, NW>(seg, min(wcnt, cap), cs, (uint32_t)k, rel, sh,
-                                                bc, lds0, cap);
+                                                bc, cap, o, lpages);
       if (st == SEL_OVERFLOW) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
       } else if (st == SEL_DONE) {
-        __syncthreads();
-        flush_out<NT>(stage, o, lpages);
         code = TOPK_PATH_SAMPLED;
       } else {
         // fewer than k keys above the cutoff: per-wave counts for the slots
@@ -1292,7 +1261,6 @@ template <int MODE>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
   extern __shared__ uint32_t smem[];
-  const uint32_t lds0 = lds_addr(smem);
   const int lrow = blockIdx.x;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
@@ -1312,7 +1280,6 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
-  int32_t* stage = reinterpret_cast<int32_t*>(smem + kStage);
   uint32_t* start = smem + kLists + kSelStart;
   uint32_t* tstart = smem + kLists + kSelTstart;
   uint32_t* segc = smem + kLists + kSelSegc;
@@ -1467,25 +1434,22 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       const uint32_t lo = min((uint32_t)wave * share, E);
       const uint32_t hi = min(lo + share, E);
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
-      const uint32_t dummy = lds0 + 4u * (kEmitDummy + lane);
       if (sampled) {
-        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc, lds0,
-                                   0xFFFFFFFFu);
+        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
+                                   0xFFFFFFFFu, o, nullptr);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key is the cutoff: every key above it, then the first ties
         const uint32_t take = (uint32_t)k - gt_total;
-        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take,
-                                        lds0 + 4u * kStage, slot, dummy);
+        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take, slot, o,
+                                        nullptr);
         const uint32_t tshare = ((Et + 64 * NW - 1) / (64 * NW)) * 64;
         const uint32_t tlo = min((uint32_t)wave * tshare, Et);
         const uint32_t thi = min(tlo + tshare, Et);
         emit_entries<MODE, false, true>(ent + 2 * (E + 64 + tlo), thi - tlo, cs, gt_total, take,
-                                        lds0 + 4u * kStage, slot, dummy);
+                                        slot, o, nullptr);
         code = TOPK_PATH_SAMPLED_TIES;
       }
-      __syncthreads();
-      flush_out<NT>(stage, o);
     }
   }
   if (direct) {
@@ -1638,7 +1602,6 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.out = out;
   p.path = opt ? opt->path_codes : nullptr;
   p.force_direct = opt ? (opt->force_direct != 0) : 0;
-  p.out_vec = (((uintptr_t)out & 15u) == 0 && (k & 3) == 0) ? 1 : 0;
 
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
