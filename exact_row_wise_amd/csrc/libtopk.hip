@@ -1271,12 +1271,6 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
   const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-  if (n <= k) {
-    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
-    else write_short_token<NT>(o, n, k);
-    set_path(p, row, TOPK_PATH_SHORT);
-    return;
-  }
   uint32_t* sh = smem + kSampHist;
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
@@ -1287,9 +1281,50 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   uint32_t* ent = smem + kLists + kSelStage;
   const int G = p.G;
   const uint32_t* slices = p.team_slices + (size_t)lrow * G * kMemberWords;
+  // -- everything the previous kernel left for this row, loaded at once
+  // without waiting for the row's length: the flags, the cutoff, every
+  // member's segment headers and the first 64 entries of segments wave,
+  // wave + NW, ... (segments of members past the row's end hold stale
+  // values and are masked once the length is known)
+  const int nseg_max = 4 * G;  // <= 4 kMaxMembers <= NT: one segment per thread
+  const uint32_t rflags = slices[H_FLAGS];
+  const uint32_t c = slices[H_CUT];
+  auto seg_src = [&](int s2) {
+    return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + (s2 & 3) * 2 * kTeamLCW;
+  };
+  auto tie_src = [&](int s2) {
+    return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
+           (s2 & 3) * 2 * kTieLCW;
+  };
+  constexpr int kPre = 8;
+  uint2 pre[kPre], tpre[kPre];  // survivor and tie entries
+#pragma unroll
+  for (int u = 0; u < kPre; ++u) {
+    const int s2 = wave + u * NW;
+    pre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
+                           : make_uint2(kDeadPair, 0u);
+    tpre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(tie_src(s2) + 2 * lane)
+                            : make_uint2(kDeadPair, 0u);
+  }
+  uint32_t hw[5] = {0u, 0u, 0u, 0u, 0u};  // the segment's header fields
+  if (tid < nseg_max) {
+    const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
+    const int w = tid & 3;
+    hw[0] = hdr[H_WCNT + w];
+    hw[1] = hdr[H_ECNT + w];
+    hw[2] = hdr[H_TW + w];
+    hw[3] = hdr[H_TKEPT + w];
+    hw[4] = hdr[H_NEQ + w];
+  }
+  if (n <= k) {
+    if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
+    else write_short_token<NT>(o, n, k);
+    set_path(p, row, TOPK_PATH_SHORT);
+    return;
+  }
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
-  if (!direct && (slices[H_FLAGS] & kFlagDirect)) {
+  if (!direct && (rflags & kFlagDirect)) {
     direct = true;
     code = TOPK_PATH_DIRECT_MISJUDGED;
   }
@@ -1298,43 +1333,24 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     const int gr = (nvec + p.team_cv - 1) / p.team_cv;  // members of this row
     // chunk starts in element units: 8 logits per vector, one block per vector
     const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
-    const int nseg = 4 * gr;  // <= 4 kMaxMembers <= NT: one segment per thread
+    const int nseg = 4 * gr;
     for (int i = tid; i < kRelHist - kSampHist + kRelWords; i += NT) sh[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-    auto seg_src = [&](int s2) {
-      return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + (s2 & 3) * 2 * kTeamLCW;
-    };
-    // the first 64 entries of segments wave, wave + NW, ... (up to kPre of
-    // them) are loaded with the headers, before their counts are known
-    auto tie_src = [&](int s2) {
-      return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
-             (s2 & 3) * 2 * kTieLCW;
-    };
-    constexpr int kPre = 8;
-    uint2 pre[kPre], tpre[kPre];  // the same for the tie entries
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      const int s2 = wave + u * NW;
-      pre[u] = s2 < nseg ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
-                         : make_uint2(kDeadPair, 0u);
-      tpre[u] = s2 < nseg ? *reinterpret_cast<const uint2*>(tie_src(s2) + 2 * lane)
-                          : make_uint2(kDeadPair, 0u);
+      if (wave + u * NW >= nseg) {
+        pre[u] = make_uint2(kDeadPair, 0u);
+        tpre[u] = make_uint2(kDeadPair, 0u);
+      }
     }
     // per segment (member, wave): entry counts, key counts, overflow
-    uint32_t wc = 0, ec = 0, tw = 0, tk = 0, nq = 0, bad = 0;
-    if (tid < nseg) {
-      const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
-      const int w = tid & 3;
-      wc = hdr[H_WCNT + w];
-      ec = hdr[H_ECNT + w];
-      tw = hdr[H_TW + w];
-      tk = hdr[H_TKEPT + w];
-      nq = hdr[H_NEQ + w];
-      bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
-    }
+    const bool mine = tid < nseg;
+    const uint32_t wc = mine ? hw[0] : 0u, ec = mine ? hw[1] : 0u, tw = mine ? hw[2] : 0u;
+    const uint32_t tk = mine ? hw[3] : 0u, nq = mine ? hw[4] : 0u;
+    const uint32_t bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
   const uint32_t iw = wave_incl_scan(wc), it = wave_incl_scan(tw);
     const uint32_t ie = wave_incl_scan(ec), ik = wave_incl_scan(tk), iq = wave_incl_scan(nq);
     const unsigned long long mb = __ballot(bad != 0);
@@ -1363,7 +1379,6 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       segc[tid] = wc;
       tsegc[tid] = tw;
     }
-    const uint32_t c = slices[H_CUT];
     const int32_t cs = (int32_t)c - 0x8000;
     __syncthreads();
     const uint32_t cap = (uint32_t)p.sel_cap;
