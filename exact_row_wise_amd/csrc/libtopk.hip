@@ -577,6 +577,15 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t
   return q < S ? q : S;
 }
 
+// Whether a cutoff with `above` of S samples strictly above it almost surely
+// has at least k of the row's n keys above it: `above` at least the
+// expected count at rank k plus 3 standard deviations and 3.
+__device__ __forceinline__ bool tie_unlikely(uint32_t k, uint32_t n, uint32_t S, uint32_t above) {
+  if (S >= n) return above >= k;  // every element sampled: exact
+  const float f0 = (float)(k * S) * __builtin_amdgcn_rcpf((float)n);
+  return (float)above >= f0 + 3.0f * __builtin_amdgcn_sqrtf(f0) + 3.0f;
+}
+
 // The q-th largest of the samples (kNone marks an empty slot; the first
 // `lead` samples are known not to be empty): two 8-bit radix passes
 // (decode_topk_cute, radix_select over the samples).  The high-byte pass
@@ -589,10 +598,11 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t k, uint32_t n, uint32_t
 // counts into LC copies (lane mod LC) at lo8, each kRelStride words, laid
 // out as the relative histogram (LC kRelStride words, zeroed; a sample
 // outside the chosen high byte counts into a spill word of its lane).
-// Every wave finds the bins itself.
+// Every wave finds the bins itself.  `above`, when given, receives the
+// number of samples strictly above the returned key.
 template <int NSK, int NT, int LC>
 __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
-                                  uint32_t* lo8) {
+                                  uint32_t* lo8, uint32_t* above = nullptr) {
   static_assert(NT >= 256, "one thread per high-byte bin");
   const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
@@ -621,6 +631,7 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
   __syncthreads();
   uint32_t i2, a2, t2;
   find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2);
+  if (above) *above = a1 + a2;  // samples strictly above the cutoff
   return (b1 << 8) | (255u - i2);
 }
 
@@ -1185,9 +1196,16 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     }
   }
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
+  uint32_t sa;
   const uint32_t c =
       sample_cutoff<NSK, NT, kRelCopies>(sk, 0, sample_rank((uint32_t)k, (uint32_t)n, S), h8,
-                                         h8 + kSampBins + 256);
+                                         h8 + kSampBins + 256, &sa);
+  // keys equal to the cutoff are only needed when fewer than k keys lie
+  // above it; when the samples above it exceed their expected count at
+  // rank k by 3 standard deviations that is a rare event, and the members
+  // skip collecting ties (a row that needs them after all finds no ties
+  // and takes the direct path, so exactness is kept)
+  const bool ties = !tie_unlikely((uint32_t)k, (uint32_t)n, S, sa);
   uint32_t* slice = p.team_slices + ((size_t)lrow * G + member) * kMemberWords;
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
     // a zero cutoff would make the zero keys of slots past the length ties:
@@ -1216,7 +1234,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
             lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         const uint32_t x = block_entry(key);
         keep_word<true>(x, (uint32_t)lvid, cs, seg, wbase, cap, wcnt, ecnt);
-        keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
+        if (ties) keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
       } else {
         if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
         const uint32_t e8 = (uint32_t)lvid * 8u;
@@ -1225,7 +1243,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
           const uint32_t w = word_of(raw[j], q2);
           const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
           keep_word<true>(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
-          keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
+          if (ties) keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
         }
       }
     }
@@ -1297,14 +1315,12 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
            (s2 & 3) * 2 * kTieLCW;
   };
   constexpr int kPre = 8;
-  uint2 pre[kPre], tpre[kPre];  // survivor and tie entries
+  uint2 pre[kPre];  // survivor entries
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
     const int s2 = wave + u * NW;
     pre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
                            : make_uint2(kDeadPair, 0u);
-    tpre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(tie_src(s2) + 2 * lane)
-                            : make_uint2(kDeadPair, 0u);
   }
   uint32_t hw[5] = {0u, 0u, 0u, 0u, 0u};  // the segment's header fields
   if (tid < nseg_max) {
@@ -1341,10 +1357,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     }
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-      if (wave + u * NW >= nseg) {
-        pre[u] = make_uint2(kDeadPair, 0u);
-        tpre[u] = make_uint2(kDeadPair, 0u);
-      }
+      if (wave + u * NW >= nseg) pre[u] = make_uint2(kDeadPair, 0u);
     }
     // per segment (member, wave): entry counts, key counts, overflow
     const bool mine = tid < nseg;
@@ -1417,20 +1430,10 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       }
       if (!sampled) {
         uint32_t* tent = ent + 2 * (E + 64);
-#pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          const int s2 = wave + u * NW;
-          if (s2 < nseg && (uint32_t)lane < tsegc[s2]) {
-            const uint32_t d = tstart[s2] + lane;
-            *reinterpret_cast<uint2*>(tent + 2 * d) =
-                make_uint2(tpre[u].x, tpre[u].y + (uint32_t)(s2 >> 2) * chunk);
-          }
-        }
         for (int s2 = wave; s2 < nseg; s2 += NW) {
-          const uint32_t from = s2 < kPre * NW ? 64u : 0u;
           const uint32_t* es = tie_src(s2);
           const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
-          for (uint32_t i = from + lane; i < tsegc[s2]; i += 64) {
+          for (uint32_t i = lane; i < tsegc[s2]; i += 64) {
             const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
             *reinterpret_cast<uint2*>(tent + 2 * (tstart[s2] + i)) = make_uint2(x.x, x.y + g);
           }

@@ -210,6 +210,49 @@ def test_crafted_overflow_row_takes_direct_path():
     assert np.all(pc == T.PATH_DIRECT_OVERFLOW), pc
 
 
+def _sampled_vectors_team(nvec, sv=1, nt=256):
+    """Vectors every member of a token team samples for a row of nvec
+    vectors (nvec > sv * nt): runs of 8 consecutive vectors, run r starting
+    at line floor((2 r + 1) lines / (2 runs)) in 32.32 fixed point."""
+    runs = sv * nt // 8
+    step = ((nvec >> 3) << 32) // (2 * runs)
+    si = np.arange(sv * nt)
+    return ((((2 * (si >> 3) + 1) * step) >> 32) << 3) + (si & 7)
+
+
+def test_team_skipped_ties_take_direct_path():
+    """A wide row of one value X, but for 20 sampled logits above it: the
+    samples above the cutoff (X) look plentiful, so the team does not collect
+    keys equal to X, yet fewer than k keys lie above X.  The row must fall
+    back to the direct path and stay exact."""
+    width, k = 150000, 512
+    L = np.full((2, width), 0x3F80, np.uint16)                    # 1.0
+    pos = (_sampled_vectors_team(width // 8) * 8)[:20]
+    L[:, pos] = (0x4000 + np.arange(20)).astype(np.uint16)         # 2.0 and up
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_DIRECT_MISJUDGED), pc
+
+
+def test_team_ties_collected_when_needed():
+    """A wide row of 0.5 with X = 1.0 at every 64th logit and 5 sampled logits
+    above X: the samples give no assurance that k keys lie above the cutoff
+    (X), so the team collects the keys equal to X and the row takes the tie
+    pass."""
+    width, k = 150000, 512
+    L = np.full((2, width), 0x3F00, np.uint16)                    # 0.5
+    L[:, ::64] = 0x3F80                                            # 1.0
+    pos = (_sampled_vectors_team(width // 8) * 8)[:5]
+    L[:, pos] = (0x4000 + np.arange(5)).astype(np.uint16)
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_SAMPLED_TIES), pc
+
+
 def test_team_scratch_reused_across_calls():
     """Consecutive team launches on one stream see clean scratch, also when
     a call has more rows than the one before it (regression: the control
