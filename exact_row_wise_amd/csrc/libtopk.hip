@@ -204,6 +204,12 @@ __device__ __forceinline__ uint32_t block_key4(uint4 v) {
   return (hi > (int32_t)kKeyPosInf - 0x8000 || lo < kSNegInf) ? kKeyNaN : (uint32_t)(hi + 0x8000);
 }
 
+// Vector i of a row (a 32-bit byte offset from the row's base: one scalar
+// base and one vector register per load)
+__device__ __forceinline__ uint4 ld_vec(const uint4* row, uint32_t i) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(row) + (i << 4));
+}
+
 __device__ __forceinline__ uint32_t half_of(uint32_t w, int h) {
   return h ? (w >> 16) : (w & 0xFFFFu);
 }
@@ -934,13 +940,13 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-    // -- stage the row: 16-byte loads into VGPRs
+    // -- stage the row: 16-byte loads into VGPRs.  Every lane loads (a lane
+    // without a vector in slot jt reads vector 0 and poisons it below; the
+    // slots past jt are never used), so that no load sits under a branch.
     uint4 raw[VPT];
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int vid = slot_vid<NT>(j, jt, rem);
-      raw[j] = vid >= 0 ? src[vid] : make_uint4(~0u, ~0u, ~0u, ~0u);
-    }
+    for (int j = 0; j < VPT; ++j)
+      raw[j] = ld_vec(src, (uint32_t)max(slot_vid<NT>(j, jt, rem), 0));
     // the row's block-table entries ride along, for an LDS copy
     constexpr int PPT = kPageLdsMax / NT;
     int32_t pgv[PPT];
@@ -975,8 +981,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
         if (j < jt) {
           s = se;
         } else if (j == jt) {
+          poison_tail(raw[j], vid >= 0 ? clamp8(v - 8 * vid) : 0);
           if (v & 7) {
-            poison_tail(raw[j], vid >= 0 ? clamp8(v - 8 * vid) : 0);
             const uint32_t s0 = key1(raw[j].x & 0xFFFFu);
             s = vid >= 0 ? ((vid * 8 + es < v) ? se : s0) : kNone;
           } else {
