@@ -105,13 +105,10 @@ static_assert(2 * kRelWords >= TOPK_MAX_K, "the u16 tie list fits the relative b
 enum {
   BC_CNT = 0,     // 16: entries per wave
   BC_ECNT = 16,   // 16: survivor keys per wave
-  BC_CGT = 32,    // 16: reductions
-  BC_CEQ = 48,    // 16: reductions
   BC_EQ = 64,     // tie-list counter
   BC_C1 = 65, BC_C2 = 66,   // direct-path write counters
   BC_SLOT = 68,   // 2 (8-byte aligned): output slots taken above T | equal to T
-  BC_X = 80,      // 16: reductions
-  BC_TMP = 96     // 32: reductions, bin searches
+  BC_TMP = 96     // 32: reductions, a team row's totals
 };
 
 // One team member's slice of global scratch (32-bit words), per wave w:
@@ -1320,6 +1317,19 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
            (s2 & 3) * 2 * kTieLCW;
   };
+  // the headers first (lane m of wave 0: member m's four segments), then
+  // the segment heads
+  static_assert(H_WCNT == 0 && H_ECNT == 4 && H_TW == 8 && H_TKEPT == 12 && H_NEQ == 16,
+                "header fields are four consecutive words each");
+  static_assert(kMaxMembers <= 64, "one lane of wave 0 per member");
+  uint4 hv[5];
+#pragma unroll
+  for (int f = 0; f < 5; ++f) hv[f] = make_uint4(0u, 0u, 0u, 0u);
+  if (wave == 0 && lane < G) {
+    const uint4* h4 = reinterpret_cast<const uint4*>(slices + (size_t)lane * kMemberWords);
+#pragma unroll
+    for (int f = 0; f < 5; ++f) hv[f] = h4[f];
+  }
   constexpr int kPre = 8;
   uint2 pre[kPre];  // survivor entries
 #pragma unroll
@@ -1327,16 +1337,6 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     const int s2 = wave + u * NW;
     pre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
                            : make_uint2(kDeadPair, 0u);
-  }
-  uint32_t hw[5] = {0u, 0u, 0u, 0u, 0u};  // the segment's header fields
-  if (tid < nseg_max) {
-    const uint32_t* hdr = slices + (size_t)(tid >> 2) * kMemberWords;
-    const int w = tid & 3;
-    hw[0] = hdr[H_WCNT + w];
-    hw[1] = hdr[H_ECNT + w];
-    hw[2] = hdr[H_TW + w];
-    hw[3] = hdr[H_TKEPT + w];
-    hw[4] = hdr[H_NEQ + w];
   }
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
@@ -1365,41 +1365,44 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     for (int u = 0; u < kPre; ++u) {
       if (wave + u * NW >= nseg) pre[u] = make_uint2(kDeadPair, 0u);
     }
-    // per segment (member, wave): entry counts, key counts, overflow
-    const bool mine = tid < nseg;
-    const uint32_t wc = mine ? hw[0] : 0u, ec = mine ? hw[1] : 0u, tw = mine ? hw[2] : 0u;
-    const uint32_t tk = mine ? hw[3] : 0u, nq = mine ? hw[4] : 0u;
-    const uint32_t bad = wc > (uint32_t)(kTeamLCW - kSpare) ? 1u : 0u;
-  const uint32_t iw = wave_incl_scan(wc), it = wave_incl_scan(tw);
-    const uint32_t ie = wave_incl_scan(ec), ik = wave_incl_scan(tk), iq = wave_incl_scan(nq);
-    const unsigned long long mb = __ballot(bad != 0);
-    if (lane == 63) {
-      bc[BC_TMP + wave] = iw;
-      bc[BC_TMP + 16 + wave] = it;
-      bc[BC_X + wave] = ie;
-      bc[BC_CGT + wave] = ik;
-      bc[BC_CEQ + wave] = iq;
+    // per segment (member, wave): entry counts, key counts, overflow.  Wave
+    // 0 alone sums them (lane m: member m) and publishes the segment starts
+    // and the row's totals; the other waves wait at the barrier.
+    if (wave == 0) {
+      const bool live = lane < gr;
+      const uint4 wc = live ? hv[0] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 tw = live ? hv[2] : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t ec = live ? hv[1].x + hv[1].y + hv[1].z + hv[1].w : 0u;
+      const uint32_t tk = live ? hv[3].x + hv[3].y + hv[3].z + hv[3].w : 0u;
+      const uint32_t nq = live ? hv[4].x + hv[4].y + hv[4].z + hv[4].w : 0u;
+      const uint32_t wsum = wc.x + wc.y + wc.z + wc.w, tsum = tw.x + tw.y + tw.z + tw.w;
+      constexpr uint32_t kCapW = (uint32_t)(kTeamLCW - kSpare);
+      const bool bad = max(max(wc.x, wc.y), max(wc.z, wc.w)) > kCapW;
+      const uint32_t iw = wave_incl_scan(wsum), it = wave_incl_scan(tsum);
+      const uint32_t ie = wave_incl_scan(ec), ik = wave_incl_scan(tk), iq = wave_incl_scan(nq);
+      const unsigned long long mb = __ballot(bad);
+      if (live) {
+        const uint32_t s0 = iw - wsum, t0 = it - tsum;
+        reinterpret_cast<uint4*>(start)[lane] =
+            make_uint4(s0, s0 + wc.x, s0 + wc.x + wc.y, s0 + wc.x + wc.y + wc.z);
+        reinterpret_cast<uint4*>(tstart)[lane] =
+            make_uint4(t0, t0 + tw.x, t0 + tw.x + tw.y, t0 + tw.x + tw.y + tw.z);
+        reinterpret_cast<uint4*>(segc)[lane] = wc;
+        reinterpret_cast<uint4*>(tsegc)[lane] = tw;
+      }
+      if (lane == 63) {
+        bc[BC_TMP + 0] = iw;
+        bc[BC_TMP + 1] = it;
+        bc[BC_TMP + 2] = ie;
+        bc[BC_TMP + 3] = ik;
+        bc[BC_TMP + 4] = iq;
+        bc[BC_TMP + 5] = mb ? 1u : 0u;
+      }
     }
-    if (lane == 0) bc[BC_CNT + wave] = mb ? 1u : 0u;
     __syncthreads();
-    // lane w < NW holds wave w's sums; scans across those lanes
-    const bool lw = lane < NW;
-    const uint32_t aw = lw ? bc[BC_TMP + lane] : 0u, at = lw ? bc[BC_TMP + 16 + lane] : 0u;
-    const uint32_t sw_ = wave_incl_scan(aw), st_ = wave_incl_scan(at);
-    const uint32_t ow = readlane(sw_ - aw, wave), ot = readlane(st_ - at, wave);
-    const uint32_t E = readlane(sw_, 63), Et = readlane(st_, 63);
-    const uint32_t gt_total = readlane(wave_incl_scan(lw ? bc[BC_X + lane] : 0u), 63);
-    const uint32_t avail = readlane(wave_incl_scan(lw ? bc[BC_CGT + lane] : 0u), 63);
-    const uint32_t eq_total = readlane(wave_incl_scan(lw ? bc[BC_CEQ + lane] : 0u), 63);
-    const uint32_t flags = __ballot(lw && bc[BC_CNT + lane] != 0u) ? 1u : 0u;
-    if (tid < nseg) {
-      start[tid] = ow + iw - wc;
-      tstart[tid] = ot + it - tw;
-      segc[tid] = wc;
-      tsegc[tid] = tw;
-    }
+    const uint32_t E = bc[BC_TMP + 0], Et = bc[BC_TMP + 1], gt_total = bc[BC_TMP + 2];
+    const uint32_t avail = bc[BC_TMP + 3], eq_total = bc[BC_TMP + 4], flags = bc[BC_TMP + 5];
     const int32_t cs = (int32_t)c - 0x8000;
-    __syncthreads();
     const uint32_t cap = (uint32_t)p.sel_cap;
     const bool sampled = gt_total >= (uint32_t)k;
     if (flags & 1u) {
