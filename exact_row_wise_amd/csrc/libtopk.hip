@@ -1330,7 +1330,13 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
 #pragma unroll
     for (int f = 0; f < 5; ++f) hv[f] = h4[f];
   }
-  constexpr int kPre = 8;
+  // heads of segments wave, wave + NW, ...: enough for every segment of a
+  // block row up to 2^20 logits (43 members), 8 for token rows
+  constexpr int kPre = MODE == TOPK_MODE_BLOCK ? 11 : 8;
+  static_assert(MODE == TOPK_MODE_TOKEN ||
+                    kPre * NW >= 4 * ((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) /
+                                      (kTeamNT * kTeamBlockVPT)),
+                "one preloaded head per segment of the widest block row");
   uint2 pre[kPre];  // survivor entries
 #pragma unroll
   for (int u = 0; u < kPre; ++u) {
