@@ -344,7 +344,8 @@ __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, u
 // summed copies, with `total` the count of all bins.
 template <int C, int STRIDE>
 __device__ __forceinline__ void find_copies(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                            uint32_t& above, uint32_t& total) {
+                                            uint32_t& above, uint32_t& total,
+                                            uint32_t* count = nullptr) {
   const int lane = __lane_id();
   uint4 h = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
@@ -376,6 +377,7 @@ __device__ __forceinline__ void find_copies(const uint32_t* hist, uint32_t need,
   }
   bin = (uint32_t)L * 4u + pos;
   above = acc;
+  if (count) *count = pos == 0 ? h0 : (pos == 1 ? h1 : (pos == 2 ? h2 : readlane(h.w, L)));
 }
 
 // Sum over the workgroup (every thread gets the total).
@@ -601,11 +603,13 @@ __device__ __forceinline__ bool tie_unlikely(uint32_t k, uint32_t n, uint32_t S,
 // counts into LC copies (lane mod LC) at lo8, each kRelStride words, laid
 // out as the relative histogram (LC kRelStride words, zeroed; a sample
 // outside the chosen high byte counts into a spill word of its lane).
-// Every wave finds the bins itself.  `above`, when given, receives the
-// number of samples strictly above the returned key.
+// Every wave finds the bins itself.  `above` and `equal`, when given,
+// receive the numbers of samples strictly above and equal to the returned
+// key.
 template <int NSK, int NT, int LC>
 __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
-                                  uint32_t* lo8, uint32_t* above = nullptr) {
+                                  uint32_t* lo8, uint32_t* above = nullptr,
+                                  uint32_t* equal = nullptr) {
   static_assert(NT >= 256, "one thread per high-byte bin");
   const uint32_t copy = __lane_id() & (kCopies - 1);
 #pragma unroll
@@ -633,7 +637,7 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
   }
   __syncthreads();
   uint32_t i2, a2, t2;
-  find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2);
+  find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2, equal);  // equal: samples at the cutoff
   if (above) *above = a1 + a2;  // samples strictly above the cutoff
   return (b1 << 8) | (255u - i2);
 }
@@ -1199,16 +1203,31 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     }
   }
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
-  uint32_t sa;
-  const uint32_t c =
+  uint32_t sa, se;
+  uint32_t c =
       sample_cutoff<NSK, NT, kRelCopies>(sk, 0, sample_rank((uint32_t)k, (uint32_t)n, S), h8,
-                                         h8 + kSampBins + 256, &sa);
+                                         h8 + kSampBins + 256, &sa, &se);
   // keys equal to the cutoff are only needed when fewer than k keys lie
   // above it; when the samples above it exceed their expected count at
   // rank k by 3 standard deviations that is a rare event, and the members
   // skip collecting ties (a row that needs them after all finds no ties
   // and takes the direct path, so exactness is kept)
-  const bool ties = !tie_unlikely((uint32_t)k, (uint32_t)n, S, sa);
+  bool ties = !tie_unlikely((uint32_t)k, (uint32_t)n, S, sa);
+  // Otherwise, when the keys at or above c are few enough for the members'
+  // regions and the select's staging, the cutoff moves to the key below c:
+  // the keys equal to c become survivors and no ties are collected (at
+  // least q of the samples lie at or above c, so k keys almost surely do;
+  // a row where they do not takes the direct path as above).  Every member
+  // takes the same decision from the same samples.
+  if (ties && c >= 2u) {
+    constexpr float kKeysPerWave = 64.0f * VPT * (MODE == TOPK_MODE_BLOCK ? 1 : 8);
+    const float f = (float)(sa + se) * __builtin_amdgcn_rcpf((float)S);
+    if (1.25f * f * kKeysPerWave + 48.0f <= (float)(kTeamLCW - kSpare) &&
+        1.25f * f * (float)n + 256.0f <= (float)p.sel_cap) {
+      c -= 1u;
+      ties = false;
+    }
+  }
   uint32_t* slice = p.team_slices + ((size_t)lrow * G + member) * kMemberWords;
   if (MODE == TOPK_MODE_TOKEN && c == 0u) {
     // a zero cutoff would make the zero keys of slots past the length ties:

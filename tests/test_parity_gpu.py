@@ -237,20 +237,40 @@ def test_team_skipped_ties_take_direct_path():
 
 
 def test_team_ties_collected_when_needed():
-    """A wide row of 0.5 with X = 1.0 at every 64th logit and 5 sampled logits
+    """A wide row of 0.5 with X = 1.0 at every 4th logit and 5 sampled logits
     above X: the samples give no assurance that k keys lie above the cutoff
-    (X), so the team collects the keys equal to X and the row takes the tie
-    pass."""
-    width, k = 150000, 512
+    (X), and the keys at X (a quarter of the row) are too many to become
+    survivors, so the team collects the keys equal to X and the row takes
+    the tie pass (a row of 5 members: their capped tie lists fit the
+    select's staging)."""
+    width, k = 40000, 512
     L = np.full((2, width), 0x3F00, np.uint16)                    # 0.5
-    L[:, ::64] = 0x3F80                                            # 1.0
-    pos = (_sampled_vectors_team(width // 8) * 8)[:5]
+    L[:, ::4] = 0x3F80                                             # 1.0
+    pos = (_sampled_vectors_team(width // 8) * 8 + 1)[:5]
     L[:, pos] = (0x4000 + np.arange(5)).astype(np.uint16)
     d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
              pages=None, page_size=0)
     g, pc = run_gpu(d)
     assert_parity(d, g, run_oracle(d))
     assert np.all(pc == T.PATH_SAMPLED_TIES), pc
+
+
+def test_team_tied_cutoff_moves_below_the_ties():
+    """A wide row of 0.5 with X = 1.0 at every 64th logit and 5 sampled
+    logits above X: fewer than k keys lie above X, but the keys at X (1/64 of
+    the row) fit the survivor regions, so the cutoff moves to the key below
+    X, the keys at X are survivors and the row takes the plain sampled
+    path, exact."""
+    width, k = 150000, 512
+    L = np.full((2, width), 0x3F00, np.uint16)                    # 0.5
+    L[:, ::64] = 0x3F80                                            # 1.0
+    pos = (_sampled_vectors_team(width // 8) * 8 + 1)[:5]
+    L[:, pos] = (0x4000 + np.arange(5)).astype(np.uint16)
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_SAMPLED), pc
 
 
 def test_team_scratch_reused_across_calls():
