@@ -647,35 +647,15 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
 // logits; a block entry holds its block's signed key in the low half and
 // the bottom key in the high half.
 //
-// Compaction of one entry: if either half of x is above the signed cutoff
-// cs, (x, eidx) goes to this wave's region at the wave's running count
-// plus the lane's rank among the kept lanes (ballot + lane-mask count, no
-// atomic).  wcnt (entries) and ecnt (keys above cs, when counted) are
-// wave-uniform; once wcnt passes cap the wave stops writing, so a region
-// needs cap + 64 entries, and a final wcnt above cap means the row
-// overflowed.
-// The region starts at entry wbase (wave-uniform) of `lists`.
-template <bool COUNT_KEYS>
-__device__ __forceinline__ void keep_word(uint32_t x, uint32_t eidx, int32_t cs, uint32_t* lists,
-                                          uint32_t wbase, uint32_t cap, uint32_t& wcnt,
-                                          uint32_t& ecnt) {
-  const unsigned long long mlo = __ballot(lo16s(x) > cs), mhi = __ballot(hi16s(x) > cs);
-  const unsigned long long m = mlo | mhi;
-  if (in_mask(wcnt <= cap ? m : 0ull)) {
-    const uint32_t pos = mbcnt(m) + (wbase + wcnt);
-    *reinterpret_cast<uint2*>(lists + 2 * pos) = make_uint2(x, eidx);
-  }
-  wcnt += popc(m);
-  if (COUNT_KEYS) ecnt += popc(mlo) + popc(mhi);
-}
-
-// The same into LDS without touching the exec mask (fewer scalar
-// instructions): one test per entry on the larger of its two keys, and
-// every lane stores, a lane without a key above cs into its own slot of a
-// dummy area (LDS byte address `dummy`).  at is the LDS byte address of
-// the wave's next entry (wave-uniform); stores stop advancing at lim, so a
-// region needs 64 entries past lim, and a final at above lim means the row
-// overflowed.
+// Compaction of one entry into LDS, without touching the exec mask: if
+// either half of x is above the signed cutoff cs, (x, eidx) goes to this
+// wave's region at the wave's running count plus the lane's rank among the
+// kept lanes (ballot + lane-mask count, no atomic); a lane without a key
+// above cs stores into its own slot of a dummy area (LDS byte address
+// `dummy`).  One test per entry on the larger of its two keys.  at is the
+// LDS byte address of the wave's next entry (wave-uniform); stores stop
+// advancing at lim, so a region needs 64 entries past lim, and a final at
+// above lim means the row overflowed.
 __device__ __forceinline__ void keep_word_lds(uint32_t x, uint32_t eidx, int32_t cs, uint32_t lim,
                                               uint32_t dummy, uint32_t& at) {
   const unsigned long long m = __ballot(max(lo16s(x), hi16s(x)) > cs);
@@ -1239,14 +1219,29 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     return;
   }
 
-  // -- entries above / equal to the cutoff straight to this wave's regions
+  // -- entries above the cutoff: compacted into this wave's region of the
+  // sample-bin area (free once every wave has its cutoff), then copied to
+  // the wave's scratch segment with whole-wave stores.  Entries holding a
+  // key equal to the cutoff (when collected at all) go straight to their
+  // global regions.
   const int32_t cs = (int32_t)c - 0x8000;
   uint32_t* seg = slice + kMemberHdr;
   uint32_t* tl = slice + kMemberHdr + 8 * kTeamLCW;
   const uint32_t wv = readfirst((uint32_t)wave);
   const uint32_t wbase = wv * kTeamLCW, tbase = wv * kTieLCW;
-  const uint32_t cap = kTeamLCW - kSpare, tcap = tie_cap(k);
-  uint32_t wcnt = 0, ecnt = 0, tcnt = 0, tw = 0, tkept = 0, neq = 0;
+  const uint32_t tcap = tie_cap(k);
+  // LDS: 64 dummy entries, then 4 wave regions of kStage entries (kStage -
+  // 64 kept, the rest for the stores past the cap)
+  constexpr uint32_t kStage = (kSampBins + 256 + kRelWords - 128) / 8;
+  static_assert(NT == 256 && kStage - 64 <= (uint32_t)(kTeamLCW - kSpare),
+                "a wave keeps no more entries than its scratch segment takes");
+  const uint32_t lds_h8 = lds_addr(h8);
+  const uint32_t first = lds_h8 + 4u * (128u + 2u * wv * kStage);
+  const uint32_t lim = first + (kStage - 64u) * 8u;
+  const uint32_t dummy = lds_h8 + 8u * (uint32_t)lane;
+  uint32_t at = first;
+  uint32_t tcnt = 0, tw = 0, tkept = 0, neq = 0;
+  __syncthreads();  // every wave is done with the sample bins
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     if (j <= jt) {
@@ -1255,7 +1250,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
         const uint32_t key =
             lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         const uint32_t x = block_entry(key);
-        keep_word<true>(x, (uint32_t)lvid, cs, seg, wbase, cap, wcnt, ecnt);
+        keep_word_lds(x, (uint32_t)lvid, cs, lim, dummy, at);
         if (ties) keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
       } else {
         if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
@@ -1264,14 +1259,28 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
         for (int q2 = 0; q2 < 4; ++q2) {
           const uint32_t w = word_of(raw[j], q2);
           const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
-          keep_word<true>(x, e8 + 2 * q2, cs, seg, wbase, cap, wcnt, ecnt);
+          keep_word_lds(x, e8 + 2 * q2, cs, lim, dummy, at);
           if (ties) keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
         }
       }
     }
   }
+  // copy-out; a token wave counts the keys above the cutoff on the way
+  // (a block entry holds one)
+  const uint32_t wcnt = (at - first) / 8u;
+  const uint32_t nw = min(wcnt, kStage - 64u);
+  const uint32_t* stg = h8 + 128 + 2 * wv * kStage;
+  uint32_t ek = 0;
+  for (uint32_t i = (uint32_t)lane; i < nw; i += 64) {
+    const uint2 e = *reinterpret_cast<const uint2*>(stg + 2 * i);
+    *reinterpret_cast<uint2*>(seg + 2 * (wbase + i)) = e;
+    if constexpr (MODE == TOPK_MODE_TOKEN)
+      ek += (lo16s(e.x) > cs ? 1u : 0u) + (hi16s(e.x) > cs ? 1u : 0u);
+  }
+  const uint32_t ecnt = MODE == TOPK_MODE_TOKEN ? readlane(wave_incl_scan(ek), 63) : nw;
   if (lane == 0) {
-    slice[H_WCNT + wave] = wcnt;
+    // a wave past its LDS region reports an entry count the select reads as overflow
+    slice[H_WCNT + wave] = wcnt > kStage - 64u ? 0xFFFFu : wcnt;
     slice[H_ECNT + wave] = ecnt;
     slice[H_TW + wave] = tw;
     slice[H_TKEPT + wave] = tkept;
