@@ -688,6 +688,12 @@ __device__ __forceinline__ int32_t clamp0(int32_t x, int32_t hi) {
 // cgt + `slot` while that is below `take`; each is written straight to the
 // row's output (through the block table, `lpages` its LDS copy or null).
 // Block entries of -inf blocks write -1.
+// Output slot i of a row (a 32-bit byte offset from the row's base: one
+// scalar base and one vector register per store)
+__device__ __forceinline__ void st_slot(int32_t* out, uint32_t i, int32_t v) {
+  *reinterpret_cast<int32_t*>(reinterpret_cast<char*>(out) + (i << 2)) = v;
+}
+
 template <int MODE, bool GT, bool EQ>
 __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32_t cgt,
                              uint32_t take, unsigned long long* slot, const Out o,
@@ -714,13 +720,16 @@ __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32
       v1 = map_out(o, lpages, v1);
     }
     if (GT) {
-      if (in_mask(g0)) out[bg + mbcnt(g0)] = v0;
-      if (in_mask(g1)) out[bg + ng0 + mbcnt(g1)] = v1;
+      if (in_mask(g0)) st_slot(out, bg + mbcnt(g0), v0);
+      if (in_mask(g1)) st_slot(out, (bg + ng0) + mbcnt(g1), v1);
     }
     if (EQ && nq) {  // keys equal to Ts are few: most chunks skip this
-      const uint32_t p0 = mbcnt(q0, bq), p1 = mbcnt(q1, bq + nq0);
-      if (in_mask(q0) && p0 < take) out[cgt + p0] = v0;
-      if (in_mask(q1) && p1 < take) out[cgt + p1] = v1;
+      // slots cgt + bq + rank while bq + rank < take (room: what is left)
+      const uint32_t b1 = bq + nq0;
+      const uint32_t room0 = bq < take ? take - bq : 0u, room1 = b1 < take ? take - b1 : 0u;
+      const uint32_t r0 = mbcnt(q0), r1 = mbcnt(q1);
+      if (in_mask(q0) && r0 < room0) st_slot(out, (cgt + bq) + r0, v0);
+      if (in_mask(q1) && r1 < room1) st_slot(out, (cgt + b1) + r1, v1);
     }
   }
 }
