@@ -238,11 +238,11 @@ __device__ __forceinline__ int clamp_len(int v, int width) {
 // every wave sees about the same number of keys whatever the length: the
 // per-wave survivor regions stay balanced on short rows.
 template <int NT>
-__device__ __forceinline__ int slot_vid(int j, int jt, int rem) {
+__device__ __forceinline__ int slot_vid(int j, int jt, int rem, int tid = (int)threadIdx.x) {
   constexpr int NW = NT / 64;
-  if (j < jt) return j * NT + (int)threadIdx.x;
+  if (j < jt) return j * NT + tid;
   if (j > jt) return -1;
-  const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int per_w = (rem + NW - 1) / NW;
   const int x = wave * per_w + lane;
   return (lane < per_w && x < rem) ? jt * NT + x : -1;
@@ -314,8 +314,8 @@ __device__ __forceinline__ uint32_t readfirst(uint32_t x) {
 // bins; the lane that crosses `need` is found with one ballot, and the bin
 // inside it with scalar code.  Every lane gets the answer.
 __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, uint32_t& bin,
-                                          uint32_t& above) {
-  const int lane = __lane_id();
+                                          uint32_t& above, int tid = (int)threadIdx.x) {
+  const int lane = (tid & 63);
   const uint4 h = *reinterpret_cast<const uint4*>(hist + lane * 4);
   const uint32_t s = h.x + h.y + h.z + h.w;
   const uint32_t incl = wave_incl_scan(s);
@@ -345,8 +345,8 @@ __device__ __forceinline__ void find_desc(const uint32_t* hist, uint32_t need, u
 template <int C, int STRIDE>
 __device__ __forceinline__ void find_copies(const uint32_t* hist, uint32_t need, uint32_t& bin,
                                             uint32_t& above, uint32_t& total,
-                                            uint32_t* count = nullptr) {
-  const int lane = __lane_id();
+                                            uint32_t* count = nullptr, int tid = (int)threadIdx.x) {
+  const int lane = (tid & 63);
   uint4 h = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int c = 0; c < C; ++c) {
@@ -382,9 +382,9 @@ __device__ __forceinline__ void find_copies(const uint32_t* hist, uint32_t need,
 
 // Sum over the workgroup (every thread gets the total).
 template <int NT>
-__device__ uint32_t block_sum(uint32_t x, uint32_t* tmp) {
+__device__ uint32_t block_sum(uint32_t x, uint32_t* tmp, int tid = (int)threadIdx.x) {
   const uint32_t incl = wave_incl_scan(x);
-  if (__lane_id() == 63) tmp[threadIdx.x >> 6] = incl;
+  if ((tid & 63) == 63) tmp[tid >> 6] = incl;
   __syncthreads();
   uint32_t t = 0;
 #pragma unroll
@@ -394,13 +394,14 @@ __device__ uint32_t block_sum(uint32_t x, uint32_t* tmp) {
 }
 
 // A slot per predicated lane from one LDS counter: one atomic per wave.
-__device__ __forceinline__ uint32_t wave_slot(bool pred, uint32_t* ctr) {
+__device__ __forceinline__ uint32_t wave_slot(bool pred, uint32_t* ctr,
+                                              int tid = (int)threadIdx.x) {
   const unsigned long long m = __ballot(pred);
   uint32_t slot = 0;
   if (m) {
     const int leader = __ffsll(m) - 1;
     uint32_t base = 0;
-    if (__lane_id() == leader) base = atomicAdd(ctr, popc(m));
+    if ((tid & 63) == leader) base = atomicAdd(ctr, popc(m));
     slot = mbcnt(m, readlane(base, leader));
   }
   return slot;
@@ -448,22 +449,24 @@ __device__ __forceinline__ int32_t map_out(const Out& o, const int32_t* lpages, 
   return x < 0 ? -1 : (lpages[i >> o.shift] << o.shift) | (i & ((1 << o.shift) - 1));
 }
 
-__device__ __forceinline__ void set_path(const Params& p, int row, int code) {
-  if (p.path && threadIdx.x == 0) p.path[row] = code;
+__device__ __forceinline__ void set_path(const Params& p, int row, int code,
+                                         int tid = (int)threadIdx.x) {
+  if (p.path && tid == 0) p.path[row] = code;
 }
 
 // Token rows with n <= k: 0..n-1 then -1, no logits read
 // (decode_topk_cute result definition; kimi_k3 IndexerSelect bypass).
 template <int NT>
-__device__ void write_short_token(const Out o, int n, int k) {
-  for (int e = threadIdx.x; e < k; e += NT) o.out[e] = o.map(e < n ? e : -1);
+__device__ void write_short_token(const Out o, int n, int k, int tid = (int)threadIdx.x) {
+  for (int e = tid; e < k; e += NT) o.out[e] = o.map(e < n ? e : -1);
 }
 
 // Block rows with n <= k: every block in order, -1 for -inf blocks, the
 // newest pinned at +inf, then -1 padding.
 template <int NT>
-__device__ void write_short_block(const Out o, const uint4* src, int n, int k) {
-  for (int b = threadIdx.x; b < k; b += NT) {
+__device__ void write_short_block(const Out o, const uint4* src, int n, int k,
+                                  int tid = (int)threadIdx.x) {
+  for (int b = tid; b < k; b += NT) {
     if (b < n) {
       const uint32_t key = (b == n - 1) ? kKeyPosInf : block_key4(src[b]);
       o.put((uint32_t)b, (uint32_t)b, key);
@@ -482,9 +485,8 @@ __device__ void write_short_block(const Out o, const uint4* src, int n, int k) {
 // `region` holds kDirectWords words of LDS.
 template <int MODE, int NT>
 __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o,
-                              uint32_t* region, uint32_t* bc) {
-  const int tid = threadIdx.x;
-  const int copy = __lane_id() & (kCopies - 1);
+                              uint32_t* region, uint32_t* bc, int tid = (int)threadIdx.x) {
+  const int copy = (tid & 63) & (kCopies - 1);
   const int nvec = (MODE == TOPK_MODE_BLOCK) ? n : (v + 7) >> 3;
   uint32_t* hist = region;
   uint32_t* sums = region + 256 * kCopies;
@@ -529,7 +531,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
     }
     __syncthreads();
     uint32_t bin, above;
-    find_desc(sums, pass == 0 ? (uint32_t)k : (uint32_t)k - a1, bin, above);
+    find_desc(sums, pass == 0 ? (uint32_t)k : (uint32_t)k - a1, bin, above, tid);
     if (pass == 0) {
       b1 = 255u - bin;
       a1 = above;
@@ -547,9 +549,9 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
     if constexpr (MODE == TOPK_MODE_BLOCK) {
       const uint32_t key = (vid == n - 1) ? kKeyPosInf : block_key4(raw);
       const bool gt = key > T, eq = key == T;
-      const uint32_t s1 = wave_slot(gt, &bc[BC_C1]);
+      const uint32_t s1 = wave_slot(gt, &bc[BC_C1], tid);
       if (gt) o.put(s1, (uint32_t)vid, key);
-      const uint32_t s2 = wave_slot(eq, &bc[BC_C2]);
+      const uint32_t s2 = wave_slot(eq, &bc[BC_C2], tid);
       if (eq && s2 < take) o.put(cgt + s2, (uint32_t)vid, key);
     } else {
       const uint32_t w[4] = {key2(raw.x), key2(raw.y), key2(raw.z), key2(raw.w)};
@@ -559,9 +561,9 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
         const uint32_t key = half_of(w[e >> 1], e & 1);
         const bool ok = (int)idx < v;
         const bool gt = ok && key > T, eq = ok && key == T;
-        const uint32_t s1 = wave_slot(gt, &bc[BC_C1]);
+        const uint32_t s1 = wave_slot(gt, &bc[BC_C1], tid);
         if (gt) o.put(s1, idx, key);
-        const uint32_t s2 = wave_slot(eq, &bc[BC_C2]);
+        const uint32_t s2 = wave_slot(eq, &bc[BC_C2], tid);
         if (eq && s2 < take) o.put(cgt + s2, idx, key);
       }
     }
@@ -609,27 +611,27 @@ __device__ __forceinline__ bool tie_unlikely(uint32_t k, uint32_t n, uint32_t S,
 template <int NSK, int NT, int LC>
 __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t q, uint32_t* h8,
                                   uint32_t* lo8, uint32_t* above = nullptr,
-                                  uint32_t* equal = nullptr) {
+                                  uint32_t* equal = nullptr, int tid = (int)threadIdx.x) {
   static_assert(NT >= 256, "one thread per high-byte bin");
-  const uint32_t copy = __lane_id() & (kCopies - 1);
+  const uint32_t copy = (tid & 63) & (kCopies - 1);
 #pragma unroll
   for (int i = 0; i < NSK; ++i) {
     if (i < lead || sk[i] != kNone) atomicAdd(&h8[copy * kCopyStride + 255u - (sk[i] >> 8)], 1u);
   }
   __syncthreads();
   uint32_t* sums = h8 + kSampBins;
-  if (threadIdx.x < 256) {
+  if (tid < 256) {
     uint32_t t = 0;
 #pragma unroll
-    for (int c = 0; c < kCopies; ++c) t += h8[c * kCopyStride + threadIdx.x];
-    sums[threadIdx.x] = t;
+    for (int c = 0; c < kCopies; ++c) t += h8[c * kCopyStride + tid];
+    sums[tid] = t;
   }
   __syncthreads();
   uint32_t i1, a1;
-  find_desc(sums, q, i1, a1);
+  find_desc(sums, q, i1, a1, tid);
   const uint32_t b1 = 255u - i1;
-  uint32_t* const loc = lo8 + (__lane_id() % LC) * kRelStride;
-  const uint32_t spill = 256u + ((__lane_id() / LC) & 15);
+  uint32_t* const loc = lo8 + ((tid & 63) % LC) * kRelStride;
+  const uint32_t spill = 256u + (((tid & 63) / LC) & 15);
 #pragma unroll
   for (int i = 0; i < NSK; ++i) {
     const uint32_t x = sk[i];  // an empty slot's high byte is never b1
@@ -637,7 +639,7 @@ __device__ uint32_t sample_cutoff(const uint32_t (&sk)[NSK], int lead, uint32_t 
   }
   __syncthreads();
   uint32_t i2, a2, t2;
-  find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2, equal);  // equal: samples at the cutoff
+  find_copies<LC, kRelStride>(lo8, q - a1, i2, a2, t2, equal, tid);  // equal: samples at the cutoff
   if (above) *above = a1 + a2;  // samples strictly above the cutoff
   return (b1 << 8) | (255u - i2);
 }
@@ -697,8 +699,8 @@ __device__ __forceinline__ void st_slot(int32_t* out, uint32_t i, int32_t v) {
 template <int MODE, bool GT, bool EQ>
 __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32_t cgt,
                              uint32_t take, unsigned long long* slot, const Out o,
-                             const int32_t* lpages) {
-  const int lane = __lane_id();
+                             const int32_t* lpages, int tid = (int)threadIdx.x) {
+  const int lane = (tid & 63);
   int32_t* const out = o.out;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint2 en = *reinterpret_cast<const uint2*>(e + 2 * (b0 + lane));
@@ -754,8 +756,8 @@ template <int MODE, int NW>
 __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, int32_t cs,
                                 uint32_t k, uint32_t* __restrict__ rel, uint32_t* sh,
                                 uint32_t* bc, uint32_t cap, const Out o,
-                                const int32_t* lpages) {
-  const int lane = __lane_id();
+                                const int32_t* lpages, int tid = (int)threadIdx.x) {
+  const int lane = (tid & 63);
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   // keys at or below cs (top - s >= kRelBins) count into the lane's own
   // spill word after its copy's bins, or into one of the 15 below it
@@ -769,7 +771,7 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
   __syncthreads();
   if (__ballot(lane < NW && bc[BC_CNT + lane] > cap)) return SEL_OVERFLOW;
   uint32_t ri, above, total;
-  find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total);
+  find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total, nullptr, tid);
   if (total < k) return SEL_TIES;
   int32_t Ts;
   uint32_t cgt;
@@ -778,7 +780,7 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
     cgt = above;
   } else {
     // the k-th key lies at or above top: 8-bit passes over those keys
-    for (int i = threadIdx.x; i < 512; i += 64 * NW) sh[i] = 0;
+    for (int i = tid; i < 512; i += 64 * NW) sh[i] = 0;
     __syncthreads();
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
@@ -791,7 +793,7 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
     }
     __syncthreads();
     uint32_t i1, a1, i2, a2;
-    find_desc(sh, k, i1, a1);
+    find_desc(sh, k, i1, a1, tid);
     const int32_t b1 = 255 - (int32_t)i1;
     for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
       const uint32_t i = b0 + lane;
@@ -803,20 +805,22 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
       }
     }
     __syncthreads();
-    find_desc(sh + 256, k - a1, i2, a2);
+    find_desc(sh + 256, k - a1, i2, a2, tid);
     Ts = ((b1 << 8) | (255 - (int32_t)i2)) - 0x8000;
     cgt = a1 + a2;
   }
   emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt,
-                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT), o, lpages);
+                                 reinterpret_cast<unsigned long long*>(bc + BC_SLOT), o, lpages,
+                                 tid);
   return SEL_DONE;
 }
 
 // Keys above cs in the entries at e (wave-uniform count).
-__device__ __forceinline__ uint32_t count_above(const uint32_t* e, uint32_t cnt, int32_t cs) {
+__device__ __forceinline__ uint32_t count_above(const uint32_t* e, uint32_t cnt, int32_t cs,
+                                                 int tid = (int)threadIdx.x) {
   uint32_t c = 0;
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
-    const uint32_t i = b0 + __lane_id();
+    const uint32_t i = b0 + (tid & 63);
     const uint32_t x = i < cnt ? e[2 * i] : kDeadPair;
     c += popc(__ballot(lo16s(x) > cs)) + popc(__ballot(hi16s(x) > cs));
   }
@@ -827,8 +831,8 @@ __device__ __forceinline__ uint32_t count_above(const uint32_t* e, uint32_t cnt,
 // to the slots from `base` on: the one-workgroup tie pass's first part.
 template <int MODE>
 __device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_t base,
-                            const Out o) {
-  const int lane = __lane_id();
+                            const Out o, int tid = (int)threadIdx.x) {
+  const int lane = (tid & 63);
   for (uint32_t b0 = 0; b0 < cnt; b0 += 64) {
     const uint32_t i = b0 + lane;
     uint32_t x = kDeadPair, id = 0;
@@ -849,8 +853,9 @@ __device__ void write_above(const uint32_t* e, uint32_t cnt, int32_t cs, uint32_
 // workgroup, one LDS atomic per wave (the rare pass of the one-workgroup
 // kernel).
 __device__ __forceinline__ void keep_equal_slot(bool eq, uint32_t idx, uint16_t* list,
-                                                uint32_t cap, uint32_t* ctr) {
-  const uint32_t slot = wave_slot(eq, ctr);
+                                                uint32_t cap, uint32_t* ctr,
+                                                int tid = (int)threadIdx.x) {
+  const uint32_t slot = wave_slot(eq, ctr, tid);
   if (eq && slot < cap) list[slot] = (uint16_t)idx;
 }
 
