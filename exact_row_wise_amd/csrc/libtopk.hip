@@ -1467,20 +1467,40 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       // stage the survivor entries (and, for the tie pass, the tie entries
       // after them) in LDS with row-level indices: the preloaded chunks
       // first, then whatever they did not cover
+      // (the counts and starts of a wave's preloaded segments read together,
+      // then the stores)
+      uint32_t pc[kPre], ps[kPre];
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        const int s2 = wave + u * NW;  // < kPre NW <= 1024 words of each array
+        const uint32_t cnt = segc[s2], st = start[s2];
+        pc[u] = s2 < nseg ? cnt : 0u;
+        ps[u] = st;
+      }
 #pragma unroll
       for (int u = 0; u < kPre; ++u) {
         const int s2 = wave + u * NW;
-        if (s2 < nseg && (uint32_t)lane < segc[s2]) {
-          const uint32_t d = start[s2] + lane;
-          *reinterpret_cast<uint2*>(ent + 2 * d) =
+        if ((uint32_t)lane < pc[u]) {
+          *reinterpret_cast<uint2*>(ent + 2 * (ps[u] + lane)) =
               make_uint2(pre[u].x, pre[u].y + (uint32_t)(s2 >> 2) * chunk);
         }
       }
-      for (int s2 = wave; s2 < nseg; s2 += NW) {
-        const uint32_t from = s2 < kPre * NW ? 64u : 0u;
+#pragma unroll
+      for (int u = 0; u < kPre; ++u) {
+        if (pc[u] > 64u) {  // what the preloaded head did not cover
+          const int s2 = wave + u * NW;
+          const uint32_t* es = seg_src(s2);
+          const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
+          for (uint32_t i = 64u + lane; i < pc[u]; i += 64) {
+            const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
+            *reinterpret_cast<uint2*>(ent + 2 * (ps[u] + i)) = make_uint2(x.x, x.y + g);
+          }
+        }
+      }
+      for (int s2 = wave + kPre * NW; s2 < nseg; s2 += NW) {  // segments without a head
         const uint32_t* es = seg_src(s2);
         const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
-        for (uint32_t i = from + lane; i < segc[s2]; i += 64) {
+        for (uint32_t i = lane; i < segc[s2]; i += 64) {
           const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
           *reinterpret_cast<uint2*>(ent + 2 * (start[s2] + i)) = make_uint2(x.x, x.y + g);
         }
