@@ -108,7 +108,7 @@ enum {
   BC_EQ = 64,     // tie-list counter
   BC_C1 = 65, BC_C2 = 66,   // direct-path write counters
   BC_SLOT = 68,   // 2 (8-byte aligned): output slots taken above T | equal to T
-  BC_TMP = 96     // 32: reductions, a team row's totals
+  BC_TMP = 96     // 32: reductions, a team row's totals, the select's bin search
 };
 
 // One team member's slice of global scratch (32-bit words), per wave w:
@@ -752,7 +752,7 @@ enum { SEL_DONE = 0, SEL_TIES = 1, SEL_OVERFLOW = 2 };
 // Returns SEL_OVERFLOW when a wave's published entry count bc[BC_CNT + w]
 // passed `cap` (checked after the histogram barrier), SEL_TIES when fewer
 // than k keys lie above cs (nothing written then), else SEL_DONE.
-template <int MODE, int NW>
+template <int MODE, int NW, bool ONE = false>
 __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, int32_t cs,
                                 uint32_t k, uint32_t* __restrict__ rel, uint32_t* sh,
                                 uint32_t* bc, uint32_t cap, const Out o,
@@ -771,7 +771,25 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
   __syncthreads();
   if (__ballot(lane < NW && bc[BC_CNT + lane] > cap)) return SEL_OVERFLOW;
   uint32_t ri, above, total;
-  find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total, nullptr, tid);
+  if constexpr (ONE) {
+    // wave 0 alone searches the bins and publishes the result (with many
+    // waves per SIMD the others would only repeat it; with few, the extra
+    // barrier costs more than the repeats)
+    if ((tid >> 6) == 0) {
+      find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total, nullptr, tid);
+      if (lane == 0) {
+        bc[BC_TMP + 8] = ri;
+        bc[BC_TMP + 9] = above;
+        bc[BC_TMP + 10] = total;
+      }
+    }
+    __syncthreads();
+    ri = bc[BC_TMP + 8];
+    above = bc[BC_TMP + 9];
+    total = bc[BC_TMP + 10];
+  } else {
+    find_copies<kRelCopies, kRelStride>(rel, k, ri, above, total, nullptr, tid);
+  }
   if (total < k) return SEL_TIES;
   int32_t Ts;
   uint32_t cgt;
@@ -1530,8 +1548,8 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       const uint32_t hi = min(lo + share, E);
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
       if (sampled) {
-        select_and_write<MODE, NW>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
-                                   0xFFFFFFFFu, o, nullptr);
+        select_and_write<MODE, NW, true>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
+                                         0xFFFFFFFFu, o, nullptr);
         code = TOPK_PATH_SAMPLED;
       } else {
         // the k-th key is the cutoff: every key above it, then the first ties
