@@ -273,6 +273,21 @@ def test_team_tied_cutoff_moves_below_the_ties():
     assert np.all(pc == T.PATH_SAMPLED), pc
 
 
+def test_team_member_region_overflow_takes_direct_path():
+    """Block rows of 4500 blocks at k = 2048 go to the team path with more
+    than half of every member's blocks above the cutoff: a member wave keeps
+    more entries than its LDS region holds, reports the overflow, and the row
+    takes the direct path, exact."""
+    rng = np.random.Generator(np.random.PCG64(4500))
+    width, k = 36000, 2048
+    L = W.f32_to_bf16_bits(rng.standard_normal((2, width), dtype=np.float32))
+    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=1, width=width,
+             pages=None, page_size=0)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert np.all(pc == T.PATH_DIRECT_OVERFLOW), pc
+
+
 def test_team_scratch_reused_across_calls():
     """Consecutive team launches on one stream see clean scratch, also when
     a call has more rows than the one before it (regression: the control
