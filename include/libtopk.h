@@ -39,12 +39,16 @@
  * Execution.  The call enqueues its kernels on `stream` (a hipStream_t;
  * NULL = the default stream) and returns without waiting.  It allocates
  * nothing on the hot path: rows wider than one workgroup's share use a
- * per-(device, stream) scratch buffer that the library allocates and
- * zeroes on first use for that stream (so the first call on a stream must
- * not be under graph capture) and grows, after synchronizing that stream,
- * when a larger call needs more.  Every launch leaves the scratch zeroed.
- * Calls that overlap on one stream's scratch are serialized by the
- * stream; calls on different streams get different scratch buffers.
+ * per-(device, stream) scratch buffer that the library allocates on first
+ * use for that stream and replaces by a larger one, after synchronizing
+ * that stream, when a call needs more.  The scratch is never cleared: every
+ * word a call reads there was written earlier in the same call.  A call
+ * that has to allocate cannot run under graph capture (it fails with
+ * TOPK_ERR_HIP), and a graph captured on a stream holds that stream's
+ * scratch address: capture after the stream's largest call, since a later
+ * call that replaces the scratch leaves earlier graphs pointing at freed
+ * memory.  Calls that overlap on one stream's scratch are serialized by
+ * the stream; calls on different streams get different scratch buffers.
  *
  * Errors.  Argument errors are reported before anything is enqueued, by
  * a negative status; out is then untouched.  Values are never errors:

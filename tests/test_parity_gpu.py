@@ -318,6 +318,46 @@ def test_side_stream():
     assert_parity(d3, g, run_oracle(d3))
 
 
+def test_graph_replays():
+    """Calls captured in one HIP graph (the row path with a block table, a
+    token team and a block team) and replayed several times, with other
+    eager calls and synchronizations between the replays: every replay's
+    outputs match the oracle (the library records no memset, and its team
+    scratch needs no clearing between calls)."""
+    ds = [W.make(2, rows=48, width=16384, seed=401), W.make(3, rows=5, width=60000, seed=402),
+          W.make(4, rows=6, width=150000, seed=403)]
+    # eager work in between: no wider than the captured team rows, so that
+    # the stream's scratch (captured by address) is not replaced
+    other = W.make(3, rows=7, width=50000, seed=404)
+    os_ = [run_oracle(d) for d in ds]
+    s = torch.cuda.Stream()
+    dev = [_dev(d) for d in ds]
+
+    def calls():
+        return [T.topk_bf16_rows(L, VL, d["k"], d["mode"], block_table=P,
+                                 page_size=d.get("page_size") or 64, width=d["width"])
+                for d, (L, VL, P) in zip(ds, dev)]
+
+    with torch.cuda.stream(s):
+        calls()  # first use on this stream: the scratch is set up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = calls()
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            for o in outs:
+                o.fill_(-7)
+            go, _ = run_gpu(other, stream=s)  # eager work on the same stream and scratch
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"graph replay {rep}", flush=True)
+        for d, o, ref in zip(ds, outs, os_):
+            assert_parity(d, o.cpu().numpy(), ref)
+    assert_parity(other, go, run_oracle(other))
+
+
 def test_widest_rows():
     """Rows of 2^20 logits in token mode (the widest team) and block mode."""
     rng = np.random.Generator(np.random.PCG64(304))
