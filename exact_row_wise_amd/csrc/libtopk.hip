@@ -125,7 +125,7 @@ static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * 8 - 1) / (kTeamNT * 8) <= kMaxMemb
               "too many token members per row");
 static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) / (kTeamNT * kTeamBlockVPT) <=
                   kMaxMembers, "too many block members per row");
-static_assert(4 * kMaxMembers <= kSelNT, "one select thread per segment");
+static_assert(4 * kMaxMembers <= 1024, "the select's segment arrays hold every segment");
 
 struct Params {
   const uint16_t* logits;
@@ -1138,9 +1138,10 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 // row; the same in every member) and then its chunk of NT * VPT vectors
 // (members past the row's valid length exit at once), derives the row's
 // cutoff while its chunk is still in flight, and writes to its scratch
-// slice the entries holding a key above the cutoff and, in the same pass,
-// those holding a key equal to it (chunk-local indices).  Short rows and
-// rows sent straight to the direct path are left to stage 2.
+// slice the entries holding a key above the cutoff (compacted in LDS, then
+// copied out) and, in the same pass when the cutoff may be tied, those
+// holding a key equal to it (chunk-local indices).  Short rows and rows
+// sent straight to the direct path are left to stage 2.
 template <int MODE, int VPT, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
