@@ -98,6 +98,19 @@ def _random_rows(rng, rows, width, kind):
     if kind == "ties":
         lv = np.array([0x3F80, 0x4000, 0xBF80, 0x0000, 0x8000, 0xFF80, 0x7F80], np.uint16)
         return lv[rng.integers(0, lv.size, size=(rows, width))]
+    if kind == "negative":  # every value below zero: the cutoff is negative
+        x = rng.standard_normal((rows, width), dtype=np.float32) - 8.0
+        return W.f32_to_bf16_bits(x)
+    if kind in ("neg_ties", "crowded"):
+        # a few levels with Zipf weights: the cutoff falls on a heavily tied
+        # key (negative levels, or N(0, 2) levels)
+        nlv = 30 if kind == "neg_ties" else 200
+        lvf = rng.standard_normal(nlv).astype(np.float32) * 2.0
+        if kind == "neg_ties":
+            lvf = -np.abs(lvf) - 0.5
+        lv = W.f32_to_bf16_bits(lvf)
+        w = 1.0 / np.arange(1, nlv + 1)
+        return lv[rng.choice(nlv, size=(rows, width), p=w / w.sum())]
     raise ValueError(kind)
 
 
@@ -128,6 +141,10 @@ EDGE = [
     (8, 1, 1, "bits", 0), (17, 2, 1, "bits", 0), (800, 50, 1, "ties", 0),
     (32768, 2048, 1, "normal", 0), (32776, 1024, 1, "bits", 0), (100001, 7, 1, "normal", 1),
     (300000, 2048, 1, "ties", 0),
+    # negative cutoffs and heavily tied cutoffs, one workgroup and team rows
+    (16384, 512, 0, "neg_ties", 0), (8000, 300, 1, "neg_ties", 0), (12000, 300, 0, "negative", 0),
+    (60000, 512, 0, "negative", 0), (60000, 512, 0, "neg_ties", 1), (40000, 100, 0, "neg_ties", 0),
+    (150000, 1024, 0, "crowded", 0), (200000, 2048, 1, "neg_ties", 0), (33000, 2048, 1, "negative", 0),
 ]
 
 
