@@ -51,6 +51,7 @@
 #include <string.h>
 
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <utility>
 
@@ -908,7 +909,7 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 // ============================================ one workgroup per row
 // Rows whose valid vectors fit NT * VPT: the whole row sits in VGPRs.
 
-template <int MODE, int NT, int VPT>
+template <int MODE, int NT, int VPT, bool ONE>
 __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   constexpr int NW = NT / 64;
   extern __shared__ uint32_t smem[];
@@ -1066,8 +1067,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       lds_store2(min(at, lim) + 8u * lane, kDeadPair, 0u);
       // exact select over the survivors; its histogram barrier also publishes
       // the entry counts (overflow) and the count of keys above the cutoff
-      const int st = select_and_write<MODE, NW>(seg, min(wcnt, cap), cs, (uint32_t)k, rel, sh,
-                                                bc, cap, o, lpages);
+      const int st = select_and_write<MODE, NW, ONE>(seg, min(wcnt, cap), cs, (uint32_t)k, rel,
+                                                     sh, bc, cap, o, lpages);
       if (st == SEL_OVERFLOW) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
@@ -1662,6 +1663,27 @@ int allow_lds(const void* kernel, size_t lds) {
   return TOPK_OK;
 }
 
+// Workgroups of `kernel` (nt threads, lds bytes) resident on the device at
+// once, cached per device, kernel and size; 0 when the runtime cannot say.
+int resident_grid(const void* kernel, int nt, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = done.find({dev, kernel, lds});
+    if (it != done.end()) return it->second;
+  }
+  if (lds > 65536 && allow_lds(kernel, lds) != TOPK_OK) return 0;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  std::lock_guard<std::mutex> g(mu);
+  return done[{dev, kernel, lds}] = per_cu * cus;
+}
+
 template <class K>
 int launch(K kernel, int grid, int nt, size_t lds, hipStream_t stream, const Params& p) {
   if (lds > 65536) {
@@ -1731,10 +1753,22 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
       p.page_lds = (int32_t)(lds / 4);
       lds += (size_t)kPageLdsMax * 4;
     }
-    if (mode == TOPK_MODE_BLOCK)
-      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT>, rows, kRowNT, lds,
+    // more rows than resident workgroups: the throughput variant, whose
+    // exact select searches its bins with one wave (the other waves' copies
+    // of that search cost issue slots that other rows' waves could use);
+    // otherwise every wave searches for itself, one barrier fewer on the
+    // row's path
+    if (mode == TOPK_MODE_BLOCK) {
+      auto lat = topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, false>;
+      if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
+        return launch(lat, rows, kRowNT, lds, stream, p);
+      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, true>, rows, kRowNT, lds,
                     stream, p);
-    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT>, rows, kRowNT, lds,
+    }
+    auto lat = topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, false>;
+    if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
+      return launch(lat, rows, kRowNT, lds, stream, p);
+    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, true>, rows, kRowNT, lds,
                   stream, p);
   }
 
