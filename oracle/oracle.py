@@ -85,6 +85,12 @@ class Oracle:
                                          ctypes.c_int32, _i32p, ctypes.c_int64,
                                          ctypes.c_int32, _i32p]
         lib.oracle_topk_rows.restype = ctypes.c_int
+        lib.oracle_topk_rows_ordered.argtypes = [_u16p, ctypes.c_int64, _i32p,
+                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, ctypes.c_int32, _i32p,
+                                                 ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
+                                                 _i32p]
+        lib.oracle_topk_rows_ordered.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -193,6 +199,44 @@ class Oracle:
         return out
 
 
+    def topk_ordered(self, logits, valid_len, k: int, mode: int, width: int | None = None,
+                     pages=None, page_size: int = 64, threads: int = 1):
+        """oracle_topk_rows_ordered over a [rows, row_stride] uint16 matrix:
+        (out [rows, k], ids [rows, k], valid [rows]), all int32."""
+        L = np.ascontiguousarray(np.asarray(logits, dtype=np.uint16))
+        assert L.ndim == 2
+        n_rows, stride = L.shape
+        if width is None:
+            width = stride
+        vl = np.ascontiguousarray(np.asarray(valid_len, dtype=np.int32))
+        P = None
+        pstride = 0
+        if pages is not None:
+            P = np.ascontiguousarray(np.asarray(pages, dtype=np.int32))
+            pstride = P.shape[1]
+        out = np.empty((n_rows, k), dtype=np.int32)
+        ids = np.empty((n_rows, k), dtype=np.int32)
+        valid = np.empty(n_rows, dtype=np.int32)
+        pp = _i32(P) if P is not None else None
+        lib = self.lib
+
+        def run(b, e):
+            rc = lib.oracle_topk_rows_ordered(_u16(L), stride, _i32(vl), b, e, int(width),
+                                              int(k), int(mode), pp, pstride, int(page_size),
+                                              _i32(out), _i32(ids), _i32(valid))
+            if rc != 0:
+                raise MemoryError("oracle_topk_rows_ordered")
+
+        threads = max(1, min(int(threads), max(n_rows, 1)))
+        if threads == 1 or n_rows < 2:
+            run(0, n_rows)
+        else:
+            bounds = np.linspace(0, n_rows, threads + 1).astype(int)
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(lambda i: run(int(bounds[i]), int(bounds[i + 1])),
+                            range(threads)))
+        return out, ids, valid
+
 def default() -> Oracle:
     """The oracle built from oracle/topk_oracle.c (compiled on first use)."""
     global _default
@@ -233,3 +277,8 @@ def topk(logits, valid_len, k, mode, width=None, pages=None, page_size=64, threa
          rows=None):
     return default().topk(logits, valid_len, k, mode, width=width, pages=pages,
                           page_size=page_size, threads=threads, rows=rows)
+
+
+def topk_ordered(logits, valid_len, k, mode, width=None, pages=None, page_size=64, threads=1):
+    return default().topk_ordered(logits, valid_len, k, mode, width=width, pages=pages,
+                                  page_size=page_size, threads=threads)

@@ -254,3 +254,102 @@ int oracle_topk_rows(const uint16_t *logits, int64_t row_stride,
     }
     return 0;
 }
+
+static int by_index_asc(const void *pa, const void *pb)
+{
+    const int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+/* The deterministic ordered result of one row ([K3] IndexerSelect class
+ * docstring and its ordered output pass: the selected keys in key order,
+ * that is by ascending element index, ties at the threshold going to the
+ * lowest indices; -1 past the row's count; the counts in `valid`; the
+ * logical element indices in `ids`):
+ *  ids[0:c]  the selected element indices in ascending order, where the
+ *            selection is the first c = min(n, k) items of the (key desc,
+ *            index asc) order (all n elements when n <= k), then -1 up to k;
+ *  out[j]    -1 where ids[j] is -1 or, in block mode, where the element's
+ *            key is that of -inf (the [DTK] -1 rule); otherwise ids[j]
+ *            through the block table, as in oracle_topk_row;
+ *  *valid    c.
+ * ids may be NULL.  Returns 0, or -2 on allocation failure. */
+int oracle_topk_row_ordered(const uint16_t *row, int32_t valid_len, int32_t width,
+                            int32_t k, int32_t mode, const int32_t *pages,
+                            int32_t page_size, int32_t *out, int32_t *ids,
+                            int32_t *valid)
+{
+    int32_t v = clamp_len(valid_len, width);
+    int32_t n, j, cnt;
+    uint16_t *keys;
+    int32_t *sel;
+    uint16_t neg_inf_key = oracle_key(0xFF80u);
+    keys = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)(width > 0 ? width : 1));
+    sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
+    if (!keys || !sel) {
+        free(keys);
+        free(sel);
+        return -2;
+    }
+    n = oracle_row_keys(row, v, mode, keys);
+    if (n <= k) {
+        for (j = 0; j < n; ++j)
+            sel[j] = j;
+        cnt = n;
+    } else {
+        oracle_item *items = (oracle_item *)malloc(sizeof(oracle_item) * (size_t)n);
+        if (!items) {
+            free(keys);
+            free(sel);
+            return -2;
+        }
+        for (j = 0; j < n; ++j) {
+            items[j].key = keys[j];
+            items[j].index = j;
+        }
+        qsort(items, (size_t)n, sizeof(oracle_item), by_key_desc);
+        for (j = 0; j < k; ++j)
+            sel[j] = items[j].index;
+        free(items);
+        cnt = k;
+        qsort(sel, (size_t)cnt, sizeof(int32_t), by_index_asc);
+    }
+    for (j = 0; j < k; ++j) {
+        int32_t i = j < cnt ? sel[j] : -1;
+        int32_t o = i;
+        if (i >= 0 && mode == ORACLE_BLOCK && keys[i] == neg_inf_key)
+            o = -1;
+        if (o >= 0 && pages)
+            o = pages[o / page_size] * page_size + o % page_size;
+        out[j] = o;
+        if (ids)
+            ids[j] = i;
+    }
+    *valid = cnt;
+    free(keys);
+    free(sel);
+    return 0;
+}
+
+/* oracle_topk_row_ordered over rows [row_begin, row_end) of a
+ * [rows, row_stride] BF16 matrix: out and ids [rows, k], valid [rows]
+ * (ids may be NULL).  Returns 0 or the first row's error. */
+int oracle_topk_rows_ordered(const uint16_t *logits, int64_t row_stride,
+                             const int32_t *valid_len, int32_t row_begin,
+                             int32_t row_end, int32_t width, int32_t k, int32_t mode,
+                             const int32_t *pages, int64_t pages_stride,
+                             int32_t page_size, int32_t *out, int32_t *ids,
+                             int32_t *valid)
+{
+    int32_t r;
+    for (r = row_begin; r < row_end; ++r) {
+        const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;
+        int rc = oracle_topk_row_ordered(logits + (int64_t)r * row_stride, valid_len[r],
+                                         width, k, mode, prow, page_size,
+                                         out + (int64_t)r * k,
+                                         ids ? ids + (int64_t)r * k : NULL, valid + r);
+        if (rc)
+            return rc;
+    }
+    return 0;
+}

@@ -327,6 +327,86 @@ def pin_worked_examples(orc):
                 assert out.tolist() == expected, f"{name}: {out.tolist()}"
 
 
+def _ordered_by_rank(keys, n, k):
+    """The ordered selection straight from its definition: element i is taken
+    when fewer than k elements come before it in the (key desc, index asc)
+    order, i.e. (keys above it) + (equal keys at lower indices) < k; the taken
+    indices are listed in ascending order.  No sort is involved."""
+    sel = []
+    for i in range(n):
+        before = int((keys[:n] > keys[i]).sum()) + int((keys[:i] == keys[i]).sum())
+        if before < k:
+            sel.append(i)
+    return sel
+
+
+def pin_ordered_rank_definition(orc):
+    """Ordered results of tiny rows (both modes, ragged and short lengths,
+    tie-heavy and NaN/inf alphabets, with and without a block table) equal the
+    rank definition bit for bit: ids ascending then -1, out mapped through the
+    table with -inf blocks as -1, valid = min(n, k)."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    alphabets = [
+        None,
+        np.array([0x3F80, 0xBF80, 0x0000, 0x8000], np.uint16),
+        np.array([0x7FC0, 0xFFC0, 0x7F80, 0xFF80, 0x4000], np.uint16),
+    ]
+    ps = 4
+    for trial in range(120):
+        mode = TOKEN if trial % 2 == 0 else BLOCK
+        width = 8 * (1 + trial % 5)
+        alpha = alphabets[trial % 3]
+        if alpha is None:
+            row = rng.integers(0, 1 << 16, size=width).astype(np.uint16)
+        else:
+            row = alpha[rng.integers(0, alpha.size, size=width)]
+        if mode == BLOCK and trial % 4 == 1:
+            row[0:8] = 0xFF80                                  # a -inf block
+        v = int(rng.integers(0, width + 1))
+        pages = rng.permutation((width + ps - 1) // ps).astype(np.int32) if trial % 3 == 0 else None
+        keys = orc.row_keys(row, v, mode)
+        n = keys.size
+        for k in (1, 2, 3, 5, 9):
+            out, ids, valid = orc.topk_ordered(row[None, :], [v], k, mode, pages=(
+                None if pages is None else pages[None, :]), page_size=ps)
+            sel = _ordered_by_rank(keys, n, k)
+            want_ids = sel + [-1] * (k - len(sel))
+            want_out = []
+            for i in want_ids:
+                o = i
+                if i >= 0 and mode == BLOCK and keys[i] == 0x007F:
+                    o = -1
+                if o >= 0 and pages is not None:
+                    o = int(pages[o // ps]) * ps + o % ps
+                want_out.append(o)
+            ctx = f"trial {trial} mode {mode} v {v} k {k}"
+            assert int(valid[0]) == min(n, k), ctx
+            assert ids[0].tolist() == want_ids, f"{ctx}: {ids[0]} vs {want_ids}"
+            assert out[0].tolist() == want_out, f"{ctx}: {out[0]} vs {want_out}"
+
+
+def pin_ordered_worked_cases(orc):
+    """Hand-derived ordered results for the row 5, 7, 7, 3, 7 (token mode):
+    the three 7s tie at the top, so k = 1 and 2 take the lowest-index 7s, k = 3
+    all three, k = 4 adds the 5, and k = 6 is a short row."""
+    row = np.array([0x40A0, 0x40E0, 0x40E0, 0x4040, 0x40E0, 0, 0, 0], np.uint16)
+    want = {1: [1], 2: [1, 2], 3: [1, 2, 4], 4: [0, 1, 2, 4], 6: [0, 1, 2, 3, 4, -1]}
+    for k, w in want.items():
+        out, ids, valid = orc.topk_ordered(row[None, :], [5], k, TOKEN)
+        assert out[0].tolist() == w and ids[0].tolist() == w, (k, out, ids)
+        assert int(valid[0]) == min(5, k)
+    # block mode: blocks (1, -inf, 9, 9) with the newest pinned: k = 2 takes
+    # block 3 (pinned +inf) and the lowest-index 9 (block 2)
+    b = np.zeros(32, np.uint16)
+    b[0:8] = 0x3F80
+    b[8:16] = 0xFF80
+    b[16:24] = 0x4110
+    b[24:32] = 0x4110
+    out, ids, valid = orc.topk_ordered(b[None, :], [32], 2, BLOCK)
+    assert ids[0].tolist() == [2, 3] and out[0].tolist() == [2, 3] and int(valid[0]) == 2
+    out, ids, valid = orc.topk_ordered(b[None, :], [32], 4, BLOCK)
+    assert ids[0].tolist() == [0, 1, 2, 3] and out[0].tolist() == [0, -1, 2, 3]
+
 ALL_PINS = [
     pin_key_fixed_points,
     pin_key_bijection,
@@ -347,6 +427,8 @@ ALL_PINS = [
     pin_poison_not_selected,
     pin_page_transform_roundtrip,
     pin_worked_examples,
+    pin_ordered_rank_definition,
+    pin_ordered_worked_cases,
 ]
 
 

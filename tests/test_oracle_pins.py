@@ -44,10 +44,15 @@ MUTANTS = [
     ("inf counted as NaN", "((bits & 0x007Fu) != 0u)", "1"),
     ("no upper clamp", "if (v > width)\n        return width;", "if (v > width)\n        return v - 0;"),
     ("k-th is one off", "t = items[k - 1].key;", "t = items[k].key;"),
-    ("short rows use <", "if (n <= k) {\n        for (j = 0; j < n; ++j)",
-     "if (n < k) {\n        for (j = 0; j < n; ++j)"),
+    ("short rows use <", "if (n <= k) {\n        for (j = 0; j < n; ++j)\n            out[j] = j;",
+     "if (n < k) {\n        for (j = 0; j < n; ++j)\n            out[j] = j;"),
     ("block max keeps first", "if (k > best)\n            best = k;", "if (k < best)\n            best = k;"),
     ("tie count includes >", "else if (keys[i] == t)", "if (keys[i] >= t)"),
+    ("ordered: no index sort", "qsort(sel, (size_t)cnt, sizeof(int32_t), by_index_asc);", ";"),
+    ("ordered: descending index", "return a < b ? -1 : (a > b ? 1 : 0);",
+     "return a < b ? 1 : (a > b ? -1 : 0);"),
+    ("ordered: count is k", "*valid = cnt;", "*valid = k;"),
+    ("ordered: ids mapped", "ids[j] = i;", "ids[j] = o;"),
 ]
 
 
