@@ -68,6 +68,12 @@ def library():
         lib.topk_bf16_rows.restype = ctypes.c_int
         lib.topk_bf16_rows_ex.argtypes = sig + [ctypes.POINTER(_Options), ctypes.c_void_p]
         lib.topk_bf16_rows_ex.restype = ctypes.c_int
+        osig = sig + [ctypes.c_void_p, ctypes.c_void_p]
+        lib.topk_bf16_rows_ordered.argtypes = osig + [ctypes.c_void_p]
+        lib.topk_bf16_rows_ordered.restype = ctypes.c_int
+        lib.topk_bf16_rows_ordered_ex.argtypes = osig + [ctypes.POINTER(_Options),
+                                                         ctypes.c_void_p]
+        lib.topk_bf16_rows_ordered_ex.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_last_error.argtypes = []
@@ -116,6 +122,28 @@ def topk_bf16_rows(logits: torch.Tensor, valid_len: torch.Tensor, k: int, mode=M
     stream      torch stream (default: the current stream)
     Returns out.
     """
+    return _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
+                 path_codes, stream)[0]
+
+
+def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int,
+                           mode=MODE_TOKEN, block_table: torch.Tensor | None = None,
+                           page_size: int = 64, out: torch.Tensor | None = None,
+                           valid: torch.Tensor | None = None, ids: torch.Tensor | None = None,
+                           want_ids: bool = True, width: int | None = None,
+                           force_direct: bool = False, path_codes: torch.Tensor | None = None,
+                           stream: torch.cuda.Stream | None = None):
+    """Deterministic ordered top-k of every row (see include/libtopk.h):
+    the selected indices in ascending order, ties at the k-th key from the
+    lowest indices, -1 past the count.  Arguments as for topk_bf16_rows, plus
+    valid (int32 [rows]) and ids (int32 [rows, k]), allocated if None (ids
+    only when want_ids).  Returns (out, valid, ids or None)."""
+    return _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
+                 path_codes, stream, True, valid, ids, want_ids)
+
+
+def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
+          path_codes, stream, ordered=False, valid=None, ids=None, want_ids=False):
     lib = library()
     if logits.dim() != 2:
         raise ValueError("logits must be 2-D [rows, row_stride]")
@@ -138,6 +166,17 @@ def topk_bf16_rows(logits: torch.Tensor, valid_len: torch.Tensor, k: int, mode=M
     elif (out.dtype != torch.int32 or tuple(out.shape) != (rows, int(k))
           or not out.is_contiguous() or out.device != dev):
         raise ValueError("out must be a contiguous int32 [rows, k] tensor on the same GPU")
+    if ordered:
+        if valid is None:
+            valid = torch.empty(rows, dtype=torch.int32, device=dev)
+        elif (valid.dtype != torch.int32 or valid.numel() != rows or not valid.is_contiguous()
+              or valid.device != dev):
+            raise ValueError("valid must be a contiguous int32 [rows] tensor on the same GPU")
+        if ids is None and want_ids:
+            ids = torch.empty((rows, int(k)), dtype=torch.int32, device=dev)
+        elif ids is not None and (ids.dtype != torch.int32 or tuple(ids.shape) != (rows, int(k))
+                                  or not ids.is_contiguous() or ids.device != dev):
+            raise ValueError("ids must be a contiguous int32 [rows, k] tensor on the same GPU")
     bt = None
     if block_table is not None:
         if (block_table.dtype != torch.int32 or block_table.dim() != 2
@@ -158,10 +197,17 @@ def topk_bf16_rows(logits: torch.Tensor, valid_len: torch.Tensor, k: int, mode=M
         args = (logits.data_ptr(), int(row_stride), valid_len.data_ptr(), int(rows),
                 int(width), int(k), _mode(mode), ctypes.byref(bt) if bt is not None else None,
                 out.data_ptr())
-        if opts is None:
-            rc = lib.topk_bf16_rows(*args, ctypes.c_void_p(s.cuda_stream))
+        st = ctypes.c_void_p(s.cuda_stream)
+        if ordered:
+            args += (valid.data_ptr(), ids.data_ptr() if ids is not None else None)
+            if opts is None:
+                rc = lib.topk_bf16_rows_ordered(*args, st)
+            else:
+                rc = lib.topk_bf16_rows_ordered_ex(*args, ctypes.byref(opts), st)
+        elif opts is None:
+            rc = lib.topk_bf16_rows(*args, st)
         else:
-            rc = lib.topk_bf16_rows_ex(*args, ctypes.byref(opts), ctypes.c_void_p(s.cuda_stream))
+            rc = lib.topk_bf16_rows_ex(*args, ctypes.byref(opts), st)
     if rc != 0:
         raise TopkError(rc, lib.topk_last_error().decode())
-    return out
+    return out, valid, ids

@@ -149,6 +149,14 @@ struct Params {
   int32_t team_cv;       // 16-byte vectors of one member
   uint32_t* team_slices; // [rows][G][kMemberWords]
   int32_t sel_cap;       // survivor entries the select kernel stages in LDS
+  // ordered results (ascending element index, lowest-index ties):
+  int32_t ord;           // 1: ordered results, with counts and logical ids
+  int32_t* valid;        // [rows] counts, or null
+  int32_t* ids;          // [rows][k] logical element indices, or null
+  int32_t ord_G;         // team rows: order-pass members per row
+  int32_t ord_span;      // team rows: 16-byte vectors per order-pass member
+  uint32_t* ord_rec;     // team rows: [rows][2] threshold key, count above (in scratch)
+  uint32_t* ord_cnt;     // team rows: [rows][ord_G] per-member counts (in scratch)
 };
 
 // ------------------------------------------------------------------ keys
@@ -486,7 +494,8 @@ __device__ void write_short_block(const Out o, const uint4* src, int n, int k,
 // `region` holds kDirectWords words of LDS.
 template <int MODE, int NT>
 __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o,
-                              uint32_t* region, uint32_t* bc, int tid = (int)threadIdx.x) {
+                              uint32_t* region, uint32_t* bc, bool ordered = false,
+                              uint2* tsel = nullptr, int tid = (int)threadIdx.x) {
   const int copy = (tid & 63) & (kCopies - 1);
   const int nvec = (MODE == TOPK_MODE_BLOCK) ? n : (v + 7) >> 3;
   uint32_t* hist = region;
@@ -545,6 +554,10 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
   const uint32_t T = (b1 << 8) | b2;
   const uint32_t cgt = a1 + a2;
   const uint32_t take = (uint32_t)k - cgt;
+  if (ordered) {  // ordered results: the caller writes
+    *tsel = make_uint2(T, cgt);
+    return;
+  }
   for (int vid = tid; vid < nvec; vid += NT) {
     const uint4 raw = src[vid];
     if constexpr (MODE == TOPK_MODE_BLOCK) {
@@ -757,7 +770,8 @@ template <int MODE, int NW, bool ONE = false>
 __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, int32_t cs,
                                 uint32_t k, uint32_t* __restrict__ rel, uint32_t* sh,
                                 uint32_t* bc, uint32_t cap, const Out o,
-                                const int32_t* lpages, int tid = (int)threadIdx.x) {
+                                const int32_t* lpages, bool ordered = false,
+                                uint2* tsel = nullptr, int tid = (int)threadIdx.x) {
   const int lane = (tid & 63);
   const int32_t top = cs + kRelBins;  // signed keys at or above top share bin 0
   // keys at or below cs (top - s >= kRelBins) count into the lane's own
@@ -827,6 +841,10 @@ __device__ int select_and_write(const uint32_t* __restrict__ e, uint32_t cnt, in
     find_desc(sh + 256, k - a1, i2, a2, tid);
     Ts = ((b1 << 8) | (255 - (int32_t)i2)) - 0x8000;
     cgt = a1 + a2;
+  }
+  if (ordered) {  // ordered results: the caller writes
+    *tsel = make_uint2((uint32_t)(Ts + 0x8000), cgt);
+    return SEL_DONE;
   }
   emit_entries<MODE, true, true>(e, cnt, Ts, cgt, k - cgt,
                                  reinterpret_cast<unsigned long long*>(bc + BC_SLOT), o, lpages,
@@ -909,7 +927,94 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 // ============================================ one workgroup per row
 // Rows whose valid vectors fit NT * VPT: the whole row sits in VGPRs.
 
-template <int MODE, int NT, int VPT, bool ONE>
+// ------------------------------------------------------- ordered results
+// The ordered write pass (vLLM kimi_k3 indexer, IndexerSelect: the selected
+// keys in key order, that is by element index, with the ties at the
+// threshold going to the lowest indices; -1 past the count; the logical
+// indices alongside).  Given the k-th key T, the count cgt of keys above it
+// and take = k - cgt, an element is selected when its key is above T, or
+// equal to T with fewer than `take` equal keys before it; its output slot
+// is the number of selected elements before it.  The workgroup walks
+// vectors [vb, ve) of the row in order, NT at a time: per vector the counts
+// of keys above and equal to T (packed 16 | 16 bits), a wave scan and the
+// waves' totals give every element its slot.  na and nt enter as the
+// counts of keys above and equal to T before vb; the walk stops once all k
+// slots are taken.  tmp: 2 NT/64 LDS words, free when called.
+template <int MODE, int NT>
+__device__ void ordered_span(const uint4* src, int vb, int ve, int v, int n, uint32_t T,
+                             uint32_t cgt, uint32_t na, uint32_t nt, const Out o,
+                             const int32_t* lpages, int32_t* ids, uint32_t* tmp,
+                             int tid = (int)threadIdx.x) {
+  constexpr int NW = NT / 64;
+  constexpr int EPV = MODE == TOPK_MODE_BLOCK ? 1 : 8;  // elements per vector
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t take = o.k - cgt;
+  int it = 0;
+  for (int c0 = vb; c0 < ve; c0 += NT, ++it) {
+    if (na >= cgt && nt >= take) break;  // every slot taken (uniform)
+    const int vid = c0 + tid;
+    uint32_t ga = 0, te = 0, kk[EPV];
+    if (vid < ve) {
+      const uint4 raw = ld_vec(src, (uint32_t)vid);
+      if constexpr (MODE == TOPK_MODE_BLOCK) {
+        kk[0] = vid == n - 1 ? kKeyPosInf : block_key4(raw);
+        ga = kk[0] > T;
+        te = kk[0] == T;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kk[e] = key1(half_of(word_of(raw, e >> 1), e & 1));
+          const bool ok = vid * 8 + e < v;
+          ga |= (uint32_t)(ok && kk[e] > T) << e;
+          te |= (uint32_t)(ok && kk[e] == T) << e;
+        }
+      }
+    }
+    const uint32_t cnt = ((uint32_t)__builtin_popcount(ga) << 16) | (uint32_t)__builtin_popcount(te);
+    const uint32_t incl = wave_incl_scan(cnt);
+    uint32_t* t = tmp + (it & 1) * NW;  // two sets: one barrier per round
+    if (lane == 63) t[wave] = incl;
+    __syncthreads();
+    uint32_t before = incl - cnt, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = t[w];
+      before += w < wave ? x : 0u;
+      tot += x;
+    }
+    uint32_t pa = na + (before >> 16), pt = nt + (before & 0xFFFFu);
+    if (ga | te) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const bool a = (ga >> e) & 1u, q = (te >> e) & 1u;
+        uint32_t pos = 0xFFFFFFFFu;
+        if (a) pos = pa + min(pt, take);
+        else if (q && pt < take) pos = pa + pt;
+        pa += a;
+        pt += q;
+        if (pos < o.k) {
+          const int32_t idx = MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + e;
+          o.out[pos] = (MODE == TOPK_MODE_BLOCK && kk[e] == kKeyNegInf) ? -1
+                                                                        : map_out(o, lpages, idx);
+          if (ids) ids[pos] = idx;
+        }
+      }
+    }
+    na += tot >> 16;
+    nt += tot & 0xFFFFu;
+  }
+}
+
+// Ordered results of a row with n <= k: the logical ids 0..n-1, then -1,
+// and the count (the output itself is written by write_short_*).
+template <int NT>
+__device__ void short_ids(const Params& p, int row, int n, int tid = (int)threadIdx.x) {
+  if (p.ids)
+    for (int e = tid; e < p.k; e += NT) p.ids[(int64_t)row * p.k + e] = e < n ? e : -1;
+  if (p.valid && tid == 0) p.valid[row] = n;
+}
+
+template <int MODE, int NT, int VPT, bool ONE, bool ORD>
 __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   constexpr int NW = NT / 64;
   extern __shared__ uint32_t smem[];
@@ -927,17 +1032,22 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   uint32_t* rel = smem + kRelHist;
   uint32_t* bc = smem + kBc;
   uint32_t* lists = smem + kLists;
-  int32_t* lpages =
-      (p.page_lds && o.pages) ? reinterpret_cast<int32_t*>(smem + p.page_lds) : nullptr;
+  // the LDS copy of the row's block-table entries (made by the sampled
+  // path, so not when the direct path is forced)
+  int32_t* lpages = (p.page_lds && o.pages && !p.force_direct)
+                        ? reinterpret_cast<int32_t*>(smem + p.page_lds)
+                        : nullptr;
 
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
     else write_short_token<NT>(o, n, k);
+    if constexpr (ORD) short_ids<NT>(p, row, n);
     set_path(p, row, TOPK_PATH_SHORT);
     return;
   }
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
+  uint2 tc = make_uint2(0u, 0u);  // ordered results: the k-th key, the count above it
   if (!direct) {
     const int nvec = (v + 7) >> 3;
     const int jt = (nvec - 1) / NT;   // last vector slot holding row data
@@ -1068,7 +1178,8 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       // exact select over the survivors; its histogram barrier also publishes
       // the entry counts (overflow) and the count of keys above the cutoff
       const int st = select_and_write<MODE, NW, ONE>(seg, min(wcnt, cap), cs, (uint32_t)k, rel,
-                                                     sh, bc, cap, o, lpages);
+                                                     sh, bc, cap, o, lpages,
+                                                     ORD, ORD ? &tc : nullptr);
       if (st == SEL_OVERFLOW) {
         direct = true;
         code = TOPK_PATH_DIRECT_OVERFLOW;
@@ -1110,9 +1221,13 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
           direct = true;
           code = TOPK_PATH_DIRECT_MISJUDGED;
         } else {
-          write_above<MODE>(seg, wcnt, cs, before, o);
-          const uint32_t take = (uint32_t)k - gt_total;
-          for (uint32_t i = tid; i < take; i += NT) o.put(gt_total + i, ties[i], c);
+          if constexpr (ORD) {
+            tc = make_uint2(c, gt_total);
+          } else {
+            write_above<MODE>(seg, wcnt, cs, before, o);
+            const uint32_t take = (uint32_t)k - gt_total;
+            for (uint32_t i = tid; i < take; i += NT) o.put(gt_total + i, ties[i], c);
+          }
           code = TOPK_PATH_SAMPLED_TIES;
         }
       }
@@ -1120,7 +1235,13 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE, NT>(src, v, n, k, o, lists, bc);
+    direct_select<MODE, NT>(src, v, n, k, o, lists, bc, ORD, ORD ? &tc : nullptr);
+  }
+  if constexpr (ORD) {
+    __syncthreads();  // the pass's LDS words are free
+    ordered_span<MODE, NT>(src, 0, (v + 7) >> 3, v, n, tc.x, tc.y, 0u, 0u, o, lpages,
+                           p.ids ? p.ids + (int64_t)row * k : nullptr, bc + BC_TMP);
+    if (p.valid && tid == 0) p.valid[row] = k;
   }
   set_path(p, row, code);
 }
@@ -1340,7 +1461,7 @@ constexpr int kSelFixed = kLists + kSelStage;  // words before the staged entrie
 // loaded together with the headers), checks that the cutoff held, and
 // writes the row: exact select over the survivors, the tie pass, or the
 // direct path.
-template <int MODE>
+template <int MODE, bool ORD>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
   extern __shared__ uint32_t smem[];
@@ -1409,11 +1530,16 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
     else write_short_token<NT>(o, n, k);
+    if constexpr (ORD) {
+      short_ids<NT>(p, row, n);
+      if (tid == 0) p.ord_rec[2 * lrow] = 0xFFFFFFFFu;  // written: the order kernels skip it
+    }
     set_path(p, row, TOPK_PATH_SHORT);
     return;
   }
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
+  uint2 tc = make_uint2(0u, 0u);  // ordered results: the k-th key, the count above it
   if (!direct && (rflags & kFlagDirect)) {
     direct = true;
     code = TOPK_PATH_DIRECT_MISJUDGED;
@@ -1551,8 +1677,11 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
       if (sampled) {
         select_and_write<MODE, NW, true>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
-                                         0xFFFFFFFFu, o, nullptr);
+                                         0xFFFFFFFFu, o, nullptr, ORD, ORD ? &tc : nullptr);
         code = TOPK_PATH_SAMPLED;
+      } else if (ORD) {
+        tc = make_uint2(c, gt_total);
+        code = TOPK_PATH_SAMPLED_TIES;
       } else {
         // the k-th key is the cutoff: every key above it, then the first ties
         const uint32_t take = (uint32_t)k - gt_total;
@@ -1569,9 +1698,93 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE, NT>(src, v, n, k, o, smem + kLists, bc);
+    direct_select<MODE, NT>(src, v, n, k, o, smem + kLists, bc, ORD, ORD ? &tc : nullptr);
+  }
+  if (ORD && tid == 0) {
+    p.ord_rec[2 * lrow] = tc.x;
+    p.ord_rec[2 * lrow + 1] = tc.y;
+    if (p.valid) p.valid[row] = k;
   }
   set_path(p, row, code);
+}
+
+// Ordered results of team rows: every row is cut into spans of
+// p.ord_span vectors, one workgroup (member) each.  The count kernel gives
+// each member's keys above and equal to the row's T (recorded by the
+// select kernel), the write kernel each member's ordered slots from the
+// counts of the members before it.
+constexpr int kOrdNT = 256;
+constexpr int kOrdVPT = 8;  // vectors per thread of one member's span
+
+template <int MODE>
+__global__ __launch_bounds__(kOrdNT) void topk_order_count(Params p) {
+  __shared__ uint32_t tmp[kOrdNT / 64];
+  const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
+  const int row = p.row0 + lrow;
+  const int tid = threadIdx.x;
+  const uint32_t T = p.ord_rec[2 * lrow];
+  if (T > 0xFFFFu) return;  // a short row, written by the select kernel
+  const int v = clamp_len(p.valid_len[row], p.width);
+  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
+  const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
+  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  uint32_t na = 0, nt = 0;
+  for (int vid = vb + tid; vid < ve; vid += kOrdNT) {
+    const uint4 raw = ld_vec(src, (uint32_t)vid);
+    if constexpr (MODE == TOPK_MODE_BLOCK) {
+      const uint32_t key = vid == n - 1 ? kKeyPosInf : block_key4(raw);
+      na += key > T;
+      nt += key == T;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t key = key1(half_of(word_of(raw, e >> 1), e & 1));
+        const bool ok = vid * 8 + e < v;
+        na += ok && key > T;
+        nt += ok && key == T;
+      }
+    }
+  }
+  // a span holds at most kOrdNT kOrdVPT 8 < 2^16 elements
+  const uint32_t t = block_sum<kOrdNT>((na << 16) | nt, tmp, tid);
+  if (tid == 0) p.ord_cnt[(size_t)lrow * p.ord_G + member] = t;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
+  __shared__ uint32_t tmp[2 * (kOrdNT / 64) + 2];
+  const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
+  const int row = p.row0 + lrow;
+  const int tid = threadIdx.x;
+  const uint32_t T = p.ord_rec[2 * lrow];
+  if (T > 0xFFFFu) return;  // a short row, written by the select kernel
+  const uint32_t cgt = p.ord_rec[2 * lrow + 1];
+  const int v = clamp_len(p.valid_len[row], p.width);
+  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
+  const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
+  if (vb >= ve) return;
+  // keys above and equal to T in the members before this one
+  if (tid < 64) {
+    uint32_t a = 0, e = 0;
+    for (int m = tid; m < member; m += 64) {
+      const uint32_t x = p.ord_cnt[(size_t)lrow * p.ord_G + m];
+      a += x >> 16;
+      e += x & 0xFFFFu;
+    }
+    a = readlane(wave_incl_scan(a), 63);
+    e = readlane(wave_incl_scan(e), 63);
+    if (tid == 0) {
+      tmp[2 * (kOrdNT / 64)] = a;
+      tmp[2 * (kOrdNT / 64) + 1] = e;
+    }
+  }
+  __syncthreads();
+  const uint32_t na = tmp[2 * (kOrdNT / 64)], nt = tmp[2 * (kOrdNT / 64) + 1];
+  __syncthreads();  // the pass reuses the first words
+  const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
+  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  ordered_span<MODE, kOrdNT>(src, vb, ve, v, n, T, cgt, na, nt, o, nullptr,
+                             p.ids ? p.ids + (int64_t)row * p.k : nullptr, tmp);
 }
 
 // ================================================================= host
@@ -1696,9 +1909,27 @@ int launch(K kernel, int grid, int nt, size_t lds, hipStream_t stream, const Par
   return TOPK_OK;
 }
 
+// One workgroup per row: the latency variant while every row's workgroup
+// is resident at once, else the throughput variant.
+template <bool ORD>
+int launch_rows(int mode, int rows, size_t lds, hipStream_t stream, const Params& p) {
+  if (mode == TOPK_MODE_BLOCK) {
+    auto lat = topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, false, ORD>;
+    if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
+      return launch(lat, rows, kRowNT, lds, stream, p);
+    return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, true, ORD>, rows, kRowNT,
+                  lds, stream, p);
+  }
+  auto lat = topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, false, ORD>;
+  if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
+    return launch(lat, rows, kRowNT, lds, stream, p);
+  return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, true, ORD>, rows, kRowNT,
+                lds, stream, p);
+}
+
 int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, int32_t rows,
         int32_t width, int32_t k, int32_t mode, const topk_block_table_t* bt, int32_t* out,
-        const topk_options_t* opt, void* stream_ptr) {
+        const topk_options_t* opt, int ord, int32_t* valid, int32_t* ids, void* stream_ptr) {
   g_err[0] = '\0';
   if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, TOPK_MAX_K);
@@ -1711,8 +1942,9 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   if (rows == 0) return TOPK_OK;
   if (!logits || !valid_len || !out) return fail(TOPK_ERR_INVALID_ARG, "null pointer");
   if (((uintptr_t)logits & 15u) != 0) return fail(TOPK_ERR_MISALIGNED, "logits not 16-byte aligned");
-  if (((uintptr_t)out & 3u) != 0 || ((uintptr_t)valid_len & 3u) != 0)
-    return fail(TOPK_ERR_MISALIGNED, "out or valid_len not 4-byte aligned");
+  if (((uintptr_t)out & 3u) != 0 || ((uintptr_t)valid_len & 3u) != 0 ||
+      ((uintptr_t)valid & 3u) != 0 || ((uintptr_t)ids & 3u) != 0)
+    return fail(TOPK_ERR_MISALIGNED, "out, valid_len, valid or ids not 4-byte aligned");
   int page_shift = 0;
   if (bt) {
     if (!bt->pages) return fail(TOPK_ERR_INVALID_ARG, "block table without pages");
@@ -1738,6 +1970,9 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.out = out;
   p.path = opt ? opt->path_codes : nullptr;
   p.force_direct = opt ? (opt->force_direct != 0) : 0;
+  p.ord = ord;
+  p.valid = ord ? valid : nullptr;
+  p.ids = ord ? ids : nullptr;
 
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
@@ -1758,18 +1993,8 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     // of that search cost issue slots that other rows' waves could use);
     // otherwise every wave searches for itself, one barrier fewer on the
     // row's path
-    if (mode == TOPK_MODE_BLOCK) {
-      auto lat = topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, false>;
-      if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
-        return launch(lat, rows, kRowNT, lds, stream, p);
-      return launch(topk_rows_wg<TOPK_MODE_BLOCK, kRowNT, kRowBlockVPT, true>, rows, kRowNT, lds,
-                    stream, p);
-    }
-    auto lat = topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, false>;
-    if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
-      return launch(lat, rows, kRowNT, lds, stream, p);
-    return launch(topk_rows_wg<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, true>, rows, kRowNT, lds,
-                  stream, p);
+    if (ord) return launch_rows<true>(mode, rows, lds, stream, p);
+    return launch_rows<false>(mode, rows, lds, stream, p);
   }
 
   // team path: G members per row (filter kernel), then one workgroup per
@@ -1782,12 +2007,21 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
   if ((size_t)batch * row_bytes > kTeamScratchMax) batch = (int)(kTeamScratchMax / row_bytes);
   batch = batch < 8 ? 8 : batch / 8 * 8;  // whole groups of 8 rows (one per XCD)
+  // ordered results: per row its threshold record and one count per
+  // order-pass member, after the slices
+  const int ord_span = kOrdNT * kOrdVPT;
+  const int ord_G = (nvec_max + ord_span - 1) / ord_span;
+  const size_t ord_bytes = ord ? (size_t)batch * (2 + ord_G) * 4 : 0;
   void* scratch = nullptr;
-  int rc = get_scratch(stream, (size_t)batch * row_bytes, &scratch);
+  int rc = get_scratch(stream, (size_t)batch * row_bytes + ord_bytes, &scratch);
   if (rc != TOPK_OK) return rc;
   p.G = G;
   p.team_cv = cv;
   p.team_slices = static_cast<uint32_t*>(scratch);
+  p.ord_G = ord_G;
+  p.ord_span = ord_span;
+  p.ord_rec = p.team_slices + (size_t)batch * row_bytes / 4;
+  p.ord_cnt = p.ord_rec + 2 * (size_t)batch;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
   // stage as many survivor entries as the LDS of one workgroup holds
@@ -1809,9 +2043,22 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
       rc = launch(topk_team_filter<TOPK_MODE_TOKEN, 8, kTokenSV>, grid, kTeamNT, 0, stream, p);
     if (rc == TOPK_OK) {
       if (mode == TOPK_MODE_BLOCK)
-        rc = launch(topk_team_select<TOPK_MODE_BLOCK>, nr, kSelNT, sel_lds, stream, p);
+        rc = ord ? launch(topk_team_select<TOPK_MODE_BLOCK, true>, nr, kSelNT, sel_lds, stream, p)
+                 : launch(topk_team_select<TOPK_MODE_BLOCK, false>, nr, kSelNT, sel_lds, stream, p);
       else
-        rc = launch(topk_team_select<TOPK_MODE_TOKEN>, nr, kSelNT, sel_lds, stream, p);
+        rc = ord ? launch(topk_team_select<TOPK_MODE_TOKEN, true>, nr, kSelNT, sel_lds, stream, p)
+                 : launch(topk_team_select<TOPK_MODE_TOKEN, false>, nr, kSelNT, sel_lds, stream, p);
+    }
+    if (rc == TOPK_OK && ord) {
+      if (mode == TOPK_MODE_BLOCK) {
+        rc = launch(topk_order_count<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
+        if (rc == TOPK_OK)
+          rc = launch(topk_order_write<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
+      } else {
+        rc = launch(topk_order_count<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
+        if (rc == TOPK_OK)
+          rc = launch(topk_order_write<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
+      }
     }
     if (rc != TOPK_OK) return rc;
   }
@@ -1825,16 +2072,33 @@ extern "C" {
 int topk_bf16_rows(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
                    int32_t rows, int32_t width, int32_t k, int32_t mode,
                    const topk_block_table_t* block_table, int32_t* out, void* stream) {
-  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr,
-             stream);
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr, 0,
+             nullptr, nullptr, stream);
 }
 
 int topk_bf16_rows_ex(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
                       int32_t rows, int32_t width, int32_t k, int32_t mode,
                       const topk_block_table_t* block_table, int32_t* out,
                       const topk_options_t* options, void* stream) {
-  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, options,
-             stream);
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, options, 0,
+             nullptr, nullptr, stream);
+}
+
+int topk_bf16_rows_ordered(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
+                           int32_t rows, int32_t width, int32_t k, int32_t mode,
+                           const topk_block_table_t* block_table, int32_t* out, int32_t* valid,
+                           int32_t* ids, void* stream) {
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr, 1,
+             valid, ids, stream);
+}
+
+int topk_bf16_rows_ordered_ex(const uint16_t* logits, int64_t row_stride,
+                              const int32_t* valid_len, int32_t rows, int32_t width, int32_t k,
+                              int32_t mode, const topk_block_table_t* block_table, int32_t* out,
+                              int32_t* valid, int32_t* ids, const topk_options_t* options,
+                              void* stream) {
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, options, 1,
+             valid, ids, stream);
 }
 
 const char* topk_status_string(int status) {

@@ -133,6 +133,39 @@ int topk_bf16_rows_ex(const uint16_t *logits, int64_t row_stride,
                       const topk_block_table_t *block_table, int32_t *out,
                       const topk_options_t *options, void *stream);
 
+/* Deterministic ordered top-k of every row (vLLM API page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.indexer",
+ * IndexerSelect: the selected keys in key order with -1 past the row's
+ * count, the counts in `valid`, the logical key indices in `ids`).  The
+ * selection is that of topk_bf16_rows with the ties at the k-th key taken
+ * from the lowest element indices, which makes the result unique:
+ *   ids[r, 0:c]  the selected element indices in ascending order, c =
+ *                min(n, k), then -1 up to k (for n <= k: 0..n-1, then -1);
+ *   out[r, j]    ids[r, j] through the block table when one is given; -1
+ *                where ids[r, j] is -1 and, in block mode, where the
+ *                element is a -inf block;
+ *   valid[r]     c.
+ * Arguments as for topk_bf16_rows, plus
+ *   valid        device int32 [rows], or NULL (not written)
+ *   ids          device int32 [rows, k], or NULL (not written)
+ * Costs over topk_bf16_rows: one more read of each row (rows up to 16384
+ * tokens or 4096 blocks, mostly from L2), or two (wider rows, which also
+ * take two more kernel launches).  Returns TOPK_OK or a negative
+ * topk_status; asynchronous like topk_bf16_rows. */
+int topk_bf16_rows_ordered(const uint16_t *logits, int64_t row_stride,
+                           const int32_t *valid_len, int32_t rows, int32_t width,
+                           int32_t k, int32_t mode,
+                           const topk_block_table_t *block_table, int32_t *out,
+                           int32_t *valid, int32_t *ids, void *stream);
+
+/* topk_bf16_rows_ordered with test and diagnosis options (NULL = none). */
+int topk_bf16_rows_ordered_ex(const uint16_t *logits, int64_t row_stride,
+                              const int32_t *valid_len, int32_t rows,
+                              int32_t width, int32_t k, int32_t mode,
+                              const topk_block_table_t *block_table,
+                              int32_t *out, int32_t *valid, int32_t *ids,
+                              const topk_options_t *options, void *stream);
+
 /* A static string naming a status code. */
 const char *topk_status_string(int status);
 

@@ -5,7 +5,8 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 (``exact_row_wise_amd``) never imports it and shares no code with it.
 
 The arithmetic lives in ``topk_oracle.c`` (plain C: per row, element keys,
-a full ``qsort`` by (key desc, index asc), the first k).  This package only
+a full ``qsort`` by (key desc, index asc), the first k; the ordered result
+sorts those k by index).  This package only
 compiles it with gcc and marshals numpy arrays.
 """
 from .oracle import (  # noqa: F401
@@ -23,5 +24,6 @@ from .oracle import (  # noqa: F401
     threshold,
     topk_row,
     topk,
+    topk_ordered,
     lib_path,
 )
