@@ -940,6 +940,21 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 // waves' totals give every element its slot.  na and nt enter as the
 // counts of keys above and equal to T before vb; the walk stops once all k
 // slots are taken.  tmp: 2 NT/64 LDS words, free when called.
+// A thread's selected elements take consecutive slots: with pa keys above
+// T and pt keys equal to T before its first element, its first slot is
+// pa + min(pt, take), and it keeps its keys above T and its first
+// take - pt keys equal to T (ga, te: bit e for element e).  Returns that
+// mask; `first` receives the first slot.
+__device__ __forceinline__ uint32_t ordered_mask(uint32_t ga, uint32_t te, uint32_t pa,
+                                                 uint32_t pt, uint32_t take, uint32_t& first) {
+  first = pa + min(pt, take);
+  const uint32_t room = pt < take ? take - pt : 0u;
+  uint32_t tk = te;
+  for (uint32_t c = (uint32_t)__builtin_popcount(te); c > room; --c)
+    tk &= ~(1u << (31 - __builtin_clz(tk)));  // drop the last tie
+  return ga | tk;
+}
+
 template <int MODE, int NT>
 __device__ void ordered_span(const uint4* src, int vb, int ve, int v, int n, uint32_t T,
                              uint32_t cgt, uint32_t na, uint32_t nt, const Out o,
@@ -982,26 +997,98 @@ __device__ void ordered_span(const uint4* src, int vb, int ve, int v, int n, uin
       before += w < wave ? x : 0u;
       tot += x;
     }
-    uint32_t pa = na + (before >> 16), pt = nt + (before & 0xFFFFu);
     if (ga | te) {
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const bool a = (ga >> e) & 1u, q = (te >> e) & 1u;
-        uint32_t pos = 0xFFFFFFFFu;
-        if (a) pos = pa + min(pt, take);
-        else if (q && pt < take) pos = pa + pt;
-        pa += a;
-        pt += q;
-        if (pos < o.k) {
-          const int32_t idx = MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + e;
-          o.out[pos] = (MODE == TOPK_MODE_BLOCK && kk[e] == kKeyNegInf) ? -1
-                                                                        : map_out(o, lpages, idx);
-          if (ids) ids[pos] = idx;
-        }
+      uint32_t pos;
+      uint32_t m = ordered_mask(ga, te, na + (before >> 16), nt + (before & 0xFFFFu), take, pos);
+      for (; m && pos < o.k; m &= m - 1, ++pos) {
+        const int e = __builtin_ctz(m);
+        const int32_t idx = MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + e;
+        o.out[pos] = (MODE == TOPK_MODE_BLOCK && kk[MODE == TOPK_MODE_BLOCK ? 0 : e] == kKeyNegInf)
+                         ? -1
+                         : map_out(o, lpages, idx);
+        if (ids) ids[pos] = idx;
       }
     }
     na += tot >> 16;
     nt += tot & 0xFFFFu;
+  }
+}
+
+// The ordered write pass over a row staged in registers (slot j of a
+// thread holds vector slot_vid(j): slots in order, and within a slot waves
+// and lanes in order, follow the element order).  As ordered_span, with
+// every slot's counts scanned before one barrier.  kb: block keys (block
+// mode).  tmp: VPT NT/64 LDS words, free when called.
+template <int MODE, int NT, int VPT, int KB>
+__device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], int jt, int rem,
+                             int v, uint32_t T, uint32_t cgt, const Out o,
+                             const int32_t* lpages, int32_t* ids, uint32_t* tmp,
+                             uint32_t* stage, int tid = (int)threadIdx.x) {
+  constexpr int NW = NT / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint32_t take = o.k - cgt;
+  uint32_t ga[VPT], te[VPT], ex[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    const int vid = slot_vid<NT>(j, jt, rem, tid);
+    ga[j] = 0;
+    te[j] = 0;
+    if (vid >= 0) {
+      if constexpr (MODE == TOPK_MODE_BLOCK) {
+        ga[j] = kb[j] > T;
+        te[j] = kb[j] == T;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t key = key1(half_of(word_of(raw[j], e >> 1), e & 1));
+          const bool ok = vid * 8 + e < v;
+          ga[j] |= (uint32_t)(ok && key > T) << e;
+          te[j] |= (uint32_t)(ok && key == T) << e;
+        }
+      }
+    }
+    // a row holds at most 2^15 elements: 16-bit counts
+    const uint32_t c = ((uint32_t)__builtin_popcount(ga[j]) << 16) |
+                       (uint32_t)__builtin_popcount(te[j]);
+    const uint32_t incl = wave_incl_scan(c);
+    ex[j] = incl - c;
+    if (lane == 63) tmp[j * NW + wave] = incl;
+  }
+  __syncthreads();
+  uint32_t base = 0;  // counts of the slots before j
+#pragma unroll
+  for (int j = 0; j < VPT; ++j) {
+    uint32_t before = base + ex[j], tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t x = tmp[j * NW + w];
+      before += w < wave ? x : 0u;
+      tot += x;
+    }
+    base += tot;
+    if (ga[j] | te[j]) {
+      // the slots' element indices (bit 31: a -inf block) go to LDS first
+      const int vid = slot_vid<NT>(j, jt, rem, tid);
+      const uint32_t neg =
+          (MODE == TOPK_MODE_BLOCK && kb[MODE == TOPK_MODE_BLOCK ? j : 0] == kKeyNegInf)
+              ? 0x80000000u
+              : 0u;
+      uint32_t pos;
+      uint32_t m = ordered_mask(ga[j], te[j], before >> 16, before & 0xFFFFu, take, pos);
+      for (; m && pos < o.k; m &= m - 1, ++pos)
+        stage[pos] = (uint32_t)(MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + __builtin_ctz(m)) | neg;
+    }
+  }
+  // then the whole rows, in runs (every slot below k is taken: cgt keys
+  // above T and take keys equal to it; an index past the row's elements,
+  // which would mean a slot left untaken, is never mapped)
+  __syncthreads();
+  const int n = MODE == TOPK_MODE_BLOCK ? (v + 7) >> 3 : v;
+  for (uint32_t i = tid; i < o.k; i += NT) {
+    const uint32_t x = stage[i];
+    const int32_t idx = (int32_t)(x & 0x7FFFFFFFu);
+    o.out[i] = ((x >> 31) || idx >= n) ? -1 : map_out(o, lpages, idx);
+    if (ids) ids[i] = idx;
   }
 }
 
@@ -1048,10 +1135,12 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
   uint2 tc = make_uint2(0u, 0u);  // ordered results: the k-th key, the count above it
+  const int nvec = (v + 7) >> 3;
+  const int jt = (nvec - 1) / NT;   // last vector slot holding row data
+  const int rem = nvec - jt * NT;   // vectors in it
+  uint4 raw[VPT];                   // the staged row
+  uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];  // its block keys (block mode)
   if (!direct) {
-    const int nvec = (v + 7) >> 3;
-    const int jt = (nvec - 1) / NT;   // last vector slot holding row data
-    const int rem = nvec - jt * NT;   // vectors in it
     // zero the sample and relative histograms and the replicated sample bins
     const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
@@ -1067,7 +1156,6 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     // -- stage the row: 16-byte loads into VGPRs.  Every lane loads (a lane
     // without a vector in slot jt reads vector 0 and poisons it below; the
     // slots past jt are never used), so that no load sits under a branch.
-    uint4 raw[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j)
       raw[j] = ld_vec(src, (uint32_t)max(slot_vid<NT>(j, jt, rem), 0));
@@ -1085,7 +1173,6 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     constexpr int SE = (MODE == TOPK_MODE_TOKEN || VPT * NT <= 2048) ? 1 : VPT * NT / 2048;
     constexpr int NSK = VPT / SE;
     uint32_t sk[NSK];
-    uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
     uint32_t S = 0;  // samples over the workgroup
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -1238,9 +1325,18 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
     direct_select<MODE, NT>(src, v, n, k, o, lists, bc, ORD, ORD ? &tc : nullptr);
   }
   if constexpr (ORD) {
+    if (p.force_direct) {  // the sampled path did not stage the row
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) {
+        const int vid = slot_vid<NT>(j, jt, rem);
+        raw[j] = ld_vec(src, (uint32_t)max(vid, 0));
+        if constexpr (MODE == TOPK_MODE_BLOCK)
+          kb[j] = vid >= 0 ? (vid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
+      }
+    }
     __syncthreads();  // the pass's LDS words are free
-    ordered_span<MODE, NT>(src, 0, (v + 7) >> 3, v, n, tc.x, tc.y, 0u, 0u, o, lpages,
-                           p.ids ? p.ids + (int64_t)row * k : nullptr, bc + BC_TMP);
+    ordered_regs<MODE, NT, VPT>(raw, kb, jt, rem, v, tc.x, tc.y, o, lpages,
+                                p.ids ? p.ids + (int64_t)row * k : nullptr, sh, lists);
     if (p.valid && tid == 0) p.valid[row] = k;
   }
   set_path(p, row, code);
