@@ -64,6 +64,9 @@ constexpr int kCopyStride = 260;         // words between the copies of a replic
 constexpr int kSampBins = kCopies * kCopyStride;  // words of the replicated sample bins
 constexpr int kTeamNT = 256;             // filter workgroup size
 constexpr int kSelNT = 1024;             // select workgroup size
+constexpr int kOrdNT = 256;              // ordered results of team rows: threads of a member
+constexpr int kOrdVPT = 8;               // vectors per thread of its span (2048 vectors)
+constexpr uint32_t kOrdCounted = 0x10000u;  // record flag: the select kernel counted the spans
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
@@ -1775,6 +1778,29 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         select_and_write<MODE, NW, true>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
                                          0xFFFFFFFFu, o, nullptr, ORD, ORD ? &tc : nullptr);
         code = TOPK_PATH_SAMPLED;
+        if constexpr (ORD) {
+          // T is above the cutoff, so every key at or above T is staged:
+          // count each order span's keys above and equal to T here (16 | 16
+          // bits), which spares the count kernel a read of the row
+          static_assert(kOrdNT * kOrdVPT == 2048, "spans of 2^11 vectors");
+          constexpr int kSpanShift = MODE == TOPK_MODE_BLOCK ? 11 : 14;  // element -> span
+          __syncthreads();  // the select's last reads of sh are done
+          for (int i = tid; i < p.ord_G; i += NT) sh[i] = 0;
+          __syncthreads();
+          for (uint32_t i = tid; i < E; i += NT) {
+            const uint2 x = *reinterpret_cast<const uint2*>(ent + 2 * i);
+            const uint32_t k0 = (uint32_t)(lo16s(x.x) + 0x8000);
+            uint32_t cnt = (k0 > tc.x ? 0x10000u : 0u) + (k0 == tc.x ? 1u : 0u);
+            if constexpr (MODE == TOPK_MODE_TOKEN) {  // block entries: the high half is dead
+              const uint32_t k1 = (uint32_t)(hi16s(x.x) + 0x8000);
+              cnt += (k1 > tc.x ? 0x10000u : 0u) + (k1 == tc.x ? 1u : 0u);
+            }
+            if (cnt) atomicAdd(&sh[x.y >> kSpanShift], cnt);
+          }
+          __syncthreads();
+          for (int i = tid; i < p.ord_G; i += NT) p.ord_cnt[(size_t)lrow * p.ord_G + i] = sh[i];
+          tc.x |= kOrdCounted;
+        }
       } else if (ORD) {
         tc = make_uint2(c, gt_total);
         code = TOPK_PATH_SAMPLED_TIES;
@@ -1809,8 +1835,6 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
 // each member's keys above and equal to the row's T (recorded by the
 // select kernel), the write kernel each member's ordered slots from the
 // counts of the members before it.
-constexpr int kOrdNT = 256;
-constexpr int kOrdVPT = 8;  // vectors per thread of one member's span
 
 template <int MODE>
 __global__ __launch_bounds__(kOrdNT) void topk_order_count(Params p) {
@@ -1819,7 +1843,7 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_count(Params p) {
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
   const uint32_t T = p.ord_rec[2 * lrow];
-  if (T > 0xFFFFu) return;  // a short row, written by the select kernel
+  if (T > 0xFFFFu) return;  // a short row, or spans counted by the select kernel
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
   const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
@@ -1852,8 +1876,9 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
   const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
-  const uint32_t T = p.ord_rec[2 * lrow];
-  if (T > 0xFFFFu) return;  // a short row, written by the select kernel
+  const uint32_t rec = p.ord_rec[2 * lrow];
+  if (rec == 0xFFFFFFFFu) return;  // a short row, written by the select kernel
+  const uint32_t T = rec & 0xFFFFu;
   const uint32_t cgt = p.ord_rec[2 * lrow + 1];
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
