@@ -937,12 +937,8 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 // indices alongside).  Given the k-th key T, the count cgt of keys above it
 // and take = k - cgt, an element is selected when its key is above T, or
 // equal to T with fewer than `take` equal keys before it; its output slot
-// is the number of selected elements before it.  The workgroup walks
-// vectors [vb, ve) of the row in order, NT at a time: per vector the counts
-// of keys above and equal to T (packed 16 | 16 bits), a wave scan and the
-// waves' totals give every element its slot.  na and nt enter as the
-// counts of keys above and equal to T before vb; the walk stops once all k
-// slots are taken.  tmp: 2 NT/64 LDS words, free when called.
+// is the number of selected elements before it.
+
 // A thread's selected elements take consecutive slots: with pa keys above
 // T and pt keys equal to T before its first element, its first slot is
 // pa + min(pt, take), and it keeps its keys above T and its first
@@ -958,85 +954,34 @@ __device__ __forceinline__ uint32_t ordered_mask(uint32_t ga, uint32_t te, uint3
   return ga | tk;
 }
 
-template <int MODE, int NT>
-__device__ void ordered_span(const uint4* src, int vb, int ve, int v, int n, uint32_t T,
-                             uint32_t cgt, uint32_t na, uint32_t nt, const Out o,
-                             const int32_t* lpages, int32_t* ids, uint32_t* tmp,
-                             int tid = (int)threadIdx.x) {
-  constexpr int NW = NT / 64;
-  constexpr int EPV = MODE == TOPK_MODE_BLOCK ? 1 : 8;  // elements per vector
-  const int lane = tid & 63, wave = tid >> 6;
-  const uint32_t take = o.k - cgt;
-  int it = 0;
-  for (int c0 = vb; c0 < ve; c0 += NT, ++it) {
-    if (na >= cgt && nt >= take) break;  // every slot taken (uniform)
-    const int vid = c0 + tid;
-    uint32_t ga = 0, te = 0, kk[EPV];
-    if (vid < ve) {
-      const uint4 raw = ld_vec(src, (uint32_t)vid);
-      if constexpr (MODE == TOPK_MODE_BLOCK) {
-        kk[0] = vid == n - 1 ? kKeyPosInf : block_key4(raw);
-        ga = kk[0] > T;
-        te = kk[0] == T;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kk[e] = key1(half_of(word_of(raw, e >> 1), e & 1));
-          const bool ok = vid * 8 + e < v;
-          ga |= (uint32_t)(ok && kk[e] > T) << e;
-          te |= (uint32_t)(ok && kk[e] == T) << e;
-        }
-      }
-    }
-    const uint32_t cnt = ((uint32_t)__builtin_popcount(ga) << 16) | (uint32_t)__builtin_popcount(te);
-    const uint32_t incl = wave_incl_scan(cnt);
-    uint32_t* t = tmp + (it & 1) * NW;  // two sets: one barrier per round
-    if (lane == 63) t[wave] = incl;
-    __syncthreads();
-    uint32_t before = incl - cnt, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t x = t[w];
-      before += w < wave ? x : 0u;
-      tot += x;
-    }
-    if (ga | te) {
-      uint32_t pos;
-      uint32_t m = ordered_mask(ga, te, na + (before >> 16), nt + (before & 0xFFFFu), take, pos);
-      for (; m && pos < o.k; m &= m - 1, ++pos) {
-        const int e = __builtin_ctz(m);
-        const int32_t idx = MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + e;
-        o.out[pos] = (MODE == TOPK_MODE_BLOCK && kk[MODE == TOPK_MODE_BLOCK ? 0 : e] == kKeyNegInf)
-                         ? -1
-                         : map_out(o, lpages, idx);
-        if (ids) ids[pos] = idx;
-      }
-    }
-    na += tot >> 16;
-    nt += tot & 0xFFFFu;
-  }
-}
-
-// The ordered write pass over a row staged in registers (slot j of a
-// thread holds vector slot_vid(j): slots in order, and within a slot waves
-// and lanes in order, follow the element order).  As ordered_span, with
-// every slot's counts scanned before one barrier.  kb: block keys (block
-// mode).  tmp: VPT NT/64 LDS words, free when called.
+// The ordered write pass over a run of vectors staged in registers: vector
+// vofs + slot_vid(j) in slot j of a thread (slots in order, and within a
+// slot waves and lanes in order, follow the element order).  Per slot the
+// counts of keys above and equal to T (packed 16 | 16 bits) are scanned
+// over the wave, and the waves' totals, published before one barrier, give
+// every thread its counts before it.  The run's selected elements take the
+// output slots from na + min(nt, take) on (na, nt: keys above and equal to
+// T before the run), staged in LDS and then written as one contiguous
+// piece.  kb: block keys
+// (block mode).  tmp: VPT NT/64 LDS words, stage: as many words as the run
+// takes slots (at most k), both free when called.
 template <int MODE, int NT, int VPT, int KB>
 __device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], int jt, int rem,
-                             int v, uint32_t T, uint32_t cgt, const Out o,
-                             const int32_t* lpages, int32_t* ids, uint32_t* tmp,
-                             uint32_t* stage, int tid = (int)threadIdx.x) {
+                             int vofs, int v, uint32_t T, uint32_t cgt, uint32_t na,
+                             uint32_t nt, const Out o, const int32_t* lpages, int32_t* ids,
+                             uint32_t* tmp, uint32_t* stage, int tid = (int)threadIdx.x) {
   constexpr int NW = NT / 64;
   const int lane = tid & 63, wave = tid >> 6;
   const uint32_t take = o.k - cgt;
+  const uint32_t lo = na + min(nt, take);  // the run's first slot
   uint32_t ga[VPT], te[VPT], ex[VPT];
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
-    const int vid = slot_vid<NT>(j, jt, rem, tid);
+    const int lv = slot_vid<NT>(j, jt, rem, tid);
+    const int vid = vofs + lv;
     ga[j] = 0;
     te[j] = 0;
-    if (vid >= 0) {
+    if (lv >= 0) {
       if constexpr (MODE == TOPK_MODE_BLOCK) {
         ga[j] = kb[j] > T;
         te[j] = kb[j] == T;
@@ -1050,7 +995,7 @@ __device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], 
         }
       }
     }
-    // a row holds at most 2^15 elements: 16-bit counts
+    // a run holds at most 2^15 elements: 16-bit counts
     const uint32_t c = ((uint32_t)__builtin_popcount(ga[j]) << 16) |
                        (uint32_t)__builtin_popcount(te[j]);
     const uint32_t incl = wave_incl_scan(c);
@@ -1071,24 +1016,26 @@ __device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], 
     base += tot;
     if (ga[j] | te[j]) {
       // the slots' element indices (bit 31: a -inf block) go to LDS first
-      const int vid = slot_vid<NT>(j, jt, rem, tid);
+      const int vid = vofs + slot_vid<NT>(j, jt, rem, tid);
       const uint32_t neg =
           (MODE == TOPK_MODE_BLOCK && kb[MODE == TOPK_MODE_BLOCK ? j : 0] == kKeyNegInf)
               ? 0x80000000u
               : 0u;
       uint32_t pos;
-      uint32_t m = ordered_mask(ga[j], te[j], before >> 16, before & 0xFFFFu, take, pos);
+      uint32_t m = ordered_mask(ga[j], te[j], na + (before >> 16), nt + (before & 0xFFFFu), take,
+                                pos);
       for (; m && pos < o.k; m &= m - 1, ++pos)
-        stage[pos] = (uint32_t)(MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + __builtin_ctz(m)) | neg;
+        stage[pos - lo] = (uint32_t)(MODE == TOPK_MODE_BLOCK ? vid : vid * 8 + __builtin_ctz(m)) | neg;
     }
   }
-  // then the whole rows, in runs (every slot below k is taken: cgt keys
-  // above T and take keys equal to it; an index past the row's elements,
-  // which would mean a slot left untaken, is never mapped)
+  // then the run's slots as one piece (every slot in [lo, hi) is taken; an
+  // index past the row's elements, which would mean a slot left untaken,
+  // is never mapped)
+  const uint32_t hi = min(na + (base >> 16) + min(nt + (base & 0xFFFFu), take), o.k);
   __syncthreads();
   const int n = MODE == TOPK_MODE_BLOCK ? (v + 7) >> 3 : v;
-  for (uint32_t i = tid; i < o.k; i += NT) {
-    const uint32_t x = stage[i];
+  for (uint32_t i = lo + tid; i < hi; i += NT) {
+    const uint32_t x = stage[i - lo];
     const int32_t idx = (int32_t)(x & 0x7FFFFFFFu);
     o.out[i] = ((x >> 31) || idx >= n) ? -1 : map_out(o, lpages, idx);
     if (ids) ids[i] = idx;
@@ -1338,7 +1285,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
       }
     }
     __syncthreads();  // the pass's LDS words are free
-    ordered_regs<MODE, NT, VPT>(raw, kb, jt, rem, v, tc.x, tc.y, o, lpages,
+    ordered_regs<MODE, NT, VPT>(raw, kb, jt, rem, 0, v, tc.x, tc.y, 0u, 0u, o, lpages,
                                 p.ids ? p.ids + (int64_t)row * k : nullptr, sh, lists);
     if (p.valid && tid == 0) p.valid[row] = k;
   }
@@ -1872,7 +1819,8 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_count(Params p) {
 
 template <int MODE>
 __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
-  __shared__ uint32_t tmp[2 * (kOrdNT / 64) + 2];
+  __shared__ uint32_t tmp[2 + kOrdVPT * (kOrdNT / 64)];
+  __shared__ uint32_t stage[TOPK_MAX_K];
   const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
@@ -1884,6 +1832,14 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
   const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
   if (vb >= ve) return;
+  // the span in registers, as the one-workgroup kernel stages a row; its
+  // loads are issued first, to overlap those of the counts below
+  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride) + vb;
+  const int jt = (ve - vb - 1) / kOrdNT, rem = (ve - vb) - jt * kOrdNT;
+  uint4 raw[kOrdVPT];
+#pragma unroll
+  for (int j = 0; j < kOrdVPT; ++j)
+    raw[j] = ld_vec(src, (uint32_t)max(slot_vid<kOrdNT>(j, jt, rem, tid), 0));
   // keys above and equal to T in the members before this one
   if (tid < 64) {
     uint32_t a = 0, e = 0;
@@ -1895,17 +1851,25 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
     a = readlane(wave_incl_scan(a), 63);
     e = readlane(wave_incl_scan(e), 63);
     if (tid == 0) {
-      tmp[2 * (kOrdNT / 64)] = a;
-      tmp[2 * (kOrdNT / 64) + 1] = e;
+      tmp[0] = a;
+      tmp[1] = e;
     }
   }
   __syncthreads();
-  const uint32_t na = tmp[2 * (kOrdNT / 64)], nt = tmp[2 * (kOrdNT / 64) + 1];
-  __syncthreads();  // the pass reuses the first words
+  const uint32_t na = tmp[0], nt = tmp[1];
+  if (na >= cgt && nt >= (uint32_t)p.k - cgt) return;  // every slot taken before the span
+  uint32_t kb[MODE == TOPK_MODE_BLOCK ? kOrdVPT : 1];
+  if constexpr (MODE == TOPK_MODE_BLOCK) {
+#pragma unroll
+    for (int j = 0; j < kOrdVPT; ++j) {
+      const int lv = slot_vid<kOrdNT>(j, jt, rem, tid);
+      kb[j] = lv >= 0 ? (vb + lv == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
+    }
+  }
   const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
-  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-  ordered_span<MODE, kOrdNT>(src, vb, ve, v, n, T, cgt, na, nt, o, nullptr,
-                             p.ids ? p.ids + (int64_t)row * p.k : nullptr, tmp);
+  ordered_regs<MODE, kOrdNT, kOrdVPT>(raw, kb, jt, rem, vb, v, T, cgt, na, nt, o, nullptr,
+                                      p.ids ? p.ids + (int64_t)row * p.k : nullptr, tmp + 2,
+                                      stage);
 }
 
 // ================================================================= host
