@@ -148,9 +148,11 @@ int topk_bf16_rows_ex(const uint16_t *logits, int64_t row_stride,
  * Arguments as for topk_bf16_rows, plus
  *   valid        device int32 [rows], or NULL (not written)
  *   ids          device int32 [rows, k], or NULL (not written)
- * Costs over topk_bf16_rows: one more read of each row (rows up to 16384
- * tokens or 4096 blocks, mostly from L2), or two (wider rows, which also
- * take two more kernel launches).  Returns TOPK_OK or a negative
+ * Costs over topk_bf16_rows: rows up to 16384 tokens or 4096 blocks are
+ * ordered from the registers that hold them; wider rows take two more
+ * kernel launches and one more read of the row (two when the row leaves the
+ * sampled path).  Scratch as for topk_bf16_rows, plus (2 + ceil(width /
+ * 16384)) words per row of a wide-row batch.  Returns TOPK_OK or a negative
  * topk_status; asynchronous like topk_bf16_rows. */
 int topk_bf16_rows_ordered(const uint16_t *logits, int64_t row_stride,
                            const int32_t *valid_len, int32_t rows, int32_t width,

@@ -181,3 +181,53 @@ def test_ordered_then_unordered_share_scratch():
                            threads=16)
         bad = check(oracle.default(), d, out.cpu().numpy(), want)
         assert not bad, "\n".join(bad)
+
+
+def test_ordered_graph_replays():
+    """Ordered calls captured in one HIP graph (a one-workgroup row batch
+    with a block table, a token team, a block team) and replayed several
+    times, with an eager ordered call and synchronizations between the
+    replays: every replay's out, ids and valid equal the oracle's (no memset
+    is recorded, and the order records and counts in the team scratch are
+    rewritten by every call)."""
+    ds = [W.make(2, rows=48, width=16384, seed=501), W.make(3, rows=5, width=60000, seed=502),
+          W.make(4, rows=6, width=150000, seed=503)]
+    # eager work in between: no wider than the captured team rows, so that
+    # the stream's scratch (captured by address) is not replaced
+    other = W.make(3, rows=7, width=50000, seed=504)
+    refs = [oracle_ordered(d) for d in ds]
+    s = torch.cuda.Stream()
+    dev = []
+    for d in ds:
+        L = torch.from_numpy(np.ascontiguousarray(d["logits"]).view(np.int16)).cuda()
+        VL = torch.from_numpy(np.ascontiguousarray(d["valid_len"])).cuda()
+        P = None if d.get("pages") is None else torch.from_numpy(d["pages"]).cuda()
+        dev.append((L, VL, P))
+
+    def calls():
+        return [T.topk_bf16_rows_ordered(L, VL, d["k"], d["mode"], block_table=P,
+                                         page_size=d.get("page_size") or 64, width=d["width"])
+                for d, (L, VL, P) in zip(ds, dev)]
+
+    with torch.cuda.stream(s):
+        calls()  # first use on this stream: the scratch is set up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        outs = calls()
+    for rep in range(3):
+        with torch.cuda.stream(s):
+            for trio in outs:
+                for t in trio:
+                    t.fill_(-7)
+            L = torch.from_numpy(other["logits"].view(np.int16)).cuda()
+            VL = torch.from_numpy(other["valid_len"]).cuda()
+            go = T.topk_bf16_rows_ordered(L, VL, other["k"], other["mode"], width=other["width"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"ordered graph replay {rep}", flush=True)
+        for d, (o, v, i), ref in zip(ds, outs, refs):
+            assert_ordered((o.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy()), ref,
+                           ctx=f"replay {rep} {d['name']}")
+        assert_ordered(tuple(t.cpu().numpy() for t in go), oracle_ordered(other), ctx="eager")
