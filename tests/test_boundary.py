@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     assert "topk_bf16_rows" in names and "topk_status_string" in names
-    assert len(names) >= 5
+    assert "topk_bf16_rows_ordered" in names and "topk_bf16_rows_ordered_ex" in names
+    assert len(names) >= 7
 
 
 def test_library_exports_every_declared_symbol():
@@ -69,3 +70,29 @@ def test_bad_block_table():
     assert _call(bt=ctypes.pointer(bt)) == -1
     bt = T._binding._BlockTable(256, 0, 8)           # rows too short for width 16
     assert _call(bt=ctypes.pointer(bt)) == -1
+
+
+def _call_ordered(**kw):
+    lib = T.library()
+    a = dict(logits=16, row_stride=16, valid_len=64, rows=4, width=16, k=8, mode=0,
+             bt=None, out=128, valid=256, ids=512, stream=None)
+    a.update(kw)
+    return lib.topk_bf16_rows_ordered(a["logits"], a["row_stride"], a["valid_len"], a["rows"],
+                                      a["width"], a["k"], a["mode"], a["bt"], a["out"],
+                                      a["valid"], a["ids"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), -1), (dict(k=2049), -1), (dict(mode=2), -1), (dict(row_stride=20), -2),
+    (dict(out=None), -1), (dict(valid=258), -2), (dict(ids=514), -2), (dict(logits=24), -2),
+])
+def test_ordered_rejects_bad_arguments(kw, status):
+    """The ordered entry point checks its arguments as the plain one does,
+    and also the alignment of valid and ids (both may be NULL)."""
+    assert _call_ordered(**kw) == status
+    assert T.library().topk_last_error()
+
+
+def test_ordered_rows_zero_is_a_noop():
+    assert _call_ordered(rows=0, logits=None, valid_len=None, out=None, valid=None,
+                         ids=None) == 0
