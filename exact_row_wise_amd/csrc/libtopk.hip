@@ -156,7 +156,7 @@ struct Params {
   int32_t ord;           // 1: ordered results, with counts and logical ids
   int32_t* valid;        // [rows] counts, or null
   int32_t* ids;          // [rows][k] logical element indices, or null
-  int32_t ord_G;         // team rows: order-pass members per row
+  int32_t ord_G;         // team rows: order spans (of ord_span vectors) per row
   int32_t ord_span;      // team rows: 16-byte vectors per order-pass member
   uint32_t* ord_rec;     // team rows: [rows][2] threshold key, count above (in scratch)
   uint32_t* ord_cnt;     // team rows: [rows][ord_G] per-member counts (in scratch)
@@ -1840,7 +1840,7 @@ __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
 #pragma unroll
   for (int j = 0; j < kOrdVPT; ++j)
     raw[j] = ld_vec(src, (uint32_t)max(slot_vid<kOrdNT>(j, jt, rem, tid), 0));
-  // keys above and equal to T in the members before this one
+  // keys above and equal to T in the spans before this one
   if (tid < 64) {
     uint32_t a = 0, e = 0;
     for (int m = tid; m < member; m += 64) {
