@@ -66,7 +66,7 @@ constexpr int kTeamNT = 256;             // filter workgroup size
 constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kOrdNT = 256;              // ordered results of team rows: threads of a member
 constexpr int kOrdVPT = 8;               // vectors per thread of its span (2048 vectors)
-constexpr uint32_t kOrdCounted = 0x10000u;  // record flag: the select kernel counted the spans
+constexpr uint32_t kOrdCounted = 0x10000u;  // the select kernel's note: spans counted from survivors
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
@@ -1746,7 +1746,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
           }
           __syncthreads();
           for (int i = tid; i < p.ord_G; i += NT) p.ord_cnt[(size_t)lrow * p.ord_G + i] = sh[i];
-          tc.x |= kOrdCounted;
+          tc.x |= kOrdCounted;  // (the record keeps T alone)
         }
       } else if (ORD) {
         tc = make_uint2(c, gt_total);
@@ -1769,53 +1769,48 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     __syncthreads();
     direct_select<MODE, NT>(src, v, n, k, o, smem + kLists, bc, ORD, ORD ? &tc : nullptr);
   }
-  if (ORD && tid == 0) {
-    p.ord_rec[2 * lrow] = tc.x;
-    p.ord_rec[2 * lrow + 1] = tc.y;
-    if (p.valid) p.valid[row] = k;
+  if constexpr (ORD) {
+    if (!(tc.x & kOrdCounted)) {
+      // the tie pass and the direct path: the spans' keys above and equal
+      // to T, counted from the row itself (the survivors need not hold
+      // every key equal to T there)
+      __syncthreads();  // the paths' last reads of LDS are done
+      for (int i = tid; i < p.ord_G; i += NT) sh[i] = 0;
+      __syncthreads();
+      const uint32_t T = tc.x;
+      for (int vid = tid; vid < ((v + 7) >> 3); vid += NT) {
+        const uint4 raw = ld_vec(src, (uint32_t)vid);
+        uint32_t cnt = 0;
+        if constexpr (MODE == TOPK_MODE_BLOCK) {
+          const uint32_t key = vid == n - 1 ? kKeyPosInf : block_key4(raw);
+          cnt = (key > T ? 0x10000u : 0u) + (key == T ? 1u : 0u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = key1(half_of(word_of(raw, e >> 1), e & 1));
+            const bool ok = vid * 8 + e < v;
+            cnt += (ok && key > T ? 0x10000u : 0u) + (ok && key == T ? 1u : 0u);
+          }
+        }
+        if (cnt) atomicAdd(&sh[vid >> 11], cnt);  // spans of 2^11 vectors
+      }
+      __syncthreads();
+      for (int i = tid; i < p.ord_G; i += NT) p.ord_cnt[(size_t)lrow * p.ord_G + i] = sh[i];
+    }
+    if (tid == 0) {
+      p.ord_rec[2 * lrow] = tc.x & 0xFFFFu;
+      p.ord_rec[2 * lrow + 1] = tc.y;
+      if (p.valid) p.valid[row] = k;
+    }
   }
   set_path(p, row, code);
 }
 
 // Ordered results of team rows: every row is cut into spans of
-// p.ord_span vectors, one workgroup (member) each.  The count kernel gives
-// each member's keys above and equal to the row's T (recorded by the
-// select kernel), the write kernel each member's ordered slots from the
-// counts of the members before it.
-
-template <int MODE>
-__global__ __launch_bounds__(kOrdNT) void topk_order_count(Params p) {
-  __shared__ uint32_t tmp[kOrdNT / 64];
-  const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
-  const int row = p.row0 + lrow;
-  const int tid = threadIdx.x;
-  const uint32_t T = p.ord_rec[2 * lrow];
-  if (T > 0xFFFFu) return;  // a short row, or spans counted by the select kernel
-  const int v = clamp_len(p.valid_len[row], p.width);
-  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
-  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-  uint32_t na = 0, nt = 0;
-  for (int vid = vb + tid; vid < ve; vid += kOrdNT) {
-    const uint4 raw = ld_vec(src, (uint32_t)vid);
-    if constexpr (MODE == TOPK_MODE_BLOCK) {
-      const uint32_t key = vid == n - 1 ? kKeyPosInf : block_key4(raw);
-      na += key > T;
-      nt += key == T;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t key = key1(half_of(word_of(raw, e >> 1), e & 1));
-        const bool ok = vid * 8 + e < v;
-        na += ok && key > T;
-        nt += ok && key == T;
-      }
-    }
-  }
-  // a span holds at most kOrdNT kOrdVPT 8 < 2^16 elements
-  const uint32_t t = block_sum<kOrdNT>((na << 16) | nt, tmp, tid);
-  if (tid == 0) p.ord_cnt[(size_t)lrow * p.ord_G + member] = t;
-}
+// p.ord_span vectors, one workgroup each.  The select kernel records the
+// row's T and count above it and each span's keys above and equal to T;
+// the write kernel gives each span its ordered slots from the counts of the
+// spans before it.
 
 template <int MODE>
 __global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
@@ -2136,13 +2131,9 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
     }
     if (rc == TOPK_OK && ord) {
       if (mode == TOPK_MODE_BLOCK) {
-        rc = launch(topk_order_count<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
-        if (rc == TOPK_OK)
-          rc = launch(topk_order_write<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
+        rc = launch(topk_order_write<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
       } else {
-        rc = launch(topk_order_count<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
-        if (rc == TOPK_OK)
-          rc = launch(topk_order_write<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
+        rc = launch(topk_order_write<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
       }
     }
     if (rc != TOPK_OK) return rc;
