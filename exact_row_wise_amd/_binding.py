@@ -152,6 +152,8 @@ def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_
     rows = logits.shape[0]
     if width is None:
         width = logits.shape[1]
+    if int(width) < 0 or int(width) > logits.shape[1]:
+        raise ValueError(f"width {width} outside [0, logits.shape[1] = {logits.shape[1]}]")
     if logits.shape[1] > 1 and logits.stride(1) != 1:
         raise ValueError("logits rows must have unit stride")
     row_stride = logits.stride(0)
@@ -183,6 +185,9 @@ def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_
                 or block_table.device != dev or block_table.shape[0] != rows
                 or (rows > 0 and block_table.stride(1) != 1)):
             raise ValueError("block_table must be int32 [rows, pages] on the same GPU")
+        if int(page_size) >= 1 and block_table.shape[1] < -(-int(width) // int(page_size)):
+            raise ValueError(f"block_table rows hold {block_table.shape[1]} pages; width "
+                             f"{width} needs ceil(width / page_size) of them")
         bt = _BlockTable(block_table.data_ptr(), block_table.stride(0), int(page_size))
     opts = None
     if force_direct or path_codes is not None:

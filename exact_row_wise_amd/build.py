@@ -1,4 +1,4 @@
-"""Build libtopk.so (HIP, gfx950) in-tree with hipcc.
+"""Build libtopk.so and libtopk_probe.so (HIP, gfx950) in-tree with hipcc.
 
     python -m exact_row_wise_amd.build        # or exact_row_wise_amd.build.build()
 """
@@ -14,6 +14,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "libtopk.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopk.so")
+PROBE_SRC = os.path.join(PKG, "csrc", "stream_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libtopk_probe.so")
 ARCH = "gfx950"
 
 
@@ -24,28 +26,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB, extra=()) -> list[str]:
+def command(out: str = LIB, extra=(), src: str = SRC) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # no packed FP32 (the path has no floating point; keep the backend from
-        # forming packed FP32 ops anywhere)
+        # no packed FP32: the only floating point on the path sizes the work
+        # (sample ranks, the cutoff shift); keep the backend from forming
+        # packed FP32 ops from it
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # every wave-level atomic here is already issued by one lane with the
         # wave's total; the backend's own aggregation would only add work
         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wall", "-Wno-unused-function",
-        "-I", INCLUDE, *extra, "-o", out, SRC,
+        "-I", INCLUDE, *extra, "-o", out, src,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
+def _build_one(src: str, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = command(tmp, src=src)
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    _build_one(PROBE_SRC, PROBE_LIB, verbose)
+    return _build_one(SRC, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -1728,7 +1728,7 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
         if constexpr (ORD) {
           // T is above the cutoff, so every key at or above T is staged:
           // count each order span's keys above and equal to T here (16 | 16
-          // bits), which spares the count kernel a read of the row
+          // bits), so that the order pass needs no count of its own
           static_assert(kOrdNT * kOrdVPT == 2048, "spans of 2^11 vectors");
           constexpr int kSpanShift = MODE == TOPK_MODE_BLOCK ? 11 : 14;  // element -> span
           __syncthreads();  // the select's last reads of sh are done
@@ -2084,9 +2084,15 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   const int cv = kTeamNT * vpt;
   const int G = (nvec_max + cv - 1) / cv;  // <= kMaxMembers
   const size_t row_bytes = (size_t)G * kMemberWords * 4;
+  // rows per launch: all of them, unless the scratch cap or kTeamBatch bounds
+  // a launch; a capped batch holds whole groups of 8 rows (one per XCD), and
+  // every launch's grid is padded to whole groups of 8 anyway
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
-  if ((size_t)batch * row_bytes > kTeamScratchMax) batch = (int)(kTeamScratchMax / row_bytes);
-  batch = batch < 8 ? 8 : batch / 8 * 8;  // whole groups of 8 rows (one per XCD)
+  if ((size_t)batch * row_bytes > kTeamScratchMax) {
+    batch = (int)(kTeamScratchMax / row_bytes);
+    batch = batch < 8 ? batch : batch / 8 * 8;
+    if (batch < 1) return fail(TOPK_ERR_HIP, "a row needs more team scratch than the cap");
+  }
   // ordered results: per row its threshold record and one count per
   // order-pass member, after the slices
   const int ord_span = kOrdNT * kOrdVPT;

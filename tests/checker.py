@@ -39,7 +39,8 @@ def check(orc, d, gpu_out, oracle_out, rows=None, max_report=5):
                 bad.append(f"row {r}: short row differs (n={n})")
         else:
             if pages is not None:
-                inv = _inverse_pages(np.asarray(pages[r], dtype=np.int64), P)
+                npg = -(-width // P)   # entries past ceil(width / P) are never used
+                inv = _inverse_pages(np.asarray(pages[r][:npg], dtype=np.int64), P)
                 g = np.where(g >= 0, inv[np.maximum(g, 0) // P] * P + np.maximum(g, 0) % P, -1)
                 o = np.where(o >= 0, inv[np.maximum(o, 0) // P] * P + np.maximum(o, 0) % P, -1)
             keys = orc.row_keys(L[r], v, mode).astype(np.int64)

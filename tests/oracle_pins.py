@@ -407,6 +407,72 @@ def pin_ordered_worked_cases(orc):
     out, ids, valid = orc.topk_ordered(b[None, :], [32], 4, BLOCK)
     assert ids[0].tolist() == [0, 1, 2, 3] and out[0].tolist() == [0, -1, 2, 3]
 
+def _multirow_case(rng, rows, width, stride_pad, P, pstride_pad, mode):
+    """A [rows, row_stride] matrix with row_stride > width (the padding holds
+    the poison +NaN, the top key, and other rows' data would differ), ragged
+    lengths (negative, zero, short, past the width) and a block table whose
+    rows are longer than ceil(width / P)."""
+    stride = width + stride_pad
+    L = rng.integers(0, 1 << 16, size=(rows, stride)).astype(np.uint16)
+    L[:, width:] = 0x7FFF
+    lens = rng.integers(-3, width + 5, size=rows).astype(np.int32)
+    lens[0], lens[-1] = width, 2
+    npg = (width + P - 1) // P
+    pages = rng.integers(0, 1000, size=(rows, npg + pstride_pad)).astype(np.int32)
+    for r in range(rows):
+        pages[r, :npg] = rng.permutation(npg) + 7 * r
+    return L, lens, pages
+
+
+def pin_multirow_driver(orc):
+    """The multi-row drivers (oracle_topk_rows and oracle_topk_rows_ordered,
+    with their host-thread split and row sub-selection) address row r at
+    logits + r * row_stride, its table at pages + r * pages_stride and its
+    outputs at r * k: each row of a multi-row call with row_stride > width,
+    a table stride above ceil(width / P), ragged lengths and several threads
+    equals the one-row call on that row alone (plain: the pinned one-row
+    selection; ordered: the rank definition, which sorts nothing)."""
+    rng = np.random.Generator(np.random.PCG64(34))
+    for mode, width, k, P in ((TOKEN, 61, 9, 4), (BLOCK, 200, 7, 8), (TOKEN, 37, 40, 2)):
+        rows = 11
+        L, lens, pages = _multirow_case(rng, rows, width, 24, P, 5, mode)
+        for threads in (1, 3):
+            for pg in (None, pages):
+                got = orc.topk(L, lens, k, mode, width=width, pages=pg, page_size=P,
+                               threads=threads)
+                for r in range(rows):
+                    want = orc.topk_row(L[r, :width], int(lens[r]), k, mode,
+                                        pages=None if pg is None else pg[r], page_size=P)
+                    assert got[r].tolist() == want.tolist(), \
+                        f"mode {mode} row {r} threads {threads} table {pg is not None}"
+        # a row subset gives the same lines as the full call
+        sub = [7, 2, 2, 10]
+        full = orc.topk(L, lens, k, mode, width=width, pages=pages, page_size=P)
+        part = orc.topk(L, lens, k, mode, width=width, pages=pages, page_size=P, rows=sub,
+                        threads=2)
+        assert part.tolist() == full[sub].tolist(), f"mode {mode}: rows= subset"
+        # ordered results, row by row against the rank definition
+        for threads in (1, 4):
+            out, ids, valid = orc.topk_ordered(L, lens, k, mode, width=width, pages=pages,
+                                               page_size=P, threads=threads)
+            for r in range(rows):
+                keys = orc.row_keys(L[r, :width], int(lens[r]), mode)
+                sel = _ordered_by_rank(keys, keys.size, k)
+                want_ids = sel + [-1] * (k - len(sel))
+                want_out = []
+                for i in want_ids:
+                    o = i
+                    if i >= 0 and mode == BLOCK and keys[i] == 0x007F:
+                        o = -1
+                    if o >= 0:
+                        o = int(pages[r, o // P]) * P + o % P
+                    want_out.append(o)
+                ctx = f"ordered mode {mode} row {r} threads {threads}"
+                assert int(valid[r]) == len(sel), ctx
+                assert ids[r].tolist() == want_ids, ctx
+                assert out[r].tolist() == want_out, ctx
+
+
 ALL_PINS = [
     pin_key_fixed_points,
     pin_key_bijection,
@@ -429,6 +495,7 @@ ALL_PINS = [
     pin_worked_examples,
     pin_ordered_rank_definition,
     pin_ordered_worked_cases,
+    pin_multirow_driver,
 ]
 
 

@@ -53,6 +53,22 @@ MUTANTS = [
      "return a < b ? 1 : (a > b ? -1 : 0);"),
     ("ordered: count is k", "*valid = cnt;", "*valid = k;"),
     ("ordered: ids mapped", "ids[j] = i;", "ids[j] = o;"),
+    ("rows: table row by page size",
+     "const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row(",
+     "const int32_t *prow = pages ? pages + (int64_t)r * page_size : NULL;\n        int rc = oracle_topk_row("),
+    ("rows: logits row by width", "oracle_topk_row(logits + (int64_t)r * row_stride,",
+     "oracle_topk_row(logits + (int64_t)r * width,"),
+    ("rows: output row by width", "out + (int64_t)r * k);", "out + (int64_t)r * width);"),
+    ("rows: first row skipped", "for (r = row_begin; r < row_end; ++r) {\n        const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row(",
+     "for (r = row_begin + 1; r < row_end; ++r) {\n        const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row("),
+    ("ordered rows: table row by page size",
+     "const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row_ordered(",
+     "const int32_t *prow = pages ? pages + (int64_t)r * page_size : NULL;\n        int rc = oracle_topk_row_ordered("),
+    ("ordered rows: logits row by width",
+     "oracle_topk_row_ordered(logits + (int64_t)r * row_stride,",
+     "oracle_topk_row_ordered(logits + (int64_t)r * width,"),
+    ("ordered rows: one count slot", "ids ? ids + (int64_t)r * k : NULL, valid + r);",
+     "ids ? ids + (int64_t)r * k : NULL, valid);"),
 ]
 
 

@@ -12,7 +12,8 @@ import pytest
 import oracle
 import workloads as W
 from checker import check
-from test_parity_gpu import (EDGE, _make, _sampled_positions_wg, _sampled_vectors_team)
+from test_parity_gpu import (EDGE, MULTI_BATCH, PAGE_CASES, _make, _sampled_positions_wg,
+                             _sampled_vectors_team, with_pages)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -83,7 +84,10 @@ def test_ordered_workloads(cfg):
     rows = d["logits"].shape[0]
     print(f"ordered workload {cfg} {d['name']} rows={rows}", flush=True)
     g = run_ordered(d)
-    sel = None if rows <= 512 else np.arange(0, rows, 16)   # the oracle on every 16th row
+    # the oracle on every row up to 512 rows; beyond, on every 16th row and
+    # on every special row of the edge workload (r % 10 == 9: constant, all
+    # -inf, NaN, signed-zero and random-bit rows)
+    sel = None if rows <= 512 else np.union1d(np.arange(0, rows, 16), np.arange(9, rows, 10))
     assert_ordered(g, oracle_ordered(d, sel), sel, ctx=d["name"])
     paths = _paths(g[3])
     print("paths", paths, flush=True)
@@ -231,3 +235,28 @@ def test_ordered_graph_replays():
             assert_ordered((o.cpu().numpy(), v.cpu().numpy(), i.cpu().numpy()), ref,
                            ctx=f"replay {rep} {d['name']}")
         assert_ordered(tuple(t.cpu().numpy() for t in go), oracle_ordered(other), ctx="eager")
+
+
+@pytest.mark.parametrize("rows,width,k,mode,kind", MULTI_BATCH)
+def test_ordered_team_multi_batch(rows, width, k, mode, kind):
+    """Ordered results of launches with more rows than one team batch holds
+    (the later batches' records, counts, ids and outputs start at row0 > 0)."""
+    rng = np.random.Generator(np.random.PCG64(rows + width + 1))
+    lens = rng.integers(k + 1, width + 1, size=rows).astype(np.int32)
+    lens[::7] = width
+    lens[3::50] = k // 2
+    d = _make(rng, rows, width, k, mode, kind, lens=lens)
+    print(f"ordered multi-batch rows={rows} width={width}", flush=True)
+    assert_ordered(run_ordered(d), oracle_ordered(d), ctx=f"rows={rows} width={width}")
+
+
+@pytest.mark.parametrize("P,width,mode", PAGE_CASES)
+def test_ordered_page_sizes(P, width, mode):
+    rng = np.random.Generator(np.random.PCG64(P * 31 + width + mode + 1))
+    k = 512 if mode == 0 else 1024
+    lens = [width, width - 5, width // 2, k - 3, 3 * k]
+    d = with_pages(_make(rng, 5, width, k, mode, "normal", lens=lens), P, rng)
+    print(f"ordered page size {P} width {width} mode {mode}", flush=True)
+    o = oracle_ordered(d)
+    for fd in (False, True):
+        assert_ordered(run_ordered(d, force_direct=fd), o, ctx=f"P={P} force_direct={fd}")

@@ -382,3 +382,54 @@ def test_widest_rows():
         d = _make(rng, 2, 1 << 20, k, mode, "normal", lens=[1 << 20, 777777])
         g, pc = run_gpu(d)
         assert_parity(d, g, run_oracle(d))
+
+
+def with_pages(d, P, rng, pad=3):
+    """d with a per-row permuted block table of page size P (rows padded by
+    `pad` unused entries past ceil(width / P))."""
+    npg = -(-d["width"] // P)
+    rows = d["logits"].shape[0]
+    pages = np.full((rows, npg + pad), 1 << 30, np.int32)
+    for r in range(rows):
+        pages[r, :npg] = rng.permutation(npg)
+    d = dict(d)
+    d["pages"], d["page_size"] = pages, P
+    return d
+
+
+# (rows, width, k, mode, kind): launches with more rows than one team batch
+# holds, so that later batches start at row0 > 0 (1024 rows a batch; 112
+# rows of 2^20 tokens fill the scratch cap)
+MULTI_BATCH = [(1100, 16392, 512, 0, "normal"), (120, 1 << 20, 2048, 0, "normal")]
+
+
+@pytest.mark.parametrize("rows,width,k,mode,kind", MULTI_BATCH)
+def test_team_multi_batch(rows, width, k, mode, kind):
+    rng = np.random.Generator(np.random.PCG64(rows + width))
+    lens = rng.integers(k + 1, width + 1, size=rows).astype(np.int32)
+    lens[::7] = width
+    lens[3::50] = k // 2                       # short rows in later batches too
+    d = _make(rng, rows, width, k, mode, kind, lens=lens)
+    print(f"multi-batch rows={rows} width={width}", flush=True)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, run_oracle(d))
+    assert -9 not in _paths(pc)
+
+
+# page sizes other than 64 on one-workgroup rows (16384 tokens, 4096 blocks:
+# the LDS copy of the table for P >= 16, the global table for P = 1) and on
+# team rows, both modes
+PAGE_CASES = [(P, width, mode) for P in (1, 16, 2048)
+              for width, mode in ((16384, 0), (32768, 1), (100000, 0), (300000, 1))]
+
+
+@pytest.mark.parametrize("P,width,mode", PAGE_CASES)
+def test_page_sizes(P, width, mode):
+    rng = np.random.Generator(np.random.PCG64(P * 31 + width + mode))
+    k = 512 if mode == 0 else 1024
+    lens = [width, width - 5, width // 2, k - 3, 3 * k]
+    d = with_pages(_make(rng, 5, width, k, mode, "normal", lens=lens), P, rng)
+    print(f"page size {P} width {width} mode {mode}", flush=True)
+    for fd in (False, True):
+        g, _ = run_gpu(d, force_direct=fd)
+        assert_parity(d, g, run_oracle(d))
