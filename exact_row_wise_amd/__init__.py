@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     PATH_SHORT,
     TopkError,
     library,
+    topk_bf16_rows_noalloc,
     topk_bf16_rows_ordered,
     library_path,
     release_scratch,

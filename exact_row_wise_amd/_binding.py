@@ -24,6 +24,8 @@ PATH_DIRECT_FORCED = 3
 PATH_DIRECT_MISJUDGED = 4
 PATH_DIRECT_OVERFLOW = 5
 
+ERR_UNSUPPORTED = -4
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libtopk.so")
 _lock = threading.Lock()
@@ -68,6 +70,8 @@ def library():
         lib.topk_bf16_rows.restype = ctypes.c_int
         lib.topk_bf16_rows_ex.argtypes = sig + [ctypes.POINTER(_Options), ctypes.c_void_p]
         lib.topk_bf16_rows_ex.restype = ctypes.c_int
+        lib.topk_bf16_rows_noalloc.argtypes = sig + [ctypes.c_void_p]
+        lib.topk_bf16_rows_noalloc.restype = ctypes.c_int
         osig = sig + [ctypes.c_void_p, ctypes.c_void_p]
         lib.topk_bf16_rows_ordered.argtypes = osig + [ctypes.c_void_p]
         lib.topk_bf16_rows_ordered.restype = ctypes.c_int
@@ -126,6 +130,20 @@ def topk_bf16_rows(logits: torch.Tensor, valid_len: torch.Tensor, k: int, mode=M
                  path_codes, stream)[0]
 
 
+def topk_bf16_rows_noalloc(logits: torch.Tensor, valid_len: torch.Tensor, k: int,
+                           mode=MODE_TOKEN, block_table: torch.Tensor | None = None,
+                           page_size: int = 64, out: torch.Tensor | None = None,
+                           width: int | None = None,
+                           stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """topk_bf16_rows through the entry point that allocates nothing (see
+    include/libtopk.h): `out` must be given, and the library uses its fixed
+    per-device scratch (calls overlapping on one GPU race).  Returns out."""
+    if out is None:
+        raise ValueError("topk_bf16_rows_noalloc needs a preallocated out")
+    return _call(logits, valid_len, k, mode, block_table, page_size, out, width, False, None,
+                 stream, noalloc=True)[0]
+
+
 def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int,
                            mode=MODE_TOKEN, block_table: torch.Tensor | None = None,
                            page_size: int = 64, out: torch.Tensor | None = None,
@@ -143,7 +161,8 @@ def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int
 
 
 def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
-          path_codes, stream, ordered=False, valid=None, ids=None, want_ids=False):
+          path_codes, stream, ordered=False, valid=None, ids=None, want_ids=False,
+          noalloc=False):
     lib = library()
     if logits.dim() != 2:
         raise ValueError("logits must be 2-D [rows, row_stride]")
@@ -209,6 +228,8 @@ def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_
                 rc = lib.topk_bf16_rows_ordered(*args, st)
             else:
                 rc = lib.topk_bf16_rows_ordered_ex(*args, ctypes.byref(opts), st)
+        elif noalloc:
+            rc = lib.topk_bf16_rows_noalloc(*args, st)
         elif opts is None:
             rc = lib.topk_bf16_rows(*args, st)
         else:

@@ -1914,6 +1914,34 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
   return TOPK_OK;
 }
 
+// The scratch of topk_bf16_rows_noalloc: one array per device, part of the
+// code object (no allocation call creates it).  In host code its name is a
+// host-side stand-in, never a device address: only the address that
+// hipGetSymbolAddress returns for the current device is passed to kernels.
+constexpr size_t kNoAllocBytes = size_t(16) << 20;
+static __device__ __align__(256) uint32_t scratch[kNoAllocBytes / 4];
+
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[64] = {};  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up once per device.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TOPK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(TOPK_ERR_UNSUPPORTED, "device %d beyond 64", dev);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(TOPK_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = g_noalloc_ptr[dev];
+  return TOPK_OK;
+}
+
 // Survivor entries per wave of the one-workgroup kernel before a wave
 // stops writing (its region holds kSpare more).  A 16384-logit row with
 // the cutoff rank of sample_rank keeps about 1.2 k + 400 entries holding a
@@ -2009,7 +2037,8 @@ int launch_rows(int mode, int rows, size_t lds, hipStream_t stream, const Params
 
 int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, int32_t rows,
         int32_t width, int32_t k, int32_t mode, const topk_block_table_t* bt, int32_t* out,
-        const topk_options_t* opt, int ord, int32_t* valid, int32_t* ids, void* stream_ptr) {
+        const topk_options_t* opt, int ord, int32_t* valid, int32_t* ids, void* stream_ptr,
+        void* fixed = nullptr, size_t fixed_bytes = 0) {
   g_err[0] = '\0';
   if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, TOPK_MAX_K);
@@ -2084,26 +2113,34 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   const int cv = kTeamNT * vpt;
   const int G = (nvec_max + cv - 1) / cv;  // <= kMaxMembers
   const size_t row_bytes = (size_t)G * kMemberWords * 4;
-  // rows per launch: all of them, unless the scratch cap or kTeamBatch bounds
-  // a launch; a capped batch holds whole groups of 8 rows (one per XCD), and
-  // every launch's grid is padded to whole groups of 8 anyway
-  int batch = rows < kTeamBatch ? rows : kTeamBatch;
-  if ((size_t)batch * row_bytes > kTeamScratchMax) {
-    batch = (int)(kTeamScratchMax / row_bytes);
-    batch = batch < 8 ? batch : batch / 8 * 8;
-    if (batch < 1) return fail(TOPK_ERR_HIP, "a row needs more team scratch than the cap");
-  }
   // ordered results: per row its threshold record and one count per
   // order-pass member, after the slices
   const int ord_span = kOrdNT * kOrdVPT;
   const int ord_G = (nvec_max + ord_span - 1) / ord_span;
-  const size_t ord_bytes = ord ? (size_t)batch * (2 + ord_G) * 4 : 0;
-  void* scratch = nullptr;
-  int rc = get_scratch(stream, (size_t)batch * row_bytes + ord_bytes, &scratch);
-  if (rc != TOPK_OK) return rc;
+  const size_t ord_row_bytes = ord ? (size_t)(2 + ord_G) * 4 : 0;
+  // rows per launch: all of them, unless the scratch cap (or the caller's
+  // fixed scratch) or kTeamBatch bounds a launch; a capped batch of 8 rows
+  // or more holds whole groups of 8 (one per XCD), and every launch's grid
+  // is padded to whole groups of 8 anyway
+  const size_t cap_bytes = fixed ? fixed_bytes : kTeamScratchMax;
+  if (row_bytes + ord_row_bytes > cap_bytes)
+    return fail(TOPK_ERR_UNSUPPORTED, "one row of width %d needs %zu bytes of team scratch, "
+                "more than the %zu available", width, row_bytes + ord_row_bytes, cap_bytes);
+  int batch = rows < kTeamBatch ? rows : kTeamBatch;
+  if ((size_t)batch * (row_bytes + ord_row_bytes) > cap_bytes) {
+    batch = (int)(cap_bytes / (row_bytes + ord_row_bytes));
+    batch = batch < 8 ? batch : batch / 8 * 8;
+  }
+  const size_t ord_bytes = (size_t)batch * ord_row_bytes;
+  void* team_buf = fixed;
+  if (!fixed) {
+    const int rc = get_scratch(stream, (size_t)batch * row_bytes + ord_bytes, &team_buf);
+    if (rc != TOPK_OK) return rc;
+  }
+  int rc = TOPK_OK;
   p.G = G;
   p.team_cv = cv;
-  p.team_slices = static_cast<uint32_t*>(scratch);
+  p.team_slices = static_cast<uint32_t*>(team_buf);
   p.ord_G = ord_G;
   p.ord_span = ord_span;
   p.ord_rec = p.team_slices + (size_t)batch * row_bytes / 4;
@@ -2166,6 +2203,17 @@ int topk_bf16_rows_ex(const uint16_t* logits, int64_t row_stride, const int32_t*
              nullptr, nullptr, stream);
 }
 
+int topk_bf16_rows_noalloc(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
+                           int32_t rows, int32_t width, int32_t k, int32_t mode,
+                           const topk_block_table_t* block_table, int32_t* out, void* stream) {
+  g_err[0] = '\0';
+  void* ptr = nullptr;
+  const int rc = noalloc_scratch(&ptr);
+  if (rc != TOPK_OK) return rc;
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr, 0,
+             nullptr, nullptr, stream, ptr, kNoAllocBytes);
+}
+
 int topk_bf16_rows_ordered(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
                            int32_t rows, int32_t width, int32_t k, int32_t mode,
                            const topk_block_table_t* block_table, int32_t* out, int32_t* valid,
@@ -2189,6 +2237,7 @@ const char* topk_status_string(int status) {
     case TOPK_ERR_INVALID_ARG: return "invalid argument";
     case TOPK_ERR_MISALIGNED: return "misaligned logits or row stride";
     case TOPK_ERR_HIP: return "HIP runtime error";
+    case TOPK_ERR_UNSUPPORTED: return "unsupported call";
     default: return "unknown status";
   }
 }

@@ -78,8 +78,11 @@ enum topk_status {
                                   row_stride < width, bad block table */
     TOPK_ERR_MISALIGNED = -2,  /* logits not 16-byte aligned, or
                                   row_stride not a multiple of 8 */
-    TOPK_ERR_HIP = -3          /* a HIP runtime call or launch failed;
+    TOPK_ERR_HIP = -3,         /* a HIP runtime call or launch failed;
                                   topk_last_error() has the detail */
+    TOPK_ERR_UNSUPPORTED = -4  /* valid arguments this library cannot
+                                  serve; topk_last_error() names the
+                                  reason */
 };
 
 /* Per-row path codes written when topk_options_t.path_codes is set. */
@@ -132,6 +135,25 @@ int topk_bf16_rows_ex(const uint16_t *logits, int64_t row_stride,
                       int32_t k, int32_t mode,
                       const topk_block_table_t *block_table, int32_t *out,
                       const topk_options_t *options, void *stream);
+
+/* topk_bf16_rows for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as topk_bf16_rows.  It
+ * calls no allocating routine: rows wider than one workgroup's share use a
+ * fixed 16 MiB scratch array that the library's code object holds on every
+ * device it runs on, for the life of the process (its address is looked up
+ * once per device, on the first call there).  Rows are processed in batches
+ * that fit it; a single row never needs more than 2.4 MB, so no call is
+ * refused for size (TOPK_ERR_UNSUPPORTED would name the reason).  Every call
+ * on one device shares that device's array: calls that overlap in time on
+ * one device, on any streams, race and must be serialized by the caller.
+ * Nothing in the array needs clearing between calls: every word a call
+ * reads there was written earlier in the same call. */
+int topk_bf16_rows_noalloc(const uint16_t *logits, int64_t row_stride,
+                           const int32_t *valid_len, int32_t rows,
+                           int32_t width, int32_t k, int32_t mode,
+                           const topk_block_table_t *block_table,
+                           int32_t *out, void *stream);
 
 /* Deterministic ordered top-k of every row (vLLM API page
  * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.indexer",
