@@ -16,6 +16,8 @@ from ._binding import (  # noqa: F401
     PATH_SHORT,
     TopkError,
     library,
+    probe_library,
+    stream_read,
     topk_bf16_rows_noalloc,
     topk_bf16_rows_ordered,
     library_path,

@@ -28,8 +28,10 @@ ERR_UNSUPPORTED = -4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "libtopk.so")
+_PROBE_LIB = os.path.join(_HERE, "libtopk_probe.so")
 _lock = threading.Lock()
 _lib = None
+_probe = None
 
 
 class TopkError(RuntimeError):
@@ -86,6 +88,36 @@ def library():
         lib.topk_release_scratch.restype = ctypes.c_int
         _lib = lib
         return lib
+
+
+def probe_library():
+    """Load libtopk_probe.so (the streaming-read probe, built beside libtopk)."""
+    global _probe
+    with _lock:
+        if _probe is not None:
+            return _probe
+        if not os.path.exists(_PROBE_LIB):
+            raise ImportError(f"{_PROBE_LIB} is missing: build it with "
+                              "`python -m exact_row_wise_amd.build`")
+        lib = ctypes.CDLL(_PROBE_LIB)
+        lib.topk_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        lib.topk_probe_stream_read.restype = ctypes.c_int
+        _probe = lib
+        return lib
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream: torch.cuda.Stream | None = None):
+    """topk_probe_stream_read over all of `buf` (a contiguous GPU tensor whose
+    byte size is a multiple of 16, zero-filled); `sink` holds 256 int32."""
+    if not buf.is_contiguous() or buf.device.type != "cuda" or sink.numel() < 256:
+        raise ValueError("stream_read needs a contiguous GPU buffer and a 256-word sink")
+    nbytes = buf.numel() * buf.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    rc = probe_library().topk_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                                ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise TopkError(rc, "topk_probe_stream_read failed")
 
 
 def status_string(status: int) -> str:

@@ -12,17 +12,47 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "libtopk.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(topk_[a-z0-9_]+)\s*\(", text)))
+
+
+# every header under include/ and the library that exports what it declares
+LIBRARIES = {"libtopk.h": "libtopk.so", "libtopk_probe.h": "libtopk_probe.so"}
+
+
+def test_every_header_has_a_library():
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == sorted(LIBRARIES)
+
+
+@pytest.mark.parametrize("header,lib", sorted(LIBRARIES.items()))
+def test_libraries_export_their_headers(header, lib):
+    so = ctypes.CDLL(os.path.join(os.path.dirname(T.library_path()), lib))
+    names = declared_functions(os.path.join(ROOT, "include", header))
+    assert names
+    for name in names:
+        assert hasattr(so, name), f"{lib} does not export {name}"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((16, -16), -1), ((16, 24), -1), ((24, 32), -1), ((None, 32), -1), ((16, 0), 0),
+    ((16, (1 << 40) + 16), -1),
+])
+def test_probe_rejects_bad_arguments(args, status):
+    """Argument errors are found before any launch (no GPU needed)."""
+    lib = T.probe_library()
+    src, nbytes = args
+    assert lib.topk_probe_stream_read(src, nbytes, 64, None) == status
 
 
 def test_header_declares_entry_points():
     names = declared_functions()
     assert "topk_bf16_rows" in names and "topk_status_string" in names
     assert "topk_bf16_rows_ordered" in names and "topk_bf16_rows_ordered_ex" in names
-    assert len(names) >= 7
+    assert "topk_bf16_rows_noalloc" in names
+    assert len(names) >= 8
 
 
 def test_library_exports_every_declared_symbol():
@@ -33,7 +63,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert T.status_string(0) == "ok"
-    for s in (-1, -2, -3):
+    for s in (-1, -2, -3, -4):
         assert T.status_string(s) and T.status_string(s) != "unknown status"
     assert T.status_string(12345) == "unknown status"
 
