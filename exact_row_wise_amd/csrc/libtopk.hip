@@ -64,9 +64,6 @@ constexpr int kCopyStride = 260;         // words between the copies of a replic
 constexpr int kSampBins = kCopies * kCopyStride;  // words of the replicated sample bins
 constexpr int kTeamNT = 256;             // filter workgroup size
 constexpr int kSelNT = 1024;             // select workgroup size
-constexpr int kOrdNT = 256;              // ordered results of team rows: threads of a member
-constexpr int kOrdVPT = 8;               // vectors per thread of its span (2048 vectors)
-constexpr uint32_t kOrdCounted = 0x10000u;  // the select kernel's note: spans counted from survivors
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
@@ -74,7 +71,6 @@ constexpr int kTeamBlockVPT = 12;        // 16-byte vectors per thread of a bloc
 constexpr int kTokenSV = 1;              // sample vectors per thread, token cutoff kernel
 constexpr int kBlockSV = 4;              // sample vectors per thread, block cutoff kernel
 constexpr int kMaxMembers = 64;          // members of a row at most (4 segments each <= 256)
-constexpr int kTeamLCW = 512;            // survivor entries per wave region of a member
 constexpr int kSpare = 64;               // region entries past the cap (one ballot step)
 constexpr int kTieLCW = TOPK_MAX_K / 4 + 128;     // tie entries per wave region of a member
 constexpr int kTeamBatch = 1024;         // rows per team launch at most
@@ -84,7 +80,6 @@ constexpr int kRelCopies = 4;            // copies of those bins (lane mod 4)
 constexpr int kRelStride = 276;          // words per copy: the bins, then per-lane spill words
 constexpr int kRelWords = kRelCopies * kRelStride;
 constexpr int kRowLoCopies = 2;           // copies of the low-byte sample bins, one-workgroup kernel
-constexpr int kSelectMin = 6144;         // staged survivor entries with 64 KB of LDS
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
 
@@ -115,16 +110,25 @@ enum {
   BC_TMP = 96     // 32: reductions, a team row's totals, the select's bin search
 };
 
-// One team member's slice of global scratch (32-bit words), per wave w:
-//   [w]      survivor entries            [4 + w]  keys above the cutoff
-//   [8 + w]  tie entries                 [12 + w] keys equal to the cutoff in them
-//   [16 + w] keys equal to the cutoff    [20] the cutoff  [21] flags
-//   [32, 32 + 8 kTeamLCW) the waves' survivor entries (2 words each)
+// One team member's slice of global scratch (32-bit words):
+//   [0, 32)                 header (MH_* fields)
+//   [32, 160)               256-bin histogram of its survivors' keys relative
+//                           to the cutoff, two 16-bit bins to a word
+//   [160, 160 + 2 kMemberCap)  its survivor entries, one list (2 words each)
 //   then the waves' tie entries (kTieLCW each, 2 words each)
-constexpr int kMemberHdr = 32;
-constexpr int kMemberWords = kMemberHdr + 4 * 2 * kTeamLCW + 4 * 2 * kTieLCW;
-constexpr int H_WCNT = 0, H_ECNT = 4, H_TW = 8, H_TKEPT = 12, H_NEQ = 16, H_CUT = 20, H_FLAGS = 21;
-constexpr uint32_t kFlagDirect = 1u;
+constexpr int kFiltStage = (kSampBins + 256 + kRelWords - 128) / 8;  // LDS entries a filter wave holds
+constexpr int kFiltCap = kFiltStage - 64;                             // kept before the overflow
+constexpr int kMemberCap = 4 * kFiltCap;
+constexpr int kMemberHistOfs = 32;
+constexpr int kMemberList = kMemberHistOfs + kRelBins / 2;
+constexpr int kMemberTies = kMemberList + 2 * kMemberCap;
+constexpr int kMemberWords = kMemberTies + 4 * 2 * kTieLCW;
+constexpr int MH_E = 0, MH_TKEPT = 2, MH_NEQ = 3, MH_TW = 4, MH_CUT = 8, MH_FLAGS = 9,
+              MH_TDROP = 12;
+constexpr uint32_t kFlagDirect = 1u;    // a zero token cutoff: the direct path
+constexpr uint32_t kFlagOverflow = 2u;  // a wave kept more entries than its region holds
+constexpr uint32_t kFlagTies = 4u;      // the keys equal to the cutoff were kept
+static_assert(kMemberList % 4 == 0 && kMemberTies % 2 == 0, "aligned lists");
 static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * 8 - 1) / (kTeamNT * 8) <= kMaxMembers,
               "too many token members per row");
 static_assert((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) / (kTeamNT * kTeamBlockVPT) <=
@@ -151,15 +155,11 @@ struct Params {
   int32_t G;             // team members per row (for the widest row)
   int32_t team_cv;       // 16-byte vectors of one member
   uint32_t* team_slices; // [rows][G][kMemberWords]
-  int32_t sel_cap;       // survivor entries the select kernel stages in LDS
+  int32_t sel_bw;        // ordered results: bitmap words over one member's elements
   // ordered results (ascending element index, lowest-index ties):
   int32_t ord;           // 1: ordered results, with counts and logical ids
   int32_t* valid;        // [rows] counts, or null
   int32_t* ids;          // [rows][k] logical element indices, or null
-  int32_t ord_G;         // team rows: order spans (of ord_span vectors) per row
-  int32_t ord_span;      // team rows: 16-byte vectors per order-pass member
-  uint32_t* ord_rec;     // team rows: [rows][2] threshold key, count above (in scratch)
-  uint32_t* ord_cnt;     // team rows: [rows][ord_G] per-member counts (in scratch)
 };
 
 // ------------------------------------------------------------------ keys
@@ -235,6 +235,15 @@ __device__ __forceinline__ void poison_tail(uint4& v, int r) {
   v.y |= r >= 4 ? 0u : (r == 3 ? 0xFFFF0000u : 0xFFFFFFFFu);
   v.z |= r >= 6 ? 0u : (r == 5 ? 0xFFFF0000u : 0xFFFFFFFFu);
   v.w |= r >= 8 ? 0u : (r == 7 ? 0xFFFF0000u : 0xFFFFFFFFu);
+}
+
+// a - b, or 0 when b >= a.  A guarded subtraction written as a comparison
+// and a difference can be hoisted out of its guard with a no-wrap flag
+// kept, from which the optimizer then wrongly concludes a >= b for every
+// other use of the pair (it folded min(b, a) into b); the saturating
+// builtin carries no such flag.
+__device__ __forceinline__ uint32_t sat_sub(uint32_t a, uint32_t b) {
+  return __builtin_elementwise_sub_sat(a, b);
 }
 
 __device__ __forceinline__ int clamp8(int x) { return x < 0 ? 0 : (x > 8 ? 8 : x); }
@@ -745,7 +754,7 @@ __device__ void emit_entries(const uint32_t* e, uint32_t cnt, int32_t Ts, uint32
     if (EQ && nq) {  // keys equal to Ts are few: most chunks skip this
       // slots cgt + bq + rank while bq + rank < take (room: what is left)
       const uint32_t b1 = bq + nq0;
-      const uint32_t room0 = bq < take ? take - bq : 0u, room1 = b1 < take ? take - b1 : 0u;
+      const uint32_t room0 = sat_sub(take, bq), room1 = sat_sub(take, b1);
       const uint32_t r0 = mbcnt(q0), r1 = mbcnt(q1);
       if (in_mask(q0) && r0 < room0) st_slot(out, (cgt + bq) + r0, v0);
       if (in_mask(q1) && r1 < room1) st_slot(out, (cgt + b1) + r1, v1);
@@ -902,11 +911,14 @@ __device__ __forceinline__ void keep_equal_slot(bool eq, uint32_t idx, uint16_t*
 // Entries whose key pair holds a key equal to cs go to this wave's tie
 // region the same way (compaction at tbase + tcnt), until tcnt passes
 // tcap.  tw counts the entries written, tkept the equal keys in them, neq
-// every equal key.
+// every equal key; tdrop is the smallest element index of an equal key
+// that was not kept (every equal key below it was).
 __device__ __forceinline__ void keep_ties(uint32_t x, uint32_t eidx, int32_t cs, uint32_t* tl,
                                           uint32_t tbase, uint32_t tcap, uint32_t& tcnt,
-                                          uint32_t& tw, uint32_t& tkept, uint32_t& neq) {
-  const unsigned long long elo = __ballot(lo16s(x) == cs), ehi = __ballot(hi16s(x) == cs);
+                                          uint32_t& tw, uint32_t& tkept, uint32_t& neq,
+                                          uint32_t& tdrop) {
+  const bool lo_eq = lo16s(x) == cs;
+  const unsigned long long elo = __ballot(lo_eq), ehi = __ballot(hi16s(x) == cs);
   const unsigned long long me = elo | ehi;
   if (me) {
     const uint32_t ne = popc(elo) + popc(ehi);
@@ -917,6 +929,10 @@ __device__ __forceinline__ void keep_ties(uint32_t x, uint32_t eidx, int32_t cs,
       }
       tw += popc(me);
       tkept += ne;
+    } else {
+      // lanes hold ascending element indices: the first lane is the smallest
+      const uint32_t e = readlane(eidx + (lo_eq ? 0u : 1u), __ffsll(me) - 1);
+      tdrop = min(tdrop, e);
     }
     tcnt += popc(me);
     neq += ne;
@@ -946,8 +962,8 @@ __device__ __forceinline__ uint32_t tie_cap(int k) { return (uint32_t)k / 4u + 6
 // mask; `first` receives the first slot.
 __device__ __forceinline__ uint32_t ordered_mask(uint32_t ga, uint32_t te, uint32_t pa,
                                                  uint32_t pt, uint32_t take, uint32_t& first) {
-  first = pa + min(pt, take);
-  const uint32_t room = pt < take ? take - pt : 0u;
+  const uint32_t room = sat_sub(take, pt);
+  first = pa + (take - room);  // pa + min(pt, take)
   uint32_t tk = te;
   for (uint32_t c = (uint32_t)__builtin_popcount(te); c > room; --c)
     tk &= ~(1u << (31 - __builtin_clz(tk)));  // drop the last tie
@@ -964,9 +980,10 @@ __device__ __forceinline__ uint32_t ordered_mask(uint32_t ga, uint32_t te, uint3
 // T before the run), staged in LDS and then written as one contiguous
 // piece.  kb: block keys
 // (block mode).  tmp: VPT NT/64 LDS words, stage: as many words as the run
-// takes slots (at most k), both free when called.
+// takes slots (at most k), both free when called.  Returns the run's counts
+// of keys above and equal to T (16 | 16 bits).
 template <int MODE, int NT, int VPT, int KB>
-__device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], int jt, int rem,
+__device__ uint32_t ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], int jt, int rem,
                              int vofs, int v, uint32_t T, uint32_t cgt, uint32_t na,
                              uint32_t nt, const Out o, const int32_t* lpages, int32_t* ids,
                              uint32_t* tmp, uint32_t* stage, int tid = (int)threadIdx.x) {
@@ -1040,6 +1057,7 @@ __device__ void ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[KB], 
     o.out[i] = ((x >> 31) || idx >= n) ? -1 : map_out(o, lpages, idx);
     if (ids) ids[i] = idx;
   }
+  return base;
 }
 
 // Ordered results of a row with n <= k: the logical ids 0..n-1, then -1,
@@ -1302,18 +1320,24 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 // blockIdx % 8, so they run on one XCD and the row's samples, loaded by
 // every member, come from that XCD's L2 after the first.
 
-// Stage 1: every member loads the row's samples (spread over the whole
-// row; the same in every member) and then its chunk of NT * VPT vectors
-// (members past the row's valid length exit at once), derives the row's
-// cutoff while its chunk is still in flight, and writes to its scratch
-// slice the entries holding a key above the cutoff (compacted in LDS, then
-// copied out) and, in the same pass when the cutoff may be tied, those
-// holding a key equal to it (chunk-local indices).  Short rows and rows
-// sent straight to the direct path are left to stage 2.
+// Stage 1: every member loads the row's samples (spread over the whole row,
+// the same in every member) and waits for them before its chunk loads go
+// out, so that the samples do not queue behind the chunks of every other
+// member; then it loads its chunk of NT * VPT vectors (members past the
+// row's valid length exit at once), derives the row's cutoff while the
+// chunk streams in, compacts the entries holding a key above the cutoff in
+// LDS and writes them to its scratch slice as one list, with a 256-bin
+// histogram of their keys relative to the cutoff; when the cutoff may be
+// tied, it also keeps the entries holding a key equal to it (chunk-local
+// indices).  Short rows and rows sent straight to the direct path are left
+// to stage 2.  Every load is issued unconditionally (a lane past the row's
+// end reads vector 0 and masks it), so that the compiler counts the loads
+// exactly and each wait covers only what it needs.
 template <int MODE, int VPT, int SV>
 __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   constexpr int NT = kTeamNT;
   __shared__ __align__(16) uint32_t h8[kSampBins + 256 + kRelWords];
+  __shared__ __align__(16) uint32_t mh[kRelWords];
   __shared__ uint32_t bc[128];
   const int G = p.G;
   const int b = blockIdx.x, xg = b & 7, yg = b >> 3;
@@ -1336,12 +1360,12 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const int jt = (ve - vb - 1) / NT;   // last occupied slot
   const int rem = (ve - vb) - jt * NT; // vectors in it
   for (int i = tid; i < kSampBins + 256 + kRelWords; i += NT) h8[i] = 0;
+  for (int i = tid; i < kRelWords; i += NT) mh[i] = 0;
 
-  // -- sample loads, then chunk loads.  The samples are the same in every
-  // member of the row: every vector of a short row; otherwise SV * NT / 8
-  // runs of 8 consecutive vectors (one 128-byte line each), run r starting
-  // at line floor((2 r + 1) lines / (2 runs)) (a 32.32 step), so that the
-  // row's members share few lines.
+  // -- samples: the same in every member of the row: every vector of a
+  // short row; otherwise SV * NT / 8 runs of 8 consecutive vectors (one
+  // 128-byte line each), run r starting at line floor((2 r + 1) lines / (2
+  // runs)) (a 32.32 step), so that the row's members share few lines
   const int ns = min(SV * NT, nvec);
   const int nl = nvec >> 3, runs = SV * NT / 8;
   const uint64_t step = nvec > SV * NT ? ((uint64_t)nl << 32) / (uint64_t)(2 * runs) : 0;
@@ -1356,15 +1380,8 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
       const int r = si >> 3;
       spos[j] = (int)((((uint64_t)(2 * r + 1) * step) >> 32) << 3) + (si & 7);
     }
-    sraw[j] = spos[j] >= 0 ? src[spos[j]] : make_uint4(~0u, ~0u, ~0u, ~0u);
+    sraw[j] = ld_vec(src, (uint32_t)max(spos[j], 0));
   }
-  uint4 raw[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j) {
-    const int lvid = slot_vid<NT>(j, jt, rem);
-    raw[j] = lvid >= 0 ? src[vb + lvid] : make_uint4(~0u, ~0u, ~0u, ~0u);
-  }
-  // -- the cutoff, identical in every member, while the chunk arrives
   constexpr int NSK = (MODE == TOPK_MODE_BLOCK) ? SV : SV * 8;
   uint32_t sk[NSK];
   uint32_t mine = 0;
@@ -1383,6 +1400,14 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
       }
     }
   }
+  // the chunk loads go out only now (the keys above waited for the samples)
+  asm volatile("" ::: "memory");
+  uint4 raw[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+    raw[j] = ld_vec(src, (uint32_t)(vb + max(slot_vid<NT>(j, jt, rem), 0)));
+
+  // -- the cutoff, identical in every member, while the chunk arrives
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
   uint32_t sa, se;
   uint32_t c =
@@ -1395,16 +1420,15 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   // and takes the direct path, so exactness is kept)
   bool ties = !tie_unlikely((uint32_t)k, (uint32_t)n, S, sa);
   // Otherwise, when the keys at or above c are few enough for the members'
-  // regions and the select's staging, the cutoff moves to the key below c:
-  // the keys equal to c become survivors and no ties are collected (at
-  // least q of the samples lie at or above c, so k keys almost surely do;
-  // a row where they do not takes the direct path as above).  Every member
-  // takes the same decision from the same samples.
+  // regions, the cutoff moves to the key below c: the keys equal to c become
+  // survivors and no ties are collected (at least q of the samples lie at or
+  // above c, so k keys almost surely do; a row where they do not takes the
+  // direct path as above).  Every member takes the same decision from the
+  // same samples.
   if (ties && c >= 2u) {
     constexpr float kKeysPerWave = 64.0f * VPT * (MODE == TOPK_MODE_BLOCK ? 1 : 8);
     const float f = (float)(sa + se) * __builtin_amdgcn_rcpf((float)S);
-    if (1.25f * f * kKeysPerWave + 48.0f <= (float)(kTeamLCW - kSpare) &&
-        1.25f * f * (float)n + 256.0f <= (float)p.sel_cap) {
+    if (1.25f * f * kKeysPerWave + 48.0f <= (float)kFiltCap) {
       c -= 1u;
       ties = false;
     }
@@ -1414,34 +1438,31 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     // a zero cutoff would make the zero keys of slots past the length ties:
     // every member sees the same cutoff and flags the row for the direct path
     if (tid == 0) {
-      slice[H_CUT] = c;
-      slice[H_FLAGS] = kFlagDirect;
+      slice[MH_CUT] = c;
+      slice[MH_FLAGS] = kFlagDirect;
     }
     return;
   }
 
   // -- entries above the cutoff: compacted into this wave's region of the
-  // sample-bin area (free once every wave has its cutoff), then copied to
-  // the wave's scratch segment with whole-wave stores.  Entries holding a
-  // key equal to the cutoff (when collected at all) go straight to their
+  // sample-bin area (free once every wave has its cutoff).  Entries holding
+  // a key equal to the cutoff (when collected at all) go straight to their
   // global regions.
   const int32_t cs = (int32_t)c - 0x8000;
-  uint32_t* seg = slice + kMemberHdr;
-  uint32_t* tl = slice + kMemberHdr + 8 * kTeamLCW;
+  uint32_t* tl = slice + kMemberTies;
   const uint32_t wv = readfirst((uint32_t)wave);
-  const uint32_t wbase = wv * kTeamLCW, tbase = wv * kTieLCW;
+  const uint32_t tbase = wv * kTieLCW;
   const uint32_t tcap = tie_cap(k);
-  // LDS: 64 dummy entries, then 4 wave regions of kStage entries (kStage -
-  // 64 kept, the rest for the stores past the cap)
-  constexpr uint32_t kStage = (kSampBins + 256 + kRelWords - 128) / 8;
-  static_assert(NT == 256 && kStage - 64 <= (uint32_t)(kTeamLCW - kSpare),
-                "a wave keeps no more entries than its scratch segment takes");
+  // LDS: 64 dummy entries, then 4 wave regions of kFiltStage entries
+  // (kFiltCap kept, the rest for the stores past the cap)
+  static_assert(NT == 256 && 128 + 8 * kFiltStage <= kSampBins + 256 + kRelWords,
+                "four wave regions in the sample-bin area");
   const uint32_t lds_h8 = lds_addr(h8);
-  const uint32_t first = lds_h8 + 4u * (128u + 2u * wv * kStage);
-  const uint32_t lim = first + (kStage - 64u) * 8u;
+  const uint32_t first = lds_h8 + 4u * (128u + 2u * wv * kFiltStage);
+  const uint32_t lim = first + (uint32_t)kFiltCap * 8u;
   const uint32_t dummy = lds_h8 + 8u * (uint32_t)lane;
   uint32_t at = first;
-  uint32_t tcnt = 0, tw = 0, tkept = 0, neq = 0;
+  uint32_t tcnt = 0, tw = 0, tkept = 0, neq = 0, tdrop = 0xFFFFFFFFu;
   __syncthreads();  // every wave is done with the sample bins
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
@@ -1452,8 +1473,10 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
             lvid >= 0 ? (vb + lvid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         const uint32_t x = block_entry(key);
         keep_word_lds(x, (uint32_t)lvid, cs, lim, dummy, at);
-        if (ties) keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
+        if (ties) keep_ties(x, (uint32_t)lvid, cs, tl, tbase, tcap, tcnt, tw, tkept, neq, tdrop);
       } else {
+        // slot jt: the row's last vector is cut at the length, and lanes
+        // without a vector there hold vector 0: both become bottom keys
         if (j == jt) poison_tail(raw[j], lvid >= 0 ? clamp8(v - 8 * (vb + lvid)) : 0);
         const uint32_t e8 = (uint32_t)lvid * 8u;
 #pragma unroll
@@ -1461,52 +1484,192 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
           const uint32_t w = word_of(raw[j], q2);
           const uint32_t x = cs >= 0 ? w : skey2(w);  // raw words serve when cs >= 0
           keep_word_lds(x, e8 + 2 * q2, cs, lim, dummy, at);
-          if (ties) keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq);
+          if (ties)
+            keep_ties(x, e8 + 2 * q2, cs, tl, tbase, tcap, tcnt, tw, tkept, neq, tdrop);
         }
       }
     }
   }
-  // copy-out; a token wave counts the keys above the cutoff on the way
-  // (a block entry holds one)
+  // -- the histogram of this wave's entries, relative to the cutoff (bin 0:
+  // keys at or above cs + 256; bin i: key cs + 256 - i; keys at or below cs
+  // into a spill word of the lane), in 4 lane-replicated copies
   const uint32_t wcnt = (at - first) / 8u;
-  const uint32_t nw = min(wcnt, kStage - 64u);
-  const uint32_t* stg = h8 + 128 + 2 * wv * kStage;
-  uint32_t ek = 0;
-  for (uint32_t i = (uint32_t)lane; i < nw; i += 64) {
-    const uint2 e = *reinterpret_cast<const uint2*>(stg + 2 * i);
-    *reinterpret_cast<uint2*>(seg + 2 * (wbase + i)) = e;
-    if constexpr (MODE == TOPK_MODE_TOKEN)
-      ek += (lo16s(e.x) > cs ? 1u : 0u) + (hi16s(e.x) > cs ? 1u : 0u);
+  const uint32_t nw = min(wcnt, (uint32_t)kFiltCap);
+  const uint32_t* stg = h8 + 128 + 2 * wv * kFiltStage;
+  {
+    const int32_t top = cs + kRelBins;
+    uint32_t* const mhc = mh + (lane & (kRelCopies - 1)) * kRelStride;
+    const int32_t spill = kRelBins + (lane >> 2);
+    for (uint32_t i = (uint32_t)lane; i < nw; i += 64) {
+      const uint32_t x = stg[2 * i];
+      atomicAdd(&mhc[clamp0(top - lo16s(x), spill)], 1u);
+      if constexpr (MODE == TOPK_MODE_TOKEN) atomicAdd(&mhc[clamp0(top - hi16s(x), spill)], 1u);
+    }
   }
-  const uint32_t ecnt = MODE == TOPK_MODE_TOKEN ? readlane(wave_incl_scan(ek), 63) : nw;
   if (lane == 0) {
-    // a wave past its LDS region reports an entry count the select reads as overflow
-    slice[H_WCNT + wave] = wcnt > kStage - 64u ? 0xFFFFu : wcnt;
-    slice[H_ECNT + wave] = ecnt;
-    slice[H_TW + wave] = tw;
-    slice[H_TKEPT + wave] = tkept;
-    slice[H_NEQ + wave] = neq;
+    bc[BC_CNT + wave] = wcnt;
+    bc[BC_ECNT + wave] = tkept;
+    bc[BC_ECNT + 4 + wave] = neq;
+    bc[BC_ECNT + 8 + wave] = tw;
+    bc[BC_ECNT + 12 + wave] = tdrop;
+  }
+  __syncthreads();
+  uint32_t off = 0, E = 0, tk = 0, nq = 0;
+  bool ovf = false;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t cw = bc[BC_CNT + w];
+    off += w < wave ? cw : 0u;
+    E += cw;
+    ovf |= cw > (uint32_t)kFiltCap;
+    tk += bc[BC_ECNT + w];
+    nq += bc[BC_ECNT + 4 + w];
+  }
+  // the list: this wave's entries after the earlier waves'
+  uint32_t* list = slice + kMemberList;
+  if (!ovf)
+    for (uint32_t i = (uint32_t)lane; i < nw; i += 64)
+      *reinterpret_cast<uint2*>(list + 2 * (off + i)) =
+          *reinterpret_cast<const uint2*>(stg + 2 * i);
+  // the histogram, two 16-bit bins to a word (a chunk holds at most 2^14
+  // keys)
+  if (tid < kRelBins / 2) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int c4 = 0; c4 < kRelCopies; ++c4) {
+      lo += mh[c4 * kRelStride + 2 * tid];
+      hi += mh[c4 * kRelStride + 2 * tid + 1];
+    }
+    slice[kMemberHistOfs + tid] = lo | (hi << 16);
+  }
+  if (tid < 4) {
+    slice[MH_TW + tid] = bc[BC_ECNT + 8 + tid];
+    slice[MH_TDROP + tid] = bc[BC_ECNT + 12 + tid];
   }
   if (tid == 0) {
-    slice[H_CUT] = c;
-    slice[H_FLAGS] = 0u;
+    slice[MH_E] = E;
+    slice[MH_TKEPT] = tk;
+    slice[MH_NEQ] = nq;
+    slice[MH_CUT] = c;
+    slice[MH_FLAGS] = (ovf ? kFlagOverflow : 0u) | (ties ? kFlagTies : 0u);
   }
 }
 
-// LDS of the select kernel past kLists (words)
-constexpr int kSelStart = 0;         // survivor entry starts of the <= 4 kMaxMembers segments
-constexpr int kSelTstart = 1024;     // tie entry starts
-constexpr int kSelSegc = 2048;       // survivor entries per segment
-constexpr int kSelTsegc = 3072;      // tie entries per segment
-constexpr int kSelStage = 4096;      // staged entries, 2 words each
-constexpr int kSelFixed = kLists + kSelStage;  // words before the staged entries
+// One chunk of 64 survivor entries (en: this lane's; a dead pair past the
+// list) of element offset g: keys above Ts to output slots from the low word
+// of `slot`, keys equal to Ts (when EQ) to slots cgt + the high word while
+// below take; one 64-bit LDS atomic per chunk, each index written straight
+// to the row's output through the block table (block entries of -inf blocks
+// write -1).
+template <int MODE, bool GT, bool EQ>
+__device__ __forceinline__ void emit_chunk(uint2 en, uint32_t g, int32_t Ts, uint32_t cgt,
+                                           uint32_t take, unsigned long long* slot,
+                                           const Out& o) {
+  const int lane = __lane_id();
+  const int32_t s0 = lo16s(en.x), s1 = hi16s(en.x);
+  const unsigned long long g0 = GT ? __ballot(s0 > Ts) : 0ull;
+  const unsigned long long g1 = GT ? __ballot(s1 > Ts) : 0ull;
+  const unsigned long long q0 = EQ ? __ballot(s0 == Ts) : 0ull;
+  const unsigned long long q1 = EQ ? __ballot(s1 == Ts) : 0ull;
+  const uint32_t ng0 = popc(g0), nq0 = popc(q0);
+  const uint32_t ng = ng0 + popc(g1), nq = nq0 + popc(q1);
+  if (!(ng | nq)) return;
+  unsigned long long base = 0;
+  if (lane == 0) base = atomicAdd(slot, (unsigned long long)ng | ((unsigned long long)nq << 32));
+  const uint32_t bg = readfirst((uint32_t)base), bq = readfirst((uint32_t)(base >> 32));
+  int32_t v0 = (int32_t)(en.y + g);
+  int32_t v1 = v0 + 1;
+  if constexpr (MODE == TOPK_MODE_BLOCK) v0 = s0 == kSNegInf ? -1 : v0;
+  if (o.pages) {
+    v0 = o.map(v0);
+    v1 = o.map(v1);
+  }
+  int32_t* const out = o.out;
+  if (GT) {
+    if (in_mask(g0)) st_slot(out, bg + mbcnt(g0), v0);
+    if (in_mask(g1)) st_slot(out, (bg + ng0) + mbcnt(g1), v1);
+  }
+  if (EQ && nq) {
+    const uint32_t b1 = bq + nq0;
+    const uint32_t room0 = sat_sub(take, bq), room1 = sat_sub(take, b1);
+    const uint32_t r0 = mbcnt(q0), r1 = mbcnt(q1);
+    if (in_mask(q0) && r0 < room0) st_slot(out, (cgt + bq) + r0, v0);
+    if (in_mask(q1) && r1 < room1) st_slot(out, (cgt + b1) + r1, v1);
+  }
+}
 
-// Stage 2: one 1024-thread workgroup per row writes short rows, and
-// otherwise reads the slices of the row's members (written by the previous
-// kernel, so plain loads see them; the first 64 entries of each segment are
-// loaded together with the headers), checks that the cutoff held, and
-// writes the row: exact select over the survivors, the tie pass, or the
-// direct path.
+// Exclusive prefix of the set bits over the bitmap words bm[0, nw) of one
+// wave (nw a multiple of 64 or below it), into pre[0, nw).
+__device__ __forceinline__ void bitmap_prefix(const uint32_t* bm, uint32_t* pre, int nw) {
+  const int lane = __lane_id();
+  uint32_t carry = 0;
+  for (int w0 = 0; w0 < nw; w0 += 64) {
+    const int w = w0 + lane;
+    const uint32_t c = w < nw ? (uint32_t)__builtin_popcount(bm[w]) : 0u;
+    const uint32_t incl = wave_incl_scan(c);
+    if (w < nw) pre[w] = carry + incl - c;
+    carry += readlane(incl, 63);
+  }
+}
+
+// Set bits in the wave's bitmap bm for the keys of entries that pass
+// `pick` (chunk-local element indices; token entries hold two keys).
+template <int MODE, class Pick>
+__device__ __forceinline__ void bitmap_mark(uint2 en, uint32_t* bm, Pick pick) {
+  const int32_t s0 = lo16s(en.x), s1 = hi16s(en.x);
+  if (pick(s0)) atomicOr(&bm[en.y >> 5], 1u << (en.y & 31));
+  if (MODE == TOPK_MODE_TOKEN && pick(s1))
+    atomicOr(&bm[(en.y + 1) >> 5], 1u << ((en.y + 1) & 31));
+}
+
+// The selected keys of one entry (bit set in the wave's bitmap sel, key at
+// or above Ts) to their ordered slots base + (selected elements before them
+// in the member's chunk); pre: the exclusive prefix of sel.
+template <int MODE>
+__device__ __forceinline__ void bitmap_write(uint2 en, uint32_t g, int32_t Ts, uint32_t base,
+                                             const uint32_t* sel, const uint32_t* pre,
+                                             const Out& o, int32_t* ids) {
+#pragma unroll
+  for (int h = 0; h < (MODE == TOPK_MODE_TOKEN ? 2 : 1); ++h) {
+    const int32_t s = h ? hi16s(en.x) : lo16s(en.x);
+    const uint32_t e = en.y + (uint32_t)h;
+    if (s >= Ts) {
+      const uint32_t w = sel[e >> 5], bit = 1u << (e & 31);
+      if (w & bit) {
+        const uint32_t pos = base + pre[e >> 5] + (uint32_t)__builtin_popcount(w & (bit - 1u));
+        const int32_t idx = (int32_t)(g + e);
+        if (pos < o.k) {
+          o.out[pos] = (MODE == TOPK_MODE_BLOCK && s == kSNegInf) ? -1 : o.map(idx);
+          if (ids) ids[pos] = idx;
+        }
+      }
+    }
+  }
+}
+
+// LDS of the select kernel (32-bit words): control words, the row's summed
+// histogram, a table of 16 words per member, the members' own histograms
+// (ordered results), then the waves' work areas (ordered bitmaps) or the
+// direct path's bins.
+constexpr int kSelHist = 128;
+constexpr int kSelMem = kSelHist + 272;
+constexpr int kSelMhist = kSelMem + 16 * kMaxMembers;
+constexpr int kSelWave = kSelMhist + (kRelBins / 2) * kMaxMembers;
+enum { MT_E = 0, MT_TK = 1, MT_NQ = 2, MT_CUT = 3, MT_TW = 4, MT_GT = 8, MT_EQ = 9, MT_BASE = 10,
+       MT_QUOTA = 11 };
+
+// Stage 2: one 1024-thread workgroup per row.  Short rows are written
+// directly.  Otherwise the members' headers, histograms and first entries
+// are loaded together (before the row's length is known); the summed
+// histogram gives the k-th key T and the count above it exactly (the keys
+// above the cutoff are all in the members' lists), and the entries are
+// written straight from the lists: unordered through LDS slot counters, or
+// in element order through per-member bitmaps (the members' counts above
+// and at T, scanned over the members, give each member its first slot and
+// its share of the ties).  A cutoff tied with the k-th key takes the tie
+// pass (the ties kept beside the lists); a misjudged cutoff, an overflow
+// of a member's list, or a k-th key 256 or more above the cutoff sends the
+// row to the direct path.
 template <int MODE, bool ORD>
 __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
@@ -1517,354 +1680,368 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   const int lane = __lane_id();
   const int wave = tid >> 6;
   const int k = p.k;
+  const int G = p.G;
+  const uint32_t* slices = p.team_slices + (size_t)lrow * G * kMemberWords;
+  // -- loads that need not wait for the row's length: the headers (lane m
+  // of wave 0: member m), the histograms (thread t: word t % 128 of
+  // members t / 128, + 8, ...) and the first 64 entries of the members this
+  // wave writes (wave, wave + NW, ...); the words of members past the row's
+  // end are stale, and dropped once the length is known
+  uint4 h0 = make_uint4(0u, 0u, 0u, 0u), h1 = h0, h2 = h0, h3 = h0;
+  if (wave == 0 && lane < G) {
+    const uint4* h4 = reinterpret_cast<const uint4*>(slices + (size_t)lane * kMemberWords);
+    h0 = h4[0];
+    h1 = h4[1];
+    h2 = h4[2];
+    if (ORD) h3 = h4[3];
+  }
+  constexpr int kHPer = kMaxMembers * (kRelBins / 2) / NT;
+  uint32_t hw[kHPer];
+#pragma unroll
+  for (int i = 0; i < kHPer; ++i) {
+    const int m = (tid >> 7) + (NT >> 7) * i;
+    hw[i] = m < G ? slices[(size_t)m * kMemberWords + kMemberHistOfs + (tid & 127)] : 0u;
+  }
+  constexpr int kPreM = kMaxMembers / NW;
+  uint2 pre[kPreM];
+#pragma unroll
+  for (int u = 0; u < kPreM; ++u) {
+    const int m = wave + u * NW;
+    pre[u] = m < G ? *reinterpret_cast<const uint2*>(slices + (size_t)m * kMemberWords +
+                                                     kMemberList + 2 * lane)
+                   : make_uint2(kDeadPair, 0u);
+  }
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
   const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
   const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
-  uint32_t* sh = smem + kSampHist;
-  uint32_t* rel = smem + kRelHist;
-  uint32_t* bc = smem + kBc;
-  uint32_t* start = smem + kLists + kSelStart;
-  uint32_t* tstart = smem + kLists + kSelTstart;
-  uint32_t* segc = smem + kLists + kSelSegc;
-  uint32_t* tsegc = smem + kLists + kSelTsegc;
-  uint32_t* ent = smem + kLists + kSelStage;
-  const int G = p.G;
-  const uint32_t* slices = p.team_slices + (size_t)lrow * G * kMemberWords;
-  // -- everything the previous kernel left for this row, loaded at once
-  // without waiting for the row's length: the flags, the cutoff, every
-  // member's segment headers and the first 64 entries of segments wave,
-  // wave + NW, ... (segments of members past the row's end hold stale
-  // values and are masked once the length is known)
-  const int nseg_max = 4 * G;  // <= 4 kMaxMembers <= NT: one segment per thread
-  const uint32_t rflags = slices[H_FLAGS];
-  const uint32_t c = slices[H_CUT];
-  auto seg_src = [&](int s2) {
-    return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + (s2 & 3) * 2 * kTeamLCW;
-  };
-  auto tie_src = [&](int s2) {
-    return slices + (size_t)(s2 >> 2) * kMemberWords + kMemberHdr + 8 * kTeamLCW +
-           (s2 & 3) * 2 * kTieLCW;
-  };
-  // the headers first (lane m of wave 0: member m's four segments), then
-  // the segment heads
-  static_assert(H_WCNT == 0 && H_ECNT == 4 && H_TW == 8 && H_TKEPT == 12 && H_NEQ == 16,
-                "header fields are four consecutive words each");
-  static_assert(kMaxMembers <= 64, "one lane of wave 0 per member");
-  uint4 hv[5];
-#pragma unroll
-  for (int f = 0; f < 5; ++f) hv[f] = make_uint4(0u, 0u, 0u, 0u);
-  if (wave == 0 && lane < G) {
-    const uint4* h4 = reinterpret_cast<const uint4*>(slices + (size_t)lane * kMemberWords);
-#pragma unroll
-    for (int f = 0; f < 5; ++f) hv[f] = h4[f];
-  }
-  // heads of segments wave, wave + NW, ...: enough for every segment of a
-  // block row up to 2^20 logits (43 members), 8 for token rows
-  constexpr int kPre = MODE == TOPK_MODE_BLOCK ? 11 : 8;
-  static_assert(MODE == TOPK_MODE_TOKEN ||
-                    kPre * NW >= 4 * ((TOPK_MAX_WIDTH / 8 + kTeamNT * kTeamBlockVPT - 1) /
-                                      (kTeamNT * kTeamBlockVPT)),
-                "one preloaded head per segment of the widest block row");
-  uint2 pre[kPre];  // survivor entries
-#pragma unroll
-  for (int u = 0; u < kPre; ++u) {
-    const int s2 = wave + u * NW;
-    pre[u] = s2 < nseg_max ? *reinterpret_cast<const uint2*>(seg_src(s2) + 2 * lane)
-                           : make_uint2(kDeadPair, 0u);
-  }
+  int32_t* const ids = (ORD && p.ids) ? p.ids + (int64_t)row * k : nullptr;
   if (n <= k) {
     if constexpr (MODE == TOPK_MODE_BLOCK) write_short_block<NT>(o, src, n, k);
     else write_short_token<NT>(o, n, k);
-    if constexpr (ORD) {
-      short_ids<NT>(p, row, n);
-      if (tid == 0) p.ord_rec[2 * lrow] = 0xFFFFFFFFu;  // written: the order kernels skip it
-    }
+    if constexpr (ORD) short_ids<NT>(p, row, n);
     set_path(p, row, TOPK_PATH_SHORT);
     return;
   }
+  uint32_t* bc = smem;
+  uint32_t* hs = smem + kSelHist;
+  uint32_t* mt = smem + kSelMem;
+  uint32_t* mhist = smem + kSelMhist;
   bool direct = p.force_direct != 0;
   int code = TOPK_PATH_DIRECT_FORCED;
   uint2 tc = make_uint2(0u, 0u);  // ordered results: the k-th key, the count above it
-  if (!direct && (rflags & kFlagDirect)) {
-    direct = true;
-    code = TOPK_PATH_DIRECT_MISJUDGED;
-  }
   if (!direct) {
     const int nvec = (v + 7) >> 3;
     const int gr = (nvec + p.team_cv - 1) / p.team_cv;  // members of this row
-    // chunk starts in element units: 8 logits per vector, one block per vector
     const uint32_t chunk = (uint32_t)p.team_cv * (MODE == TOPK_MODE_BLOCK ? 1u : 8u);
-    const int nseg = 4 * gr;
-    for (int i = tid; i < kRelHist - kSampHist + kRelWords; i += NT) sh[i] = 0;
+    for (int i = tid; i < kRelBins; i += NT) hs[i] = 0;
     if (tid == 0) {
       bc[BC_SLOT] = 0;
       bc[BC_SLOT + 1] = 0;
     }
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      if (wave + u * NW >= nseg) pre[u] = make_uint2(kDeadPair, 0u);
-    }
-    // per segment (member, wave): entry counts, key counts, overflow.  Wave
-    // 0 alone sums them (lane m: member m) and publishes the segment starts
-    // and the row's totals; the other waves wait at the barrier.
+    // the member table and the row's totals (wave 0, lane m: member m)
     if (wave == 0) {
       const bool live = lane < gr;
-      const uint4 wc = live ? hv[0] : make_uint4(0u, 0u, 0u, 0u);
-      const uint4 tw = live ? hv[2] : make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t ec = live ? hv[1].x + hv[1].y + hv[1].z + hv[1].w : 0u;
-      const uint32_t tk = live ? hv[3].x + hv[3].y + hv[3].z + hv[3].w : 0u;
-      const uint32_t nq = live ? hv[4].x + hv[4].y + hv[4].z + hv[4].w : 0u;
-      const uint32_t wsum = wc.x + wc.y + wc.z + wc.w, tsum = tw.x + tw.y + tw.z + tw.w;
-      constexpr uint32_t kCapW = (uint32_t)(kTeamLCW - kSpare);
-      const bool bad = max(max(wc.x, wc.y), max(wc.z, wc.w)) > kCapW;
-      const uint32_t iw = wave_incl_scan(wsum), it = wave_incl_scan(tsum);
-      const uint32_t ie = wave_incl_scan(ec), ik = wave_incl_scan(tk), iq = wave_incl_scan(nq);
-      const unsigned long long mb = __ballot(bad);
-      if (live) {
-        const uint32_t s0 = iw - wsum, t0 = it - tsum;
-        reinterpret_cast<uint4*>(start)[lane] =
-            make_uint4(s0, s0 + wc.x, s0 + wc.x + wc.y, s0 + wc.x + wc.y + wc.z);
-        reinterpret_cast<uint4*>(tstart)[lane] =
-            make_uint4(t0, t0 + tw.x, t0 + tw.x + tw.y, t0 + tw.x + tw.y + tw.z);
-        reinterpret_cast<uint4*>(segc)[lane] = wc;
-        reinterpret_cast<uint4*>(tsegc)[lane] = tw;
+      const uint32_t tk = live ? h0.z : 0u, nq = live ? h0.w : 0u;
+      const uint32_t fl = live ? h2.y : 0u;
+      if (lane < kMaxMembers) {
+        uint32_t* e = mt + lane * 16;
+        // the member's tie cut: every key equal to the cutoff below this
+        // chunk-local element index was kept
+        const uint32_t cut = min(min(h3.x, h3.y), min(h3.z, h3.w));
+        *reinterpret_cast<uint4*>(e) = make_uint4(live ? h0.x : 0u, tk, nq, cut);
+        *reinterpret_cast<uint4*>(e + MT_TW) = live ? h1 : make_uint4(0u, 0u, 0u, 0u);
       }
+      const uint32_t itk = wave_incl_scan(tk), inq = wave_incl_scan(nq);
+      const unsigned long long fd = __ballot(fl & kFlagDirect), fo = __ballot(fl & kFlagOverflow);
+      const unsigned long long ft = __ballot(fl & kFlagTies);
       if (lane == 63) {
-        bc[BC_TMP + 0] = iw;
-        bc[BC_TMP + 1] = it;
-        bc[BC_TMP + 2] = ie;
-        bc[BC_TMP + 3] = ik;
-        bc[BC_TMP + 4] = iq;
-        bc[BC_TMP + 5] = mb ? 1u : 0u;
+        bc[BC_TMP + 0] = (fd ? 1u : 0u) | (fo ? 2u : 0u) | (ft ? 4u : 0u);
+        bc[BC_TMP + 1] = itk;  // tie keys kept
+        bc[BC_TMP + 2] = inq;  // keys equal to the cutoff
+      }
+      if (lane == 0) bc[BC_TMP + 3] = h2.x;  // the cutoff (the same in every member)
+    }
+    __syncthreads();
+    // the row's histogram, and (ordered results) the members' own
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) {
+      const int m = (tid >> 7) + (NT >> 7) * i;
+      const uint32_t w = hw[i];
+      if (m < gr) {
+        if (w) {
+          atomicAdd(&hs[2 * (tid & 127)], w & 0xFFFFu);
+          atomicAdd(&hs[2 * (tid & 127) + 1], w >> 16);
+        }
+        if (ORD) mhist[m * (kRelBins / 2) + (tid & 127)] = w;
       }
     }
     __syncthreads();
-    const uint32_t E = bc[BC_TMP + 0], Et = bc[BC_TMP + 1], gt_total = bc[BC_TMP + 2];
-    const uint32_t avail = bc[BC_TMP + 3], eq_total = bc[BC_TMP + 4], flags = bc[BC_TMP + 5];
+    const uint32_t fl = bc[BC_TMP + 0], avail = bc[BC_TMP + 1], eq_total = bc[BC_TMP + 2];
+    const uint32_t c = bc[BC_TMP + 3];
     const int32_t cs = (int32_t)c - 0x8000;
-    const uint32_t cap = (uint32_t)p.sel_cap;
-    const bool sampled = gt_total >= (uint32_t)k;
-    if (flags & 1u) {
-      direct = true;
-      code = TOPK_PATH_DIRECT_OVERFLOW;
-    } else if (gt_total + eq_total < (uint32_t)k) {
+    uint32_t ri, above, total;
+    find_copies<1, kRelStride>(hs, (uint32_t)k, ri, above, total);
+    bool tie_pass = false;
+    int32_t Ts = 0;
+    uint32_t cgt = 0;
+    if (fl & 1u) {
       direct = true;
       code = TOPK_PATH_DIRECT_MISJUDGED;
-    } else if (E + 64u + (sampled ? 0u : Et + 64u) > cap ||
-               (!sampled && avail < (uint32_t)k - gt_total)) {
+    } else if (fl & 2u) {
       direct = true;
       code = TOPK_PATH_DIRECT_OVERFLOW;
+    } else if (total >= (uint32_t)k) {
+      if (ri == 0) {  // the k-th key lies 256 or more above the cutoff
+        direct = true;
+        code = TOPK_PATH_DIRECT_OVERFLOW;
+      } else {
+        Ts = cs + kRelBins - (int32_t)ri;
+        cgt = above;
+        code = TOPK_PATH_SAMPLED;
+      }
+    } else if ((fl & 4u) && total + eq_total >= (uint32_t)k && avail >= (uint32_t)k - total) {
+      tie_pass = true;  // the k-th key is the cutoff
+      Ts = cs;
+      cgt = total;
+      code = TOPK_PATH_SAMPLED_TIES;
     } else {
-      // stage the survivor entries (and, for the tie pass, the tie entries
-      // after them) in LDS with row-level indices: the preloaded chunks
-      // first, then whatever they did not cover
-      // (the counts and starts of a wave's preloaded segments read together,
-      // then the stores)
-      uint32_t pc[kPre], ps[kPre];
+      direct = true;
+      code = TOPK_PATH_DIRECT_MISJUDGED;
+    }
+    const uint32_t take = (uint32_t)k - cgt;
+    if (!direct && !ORD) {
+      // -- unordered: every wave writes the lists of its members
+      unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
 #pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        const int s2 = wave + u * NW;  // < kPre NW <= 1024 words of each array
-        const uint32_t cnt = segc[s2], st = start[s2];
-        pc[u] = s2 < nseg ? cnt : 0u;
-        ps[u] = st;
-      }
+      for (int u = 0; u < kPreM; ++u) {
+        const int m = wave + u * NW;
+        if (m < gr) {
+          const uint32_t Em = mt[m * 16 + MT_E];
+          const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
+          const uint32_t g = (uint32_t)m * chunk;
+          for (uint32_t b0 = 0; b0 < Em; b0 += 64) {
+            uint2 en = b0 == 0 ? pre[u] : *reinterpret_cast<const uint2*>(list + 2 * (b0 + lane));
+            if (b0 + lane >= Em) en = make_uint2(kDeadPair, 0u);
+            if (tie_pass) emit_chunk<MODE, true, false>(en, g, Ts, cgt, take, slot, o);
+            else emit_chunk<MODE, true, true>(en, g, Ts, cgt, take, slot, o);
+          }
+          if (tie_pass) {
+            // the first keys equal to the cutoff, from the tie regions
+            const uint32_t* tl = slices + (size_t)m * kMemberWords + kMemberTies;
 #pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        const int s2 = wave + u * NW;
-        if ((uint32_t)lane < pc[u]) {
-          *reinterpret_cast<uint2*>(ent + 2 * (ps[u] + lane)) =
-              make_uint2(pre[u].x, pre[u].y + (uint32_t)(s2 >> 2) * chunk);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kPre; ++u) {
-        if (pc[u] > 64u) {  // what the preloaded head did not cover
-          const int s2 = wave + u * NW;
-          const uint32_t* es = seg_src(s2);
-          const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
-          for (uint32_t i = 64u + lane; i < pc[u]; i += 64) {
-            const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
-            *reinterpret_cast<uint2*>(ent + 2 * (ps[u] + i)) = make_uint2(x.x, x.y + g);
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t tw = mt[m * 16 + MT_TW + w];
+              for (uint32_t b0 = 0; b0 < tw; b0 += 64) {
+                uint2 en = b0 + lane < tw ? *reinterpret_cast<const uint2*>(
+                                                tl + 2 * (w * kTieLCW + b0 + lane))
+                                          : make_uint2(kDeadPair, 0u);
+                emit_chunk<MODE, false, true>(en, g, Ts, cgt, take, slot, o);
+              }
+            }
           }
         }
       }
-      for (int s2 = wave + kPre * NW; s2 < nseg; s2 += NW) {  // segments without a head
-        const uint32_t* es = seg_src(s2);
-        const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
-        for (uint32_t i = lane; i < segc[s2]; i += 64) {
-          const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
-          *reinterpret_cast<uint2*>(ent + 2 * (start[s2] + i)) = make_uint2(x.x, x.y + g);
-        }
-      }
-      if (!sampled) {
-        uint32_t* tent = ent + 2 * (E + 64);
-        for (int s2 = wave; s2 < nseg; s2 += NW) {
-          const uint32_t* es = tie_src(s2);
-          const uint32_t g = (uint32_t)(s2 >> 2) * chunk;
-          for (uint32_t i = lane; i < tsegc[s2]; i += 64) {
-            const uint2 x = *reinterpret_cast<const uint2*>(es + 2 * i);
-            *reinterpret_cast<uint2*>(tent + 2 * (tstart[s2] + i)) = make_uint2(x.x, x.y + g);
+    } else if (!direct) {
+      // -- ordered: each member's keys above and at T, scanned over the
+      // members (wave w: members w, w + NW, ...; lane l: bins 4l .. 4l + 3)
+#pragma unroll
+      for (int u = 0; u < kPreM; ++u) {
+        const int m = wave + u * NW;
+        if (m < gr) {
+          uint32_t gt = 0, eq = 0;
+          if (tie_pass) {
+            const uint2 w2 = *reinterpret_cast<const uint2*>(mhist + m * (kRelBins / 2) + 2 * lane);
+            gt = (w2.x & 0xFFFFu) + (w2.x >> 16) + (w2.y & 0xFFFFu) + (w2.y >> 16);
+          } else {
+            const uint2 w2 = *reinterpret_cast<const uint2*>(mhist + m * (kRelBins / 2) + 2 * lane);
+            const uint32_t b4[4] = {w2.x & 0xFFFFu, w2.x >> 16, w2.y & 0xFFFFu, w2.y >> 16};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t bin = 4u * (uint32_t)lane + q;
+              gt += bin < ri ? b4[q] : 0u;
+              eq += bin == ri ? b4[q] : 0u;
+            }
+          }
+          gt = readlane(wave_incl_scan(gt), 63);
+          eq = tie_pass ? mt[m * 16 + MT_NQ] : readlane(wave_incl_scan(eq), 63);
+          if (lane == 0) {
+            mt[m * 16 + MT_GT] = gt;
+            mt[m * 16 + MT_EQ] = eq;
           }
         }
-      }
-      // dead entries after the survivors and after the ties
-      if (tid < 64) {
-        *reinterpret_cast<uint2*>(ent + 2 * (E + tid)) = make_uint2(kDeadPair, 0u);
-        if (!sampled)
-          *reinterpret_cast<uint2*>(ent + 2 * (E + 64 + Et + tid)) = make_uint2(kDeadPair, 0u);
       }
       __syncthreads();
-      // each wave takes whole 64-entry chunks: only the last share ends in
-      // the padding
-      const uint32_t share = ((E + 64 * NW - 1) / (64 * NW)) * 64;
-      const uint32_t lo = min((uint32_t)wave * share, E);
-      const uint32_t hi = min(lo + share, E);
-      unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
-      if (sampled) {
-        select_and_write<MODE, NW, true>(ent + 2 * lo, hi - lo, cs, (uint32_t)k, rel, sh, bc,
-                                         0xFFFFFFFFu, o, nullptr, ORD, ORD ? &tc : nullptr);
-        code = TOPK_PATH_SAMPLED;
-        if constexpr (ORD) {
-          // T is above the cutoff, so every key at or above T is staged:
-          // count each order span's keys above and equal to T here (16 | 16
-          // bits), so that the order pass needs no count of its own
-          static_assert(kOrdNT * kOrdVPT == 2048, "spans of 2^11 vectors");
-          constexpr int kSpanShift = MODE == TOPK_MODE_BLOCK ? 11 : 14;  // element -> span
-          __syncthreads();  // the select's last reads of sh are done
-          for (int i = tid; i < p.ord_G; i += NT) sh[i] = 0;
-          __syncthreads();
-          for (uint32_t i = tid; i < E; i += NT) {
-            const uint2 x = *reinterpret_cast<const uint2*>(ent + 2 * i);
-            const uint32_t k0 = (uint32_t)(lo16s(x.x) + 0x8000);
-            uint32_t cnt = (k0 > tc.x ? 0x10000u : 0u) + (k0 == tc.x ? 1u : 0u);
-            if constexpr (MODE == TOPK_MODE_TOKEN) {  // block entries: the high half is dead
-              const uint32_t k1 = (uint32_t)(hi16s(x.x) + 0x8000);
-              cnt += (k1 > tc.x ? 0x10000u : 0u) + (k1 == tc.x ? 1u : 0u);
-            }
-            if (cnt) atomicAdd(&sh[x.y >> kSpanShift], cnt);
-          }
-          __syncthreads();
-          for (int i = tid; i < p.ord_G; i += NT) p.ord_cnt[(size_t)lrow * p.ord_G + i] = sh[i];
-          tc.x |= kOrdCounted;  // (the record keeps T alone)
+      if (wave == 0) {
+        const bool live = lane < gr;
+        const uint32_t gt = live ? mt[lane * 16 + MT_GT] : 0u;
+        const uint32_t eq = live ? mt[lane * 16 + MT_EQ] : 0u;
+        const uint32_t gb = wave_incl_scan(gt) - gt, eb = wave_incl_scan(eq) - eq;
+        const uint32_t room = sat_sub(take, eb);  // ties left for this member and after
+        const uint32_t quota = min(room, eq);
+        // the tie pass needs each member's first `quota` ties by element
+        // index: all of them when it takes every tie (none dropped), else
+        // (the one member that takes some) enough kept below its cut
+        const uint32_t cut = live ? mt[lane * 16 + MT_CUT] : 0xFFFFFFFFu;
+        const bool all_short = live && tie_pass && quota > 0 && quota >= eq && cut != 0xFFFFFFFFu;
+        const bool some = live && tie_pass && quota > 0 && quota < eq && cut != 0xFFFFFFFFu;
+        if (live) {
+          mt[lane * 16 + MT_BASE] = gb + (take - room);  // gb + min(eb, take)
+          mt[lane * 16 + MT_QUOTA] = quota;
         }
-      } else if (ORD) {
-        tc = make_uint2(c, gt_total);
-        code = TOPK_PATH_SAMPLED_TIES;
+        const unsigned long long bad = __ballot(all_short);
+        const unsigned long long chk = __ballot(some);
+        uint32_t fail_ties = bad ? 1u : 0u;
+        if (chk) {
+          // that member's kept ties below its cut, counted in wave 0's area
+          const int m = __ffsll(chk) - 1;
+          const uint32_t cm = readlane(cut, m), qm = readlane(quota, m);
+          uint32_t* wb = smem + kSelWave;
+          const int bw = p.sel_bw;
+          for (int i = lane; i < bw; i += 64) wb[i] = 0;
+          const uint32_t* tl = slices + (size_t)m * kMemberWords + kMemberTies;
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t tw = mt[m * 16 + MT_TW + w];
+            for (uint32_t b0 = 0; b0 < tw; b0 += 64) {
+              const uint2 en = b0 + lane < tw ? *reinterpret_cast<const uint2*>(
+                                                    tl + 2 * (w * kTieLCW + b0 + lane))
+                                              : make_uint2(kDeadPair, 0u);
+              bitmap_mark<MODE>(en, wb, [&](int32_t s) { return s == Ts; });
+            }
+          }
+          uint32_t below = 0;
+          for (int i = lane; i < bw; i += 64) {
+            const uint32_t lo = (uint32_t)i * 32u;
+            const uint32_t keep = cm >= lo + 32u ? 0xFFFFFFFFu
+                                                 : (cm > lo ? (1u << (cm - lo)) - 1u : 0u);
+            below += (uint32_t)__builtin_popcount(wb[i] & keep);
+          }
+          below = readlane(wave_incl_scan(below), 63);
+          if (below < qm) fail_ties = 1u;
+        }
+        if (lane == 0) bc[BC_TMP + 4] = fail_ties;
+      }
+      __syncthreads();
+      if (bc[BC_TMP + 4]) {
+        direct = true;
+        code = TOPK_PATH_DIRECT_OVERFLOW;
       } else {
-        // the k-th key is the cutoff: every key above it, then the first ties
-        const uint32_t take = (uint32_t)k - gt_total;
-        emit_entries<MODE, true, false>(ent + 2 * lo, hi - lo, cs, gt_total, take, slot, o,
-                                        nullptr);
-        const uint32_t tshare = ((Et + 64 * NW - 1) / (64 * NW)) * 64;
-        const uint32_t tlo = min((uint32_t)wave * tshare, Et);
-        const uint32_t thi = min(tlo + tshare, Et);
-        emit_entries<MODE, false, true>(ent + 2 * (E + 64 + tlo), thi - tlo, cs, gt_total, take,
-                                        slot, o, nullptr);
-        code = TOPK_PATH_SAMPLED_TIES;
+        // per member: the selected keys' bitmap over its chunk (keys above
+        // T, and its first `quota` keys at T by element index), its prefix,
+        // then every selected key to base + its rank
+        const int bw = p.sel_bw;
+        uint32_t* sel = smem + kSelWave + wave * 3 * bw;
+        uint32_t* wk = sel + bw;
+        uint32_t* pf = wk + bw;
+#pragma unroll 1
+        for (int u = 0; u < kPreM; ++u) {
+          const int m = wave + u * NW;
+          if (m >= gr) break;
+          const uint32_t Em = mt[m * 16 + MT_E], eqm = mt[m * 16 + MT_EQ];
+          const uint32_t quota = mt[m * 16 + MT_QUOTA], base = mt[m * 16 + MT_BASE];
+          const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
+          const uint32_t* tl = slices + (size_t)m * kMemberWords + kMemberTies;
+          const uint32_t g = (uint32_t)m * chunk;
+          for (int i = lane; i < bw; i += 64) {
+            sel[i] = 0;
+            wk[i] = 0;
+          }
+          // the entries at T: in the list (sampled path) or the tie regions
+          // (the lists' first chunks come from L2: the loads ahead brought them)
+          auto for_list = [&](auto&& f) {
+            for (uint32_t b0 = 0; b0 < Em; b0 += 64) {
+              const uint2 en = b0 + lane < Em
+                                   ? *reinterpret_cast<const uint2*>(list + 2 * (b0 + lane))
+                                   : make_uint2(kDeadPair, 0u);
+              f(en);
+            }
+          };
+          auto for_ties = [&](auto&& f) {
+            if (!tie_pass) {
+              for_list(f);
+            } else {
+              for (int w = 0; w < 4; ++w) {
+                const uint32_t tw = mt[m * 16 + MT_TW + w];
+                for (uint32_t b0 = 0; b0 < tw; b0 += 64) {
+                  const uint2 en = b0 + lane < tw ? *reinterpret_cast<const uint2*>(
+                                                        tl + 2 * (w * kTieLCW + b0 + lane))
+                                                  : make_uint2(kDeadPair, 0u);
+                  f(en);
+                }
+              }
+            }
+          };
+          for_list([&](uint2 en) { bitmap_mark<MODE>(en, sel, [&](int32_t s) { return s > Ts; }); });
+          if (quota > 0) {
+            if (quota >= eqm) {
+              for_ties([&](uint2 en) {
+                bitmap_mark<MODE>(en, sel, [&](int32_t s) { return s == Ts; });
+              });
+            } else {
+              // the member's first `quota` keys at T: ranks from their own
+              // bitmap's prefix
+              for_ties([&](uint2 en) {
+                bitmap_mark<MODE>(en, wk, [&](int32_t s) { return s == Ts; });
+              });
+              bitmap_prefix(wk, pf, bw);
+              for_ties([&](uint2 en) {
+#pragma unroll
+                for (int h = 0; h < (MODE == TOPK_MODE_TOKEN ? 2 : 1); ++h) {
+                  const int32_t s = h ? hi16s(en.x) : lo16s(en.x);
+                  const uint32_t e = en.y + (uint32_t)h;
+                  if (s == Ts) {
+                    const uint32_t r = pf[e >> 5] +
+                        (uint32_t)__builtin_popcount(wk[e >> 5] & ((1u << (e & 31)) - 1u));
+                    if (r < quota) atomicOr(&sel[e >> 5], 1u << (e & 31));
+                  }
+                }
+              });
+            }
+          }
+          bitmap_prefix(sel, pf, bw);
+          for_list([&](uint2 en) { bitmap_write<MODE>(en, g, Ts, base, sel, pf, o, ids); });
+          if (tie_pass && quota > 0)
+            for_ties([&](uint2 en) { bitmap_write<MODE>(en, g, Ts, base, sel, pf, o, ids); });
+        }
+        if (tid == 0 && p.valid) p.valid[row] = k;
       }
     }
+    tc = make_uint2((uint32_t)(Ts + 0x8000), cgt);
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE, NT>(src, v, n, k, o, smem + kLists, bc, ORD, ORD ? &tc : nullptr);
-  }
-  if constexpr (ORD) {
-    if (!(tc.x & kOrdCounted)) {
-      // the tie pass and the direct path: the spans' keys above and equal
-      // to T, counted from the row itself (the survivors need not hold
-      // every key equal to T there)
-      __syncthreads();  // the paths' last reads of LDS are done
-      for (int i = tid; i < p.ord_G; i += NT) sh[i] = 0;
-      __syncthreads();
-      const uint32_t T = tc.x;
-      for (int vid = tid; vid < ((v + 7) >> 3); vid += NT) {
-        const uint4 raw = ld_vec(src, (uint32_t)vid);
-        uint32_t cnt = 0;
-        if constexpr (MODE == TOPK_MODE_BLOCK) {
-          const uint32_t key = vid == n - 1 ? kKeyPosInf : block_key4(raw);
-          cnt = (key > T ? 0x10000u : 0u) + (key == T ? 1u : 0u);
-        } else {
+    direct_select<MODE, NT>(src, v, n, k, o, smem + kSelWave, bc, ORD, ORD ? &tc : nullptr);
+    if constexpr (ORD) {
+      // the ordered write pass over the row, in spans of NT * 2 vectors
+      constexpr int VPT = 2;
+      uint32_t* tmp = smem + kSelWave;
+      uint32_t* stage = tmp + VPT * NW;
+      const int nvec = (v + 7) >> 3;
+      uint32_t na = 0, nt = 0;
+      const uint32_t take = (uint32_t)k - tc.y;
+#pragma unroll 1
+      for (int vb = 0; vb < nvec && (na < tc.y || nt < take); vb += NT * VPT) {
+        const int ve = min(vb + NT * VPT, nvec);
+        const int jt = (ve - vb - 1) / NT, rem = (ve - vb) - jt * NT;
+        uint4 raw[VPT];
+        uint32_t kb[MODE == TOPK_MODE_BLOCK ? VPT : 1];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t key = key1(half_of(word_of(raw, e >> 1), e & 1));
-            const bool ok = vid * 8 + e < v;
-            cnt += (ok && key > T ? 0x10000u : 0u) + (ok && key == T ? 1u : 0u);
-          }
+        for (int j = 0; j < VPT; ++j) {
+          const int lv = slot_vid<NT>(j, jt, rem, tid);
+          raw[j] = ld_vec(src, (uint32_t)(vb + max(lv, 0)));
+          if constexpr (MODE == TOPK_MODE_BLOCK)
+            kb[j] = lv >= 0 ? (vb + lv == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         }
-        if (cnt) atomicAdd(&sh[vid >> 11], cnt);  // spans of 2^11 vectors
+        __syncthreads();  // the previous span's LDS words are free
+        const uint32_t tot = ordered_regs<MODE, NT, VPT>(raw, kb, jt, rem, vb, v, tc.x, tc.y, na,
+                                                         nt, o, nullptr, ids, tmp, stage);
+        na += tot >> 16;
+        nt += tot & 0xFFFFu;
       }
-      __syncthreads();
-      for (int i = tid; i < p.ord_G; i += NT) p.ord_cnt[(size_t)lrow * p.ord_G + i] = sh[i];
-    }
-    if (tid == 0) {
-      p.ord_rec[2 * lrow] = tc.x & 0xFFFFu;
-      p.ord_rec[2 * lrow + 1] = tc.y;
-      if (p.valid) p.valid[row] = k;
+      if (tid == 0 && p.valid) p.valid[row] = k;
     }
   }
   set_path(p, row, code);
-}
-
-// Ordered results of team rows: every row is cut into spans of
-// p.ord_span vectors, one workgroup each.  The select kernel records the
-// row's T and count above it and each span's keys above and equal to T;
-// the write kernel gives each span its ordered slots from the counts of the
-// spans before it.
-
-template <int MODE>
-__global__ __launch_bounds__(kOrdNT) void topk_order_write(Params p) {
-  __shared__ uint32_t tmp[2 + kOrdVPT * (kOrdNT / 64)];
-  __shared__ uint32_t stage[TOPK_MAX_K];
-  const int lrow = blockIdx.x / p.ord_G, member = blockIdx.x % p.ord_G;
-  const int row = p.row0 + lrow;
-  const int tid = threadIdx.x;
-  const uint32_t rec = p.ord_rec[2 * lrow];
-  if (rec == 0xFFFFFFFFu) return;  // a short row, written by the select kernel
-  const uint32_t T = rec & 0xFFFFu;
-  const uint32_t cgt = p.ord_rec[2 * lrow + 1];
-  const int v = clamp_len(p.valid_len[row], p.width);
-  const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
-  const int vb = member * p.ord_span, ve = min(vb + p.ord_span, (v + 7) >> 3);
-  if (vb >= ve) return;
-  // the span in registers, as the one-workgroup kernel stages a row; its
-  // loads are issued first, to overlap those of the counts below
-  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride) + vb;
-  const int jt = (ve - vb - 1) / kOrdNT, rem = (ve - vb) - jt * kOrdNT;
-  uint4 raw[kOrdVPT];
-#pragma unroll
-  for (int j = 0; j < kOrdVPT; ++j)
-    raw[j] = ld_vec(src, (uint32_t)max(slot_vid<kOrdNT>(j, jt, rem, tid), 0));
-  // keys above and equal to T in the spans before this one
-  if (tid < 64) {
-    uint32_t a = 0, e = 0;
-    for (int m = tid; m < member; m += 64) {
-      const uint32_t x = p.ord_cnt[(size_t)lrow * p.ord_G + m];
-      a += x >> 16;
-      e += x & 0xFFFFu;
-    }
-    a = readlane(wave_incl_scan(a), 63);
-    e = readlane(wave_incl_scan(e), 63);
-    if (tid == 0) {
-      tmp[0] = a;
-      tmp[1] = e;
-    }
-  }
-  __syncthreads();
-  const uint32_t na = tmp[0], nt = tmp[1];
-  if (na >= cgt && nt >= (uint32_t)p.k - cgt) return;  // every slot taken before the span
-  uint32_t kb[MODE == TOPK_MODE_BLOCK ? kOrdVPT : 1];
-  if constexpr (MODE == TOPK_MODE_BLOCK) {
-#pragma unroll
-    for (int j = 0; j < kOrdVPT; ++j) {
-      const int lv = slot_vid<kOrdNT>(j, jt, rem, tid);
-      kb[j] = lv >= 0 ? (vb + lv == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
-    }
-  }
-  const Out o = row_out(p, row, MODE == TOPK_MODE_BLOCK);
-  ordered_regs<MODE, kOrdNT, kOrdVPT>(raw, kb, jt, rem, vb, v, T, cgt, na, nt, o, nullptr,
-                                      p.ids ? p.ids + (int64_t)row * p.k : nullptr, tmp + 2,
-                                      stage);
 }
 
 // ================================================================= host
@@ -2113,45 +2290,39 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   const int cv = kTeamNT * vpt;
   const int G = (nvec_max + cv - 1) / cv;  // <= kMaxMembers
   const size_t row_bytes = (size_t)G * kMemberWords * 4;
-  // ordered results: per row its threshold record and one count per
-  // order-pass member, after the slices
-  const int ord_span = kOrdNT * kOrdVPT;
-  const int ord_G = (nvec_max + ord_span - 1) / ord_span;
-  const size_t ord_row_bytes = ord ? (size_t)(2 + ord_G) * 4 : 0;
   // rows per launch: all of them, unless the scratch cap (or the caller's
   // fixed scratch) or kTeamBatch bounds a launch; a capped batch of 8 rows
   // or more holds whole groups of 8 (one per XCD), and every launch's grid
   // is padded to whole groups of 8 anyway
   const size_t cap_bytes = fixed ? fixed_bytes : kTeamScratchMax;
-  if (row_bytes + ord_row_bytes > cap_bytes)
+  if (row_bytes > cap_bytes)
     return fail(TOPK_ERR_UNSUPPORTED, "one row of width %d needs %zu bytes of team scratch, "
-                "more than the %zu available", width, row_bytes + ord_row_bytes, cap_bytes);
+                "more than the %zu available", width, row_bytes, cap_bytes);
   int batch = rows < kTeamBatch ? rows : kTeamBatch;
-  if ((size_t)batch * (row_bytes + ord_row_bytes) > cap_bytes) {
-    batch = (int)(cap_bytes / (row_bytes + ord_row_bytes));
+  if ((size_t)batch * row_bytes > cap_bytes) {
+    batch = (int)(cap_bytes / row_bytes);
     batch = batch < 8 ? batch : batch / 8 * 8;
   }
-  const size_t ord_bytes = (size_t)batch * ord_row_bytes;
   void* team_buf = fixed;
   if (!fixed) {
-    const int rc = get_scratch(stream, (size_t)batch * row_bytes + ord_bytes, &team_buf);
+    const int rc = get_scratch(stream, (size_t)batch * row_bytes, &team_buf);
     if (rc != TOPK_OK) return rc;
   }
   int rc = TOPK_OK;
   p.G = G;
   p.team_cv = cv;
   p.team_slices = static_cast<uint32_t*>(team_buf);
-  p.ord_G = ord_G;
-  p.ord_span = ord_span;
-  p.ord_rec = p.team_slices + (size_t)batch * row_bytes / 4;
-  p.ord_cnt = p.ord_rec + 2 * (size_t)batch;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  // stage as many survivor entries as the LDS of one workgroup holds
-  int cap = (device_lds_limit(dev) / 4 - kSelFixed) / 2;
-  cap = cap < kSelectMin ? kSelectMin : (cap > 32768 ? 32768 : cap);
-  p.sel_cap = cap;
-  const size_t sel_lds = (size_t)(kSelFixed + 2 * cap) * 4;
+  // select kernel LDS: its tables, then the direct path's bins or (ordered
+  // results) three bitmaps over one member's elements per wave
+  p.sel_bw = (cv * (mode == TOPK_MODE_BLOCK ? 1 : 8) + 31) / 32;
+  size_t sel_words = kDirectWords;
+  if (ord) {
+    const size_t bm = (size_t)3 * (kSelNT / 64) * p.sel_bw;
+    const size_t od = (size_t)2 * (kSelNT / 64) + TOPK_MAX_K;  // the ordered direct pass
+    sel_words = bm > sel_words ? bm : sel_words;
+    sel_words = od > sel_words ? od : sel_words;
+  }
+  const size_t sel_lds = (kSelWave + sel_words) * 4;
   for (int r0 = 0; r0 < rows; r0 += batch) {
     const int nr = (rows - r0) < batch ? (rows - r0) : batch;
     p.row0 = r0;
@@ -2171,13 +2342,6 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
       else
         rc = ord ? launch(topk_team_select<TOPK_MODE_TOKEN, true>, nr, kSelNT, sel_lds, stream, p)
                  : launch(topk_team_select<TOPK_MODE_TOKEN, false>, nr, kSelNT, sel_lds, stream, p);
-    }
-    if (rc == TOPK_OK && ord) {
-      if (mode == TOPK_MODE_BLOCK) {
-        rc = launch(topk_order_write<TOPK_MODE_BLOCK>, nr * ord_G, kOrdNT, 0, stream, p);
-      } else {
-        rc = launch(topk_order_write<TOPK_MODE_TOKEN>, nr * ord_G, kOrdNT, 0, stream, p);
-      }
     }
     if (rc != TOPK_OK) return rc;
   }
