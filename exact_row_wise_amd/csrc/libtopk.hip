@@ -33,12 +33,14 @@
 //     overflow sends the row to the direct path: two whole-row 8-bit radix
 //     histograms, every atomic spread over 8 replicated bins (lane mod 8);
 //   * rows wider than one workgroup's registers are split over a team of
-//     workgroups that share blockIdx % 8 (one XCD, one L2).  Every member
-//     derives the same cutoff from the same samples and writes its
-//     survivors to its own slice of global scratch; a second kernel, one
-//     1024-thread workgroup per row, reads them after the kernel boundary
-//     and finishes the row.  No workgroup ever waits for another, no atomic
-//     or fence crosses workgroups, and the scratch needs no reset.
+//     workgroups.  Every member derives the same cutoff from the same
+//     samples, then loads its chunk and writes its survivors, with a
+//     histogram of their keys relative to the cutoff, to its own slice of
+//     global scratch; a second kernel, one 1024-thread workgroup per row,
+//     takes the k-th key from the summed histograms after the kernel
+//     boundary and writes the row from the members' lists.  No workgroup
+//     ever waits for another, no atomic or fence crosses workgroups, and the
+//     scratch needs no reset.
 // There is no MFMA: this is a memory-bound selection, and all selection
 // arithmetic is on integer keys.
 
@@ -1316,9 +1318,7 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
 // A row wider than one workgroup is split over member workgroups of fixed
 // chunks of its valid length (G per row in the grid, for the widest row); a
 // second kernel, one workgroup per row, finishes it after the kernel
-// boundary.  The members of a row share
-// blockIdx % 8, so they run on one XCD and the row's samples, loaded by
-// every member, come from that XCD's L2 after the first.
+// boundary.
 
 // Stage 1: every member loads the row's samples (spread over the whole row,
 // the same in every member) and waits for them before its chunk loads go
@@ -1340,8 +1340,12 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   __shared__ __align__(16) uint32_t mh[kRelWords];
   __shared__ uint32_t bc[128];
   const int G = p.G;
+  // groups of 8 rows: member m of row r of a group runs on XCD (r + m) % 8
+  // (blockIdx % 8), which spreads the rows' members evenly over the XCDs
+  // whatever the rows' lengths
   const int b = blockIdx.x, xg = b & 7, yg = b >> 3;
-  const int lrow = (yg / G) * 8 + xg, member = yg % G;
+  const int member = yg % G;
+  const int lrow = (yg / G) * 8 + ((xg - member) & 7);
   if (lrow >= p.rows) return;
   const int row = p.row0 + lrow;
   const int tid = threadIdx.x;
@@ -1400,14 +1404,10 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
       }
     }
   }
-  // the chunk loads go out only now (the keys above waited for the samples)
-  asm volatile("" ::: "memory");
-  uint4 raw[VPT];
-#pragma unroll
-  for (int j = 0; j < VPT; ++j)
-    raw[j] = ld_vec(src, (uint32_t)(vb + max(slot_vid<NT>(j, jt, rem), 0)));
-
-  // -- the cutoff, identical in every member, while the chunk arrives
+  // -- the cutoff, identical in every member, before the chunk loads go
+  // out: issued behind every member's chunk, the samples would arrive late,
+  // and a wave issuing into the full memory queues stalls there; with the
+  // cutoff known, the filter takes each vector as it arrives
   const uint32_t S = block_sum<NT>(mine, bc + BC_TMP);  // also publishes the zeroed hists
   uint32_t sa, se;
   uint32_t c =
@@ -1443,6 +1443,12 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
     }
     return;
   }
+  // -- the chunk
+  asm volatile("" ::: "memory");
+  uint4 raw[VPT];
+#pragma unroll
+  for (int j = 0; j < VPT; ++j)
+    raw[j] = ld_vec(src, (uint32_t)(vb + max(slot_vid<NT>(j, jt, rem), 0)));
 
   // -- entries above the cutoff: compacted into this wave's region of the
   // sample-bin area (free once every wave has its cutoff).  Entries holding
@@ -1463,7 +1469,7 @@ __global__ __launch_bounds__(kTeamNT) void topk_team_filter(Params p) {
   const uint32_t dummy = lds_h8 + 8u * (uint32_t)lane;
   uint32_t at = first;
   uint32_t tcnt = 0, tw = 0, tkept = 0, neq = 0, tdrop = 0xFFFFFFFFu;
-  __syncthreads();  // every wave is done with the sample bins
+  __syncthreads();  // every wave is done with the sample bins (and the samples were waited for)
 #pragma unroll
   for (int j = 0; j < VPT; ++j) {
     if (j <= jt) {
@@ -1598,6 +1604,12 @@ __device__ __forceinline__ void emit_chunk(uint2 en, uint32_t g, int32_t Ts, uin
   }
 }
 
+// Survivor entry i of a member's list (i clamped into the list's region, so
+// that speculative loads past the list's end stay inside the slice).
+__device__ __forceinline__ uint2 ld_entry(const uint32_t* list, uint32_t i) {
+  return *reinterpret_cast<const uint2*>(list + 2 * min(i, (uint32_t)kMemberCap - 1u));
+}
+
 // Exclusive prefix of the set bits over the bitmap words bm[0, nw) of one
 // wave (nw a multiple of 64 or below it), into pre[0, nw).
 __device__ __forceinline__ void bitmap_prefix(const uint32_t* bm, uint32_t* pre, int nw) {
@@ -1657,6 +1669,8 @@ constexpr int kSelMhist = kSelMem + 16 * kMaxMembers;
 constexpr int kSelWave = kSelMhist + (kRelBins / 2) * kMaxMembers;
 enum { MT_E = 0, MT_TK = 1, MT_NQ = 2, MT_CUT = 3, MT_TW = 4, MT_GT = 8, MT_EQ = 9, MT_BASE = 10,
        MT_QUOTA = 11 };
+constexpr int kListBatch = 8;  // 64-entry chunks of a member's list loaded together
+constexpr int kListPre = 2;    // of them, loaded with the headers
 
 // Stage 2: one 1024-thread workgroup per row.  Short rows are written
 // directly.  Otherwise the members' headers, histograms and first entries
@@ -1670,8 +1684,10 @@ enum { MT_E = 0, MT_TK = 1, MT_NQ = 2, MT_CUT = 3, MT_TW = 4, MT_GT = 8, MT_EQ =
 // pass (the ties kept beside the lists); a misjudged cutoff, an overflow
 // of a member's list, or a k-th key 256 or more above the cutoff sends the
 // row to the direct path.
+// (one 1024-thread workgroup: 4 waves a SIMD, so each may hold 128 VGPRs)
 template <int MODE, bool ORD>
-__global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
+__global__ __launch_bounds__(kSelNT) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+topk_team_select(Params p) {
   constexpr int NT = kSelNT, NW = NT / 64;
   extern __shared__ uint32_t smem[];
   const int lrow = blockIdx.x;
@@ -1684,9 +1700,9 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
   const uint32_t* slices = p.team_slices + (size_t)lrow * G * kMemberWords;
   // -- loads that need not wait for the row's length: the headers (lane m
   // of wave 0: member m), the histograms (thread t: word t % 128 of
-  // members t / 128, + 8, ...) and the first 64 entries of the members this
-  // wave writes (wave, wave + NW, ...); the words of members past the row's
-  // end are stale, and dropped once the length is known
+  // members t / 128, + 8, ...) and the first kListPre 64-entry chunks of the
+  // members this wave writes (wave, wave + NW, ...); the words of members
+  // past the row's end are stale, and dropped once the length is known
   uint4 h0 = make_uint4(0u, 0u, 0u, 0u), h1 = h0, h2 = h0, h3 = h0;
   if (wave == 0 && lane < G) {
     const uint4* h4 = reinterpret_cast<const uint4*>(slices + (size_t)lane * kMemberWords);
@@ -1703,13 +1719,15 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     hw[i] = m < G ? slices[(size_t)m * kMemberWords + kMemberHistOfs + (tid & 127)] : 0u;
   }
   constexpr int kPreM = kMaxMembers / NW;
-  uint2 pre[kPreM];
+  uint2 pre[kPreM][kListPre];
 #pragma unroll
   for (int u = 0; u < kPreM; ++u) {
     const int m = wave + u * NW;
-    pre[u] = m < G ? *reinterpret_cast<const uint2*>(slices + (size_t)m * kMemberWords +
-                                                     kMemberList + 2 * lane)
-                   : make_uint2(kDeadPair, 0u);
+#pragma unroll
+    for (int c = 0; c < kListPre; ++c)
+      pre[u][c] = m < G ? ld_entry(slices + (size_t)m * kMemberWords + kMemberList,
+                                   (uint32_t)c * 64u + (uint32_t)lane)
+                        : make_uint2(kDeadPair, 0u);
   }
   const int v = clamp_len(p.valid_len[row], p.width);
   const int n = (MODE == TOPK_MODE_BLOCK) ? (v + 7) >> 3 : v;
@@ -1811,20 +1829,45 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
     }
     const uint32_t take = (uint32_t)k - cgt;
     if (!direct && !ORD) {
-      // -- unordered: every wave writes the lists of its members
+      // -- unordered: every wave writes the lists of its members.  The first
+      // kListBatch chunks of all of them are loaded together (the first one
+      // came with the headers), then written; longer lists follow in batches.
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
+      uint2 en[kPreM][kListBatch];
+      uint32_t Em[kPreM];
+#pragma unroll
+      for (int u = 0; u < kPreM; ++u) {
+        const int m = wave + u * NW;
+        Em[u] = m < gr ? mt[m * 16 + MT_E] : 0u;
+#pragma unroll
+        for (int c = 0; c < kListPre; ++c) en[u][c] = pre[u][c];
+        if (m < gr && Em[u] > kListPre * 64u) {
+          const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
+#pragma unroll
+          for (int c = kListPre; c < kListBatch; ++c)
+            en[u][c] = ld_entry(list, (uint32_t)c * 64u + (uint32_t)lane);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kPreM; ++u) {
         const int m = wave + u * NW;
         if (m < gr) {
-          const uint32_t Em = mt[m * 16 + MT_E];
           const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
           const uint32_t g = (uint32_t)m * chunk;
-          for (uint32_t b0 = 0; b0 < Em; b0 += 64) {
-            uint2 en = b0 == 0 ? pre[u] : *reinterpret_cast<const uint2*>(list + 2 * (b0 + lane));
-            if (b0 + lane >= Em) en = make_uint2(kDeadPair, 0u);
-            if (tie_pass) emit_chunk<MODE, true, false>(en, g, Ts, cgt, take, slot, o);
-            else emit_chunk<MODE, true, true>(en, g, Ts, cgt, take, slot, o);
+          const uint32_t E = Em[u];
+#pragma unroll
+          for (int c = 0; c < kListBatch; ++c) {
+            const uint32_t b0 = (uint32_t)c * 64u;
+            if (b0 < E) {
+              const uint2 e = b0 + lane < E ? en[u][c] : make_uint2(kDeadPair, 0u);
+              if (tie_pass) emit_chunk<MODE, true, false>(e, g, Ts, cgt, take, slot, o);
+              else emit_chunk<MODE, true, true>(e, g, Ts, cgt, take, slot, o);
+            }
+          }
+          for (uint32_t b0 = kListBatch * 64u; b0 < E; b0 += 64u) {
+            const uint2 e = b0 + lane < E ? ld_entry(list, b0 + lane) : make_uint2(kDeadPair, 0u);
+            if (tie_pass) emit_chunk<MODE, true, false>(e, g, Ts, cgt, take, slot, o);
+            else emit_chunk<MODE, true, true>(e, g, Ts, cgt, take, slot, o);
           }
           if (tie_pass) {
             // the first keys equal to the cutoff, from the tie regions
@@ -1833,10 +1876,10 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
             for (int w = 0; w < 4; ++w) {
               const uint32_t tw = mt[m * 16 + MT_TW + w];
               for (uint32_t b0 = 0; b0 < tw; b0 += 64) {
-                uint2 en = b0 + lane < tw ? *reinterpret_cast<const uint2*>(
-                                                tl + 2 * (w * kTieLCW + b0 + lane))
-                                          : make_uint2(kDeadPair, 0u);
-                emit_chunk<MODE, false, true>(en, g, Ts, cgt, take, slot, o);
+                uint2 e = b0 + lane < tw ? *reinterpret_cast<const uint2*>(
+                                               tl + 2 * (w * kTieLCW + b0 + lane))
+                                         : make_uint2(kDeadPair, 0u);
+                emit_chunk<MODE, false, true>(e, g, Ts, cgt, take, slot, o);
               }
             }
           }
@@ -1946,14 +1989,23 @@ __global__ __launch_bounds__(kSelNT) void topk_team_select(Params p) {
             sel[i] = 0;
             wk[i] = 0;
           }
-          // the entries at T: in the list (sampled path) or the tie regions
-          // (the lists' first chunks come from L2: the loads ahead brought them)
+          // the list's first kListBatch chunks in registers, for every pass
+          // below; the rest (long lists) read again per pass
+          uint2 en[kListBatch];
+#pragma unroll
+          for (int c = 0; c < kListBatch; ++c)
+            en[c] = ld_entry(list, (uint32_t)c * 64u + (uint32_t)lane);
           auto for_list = [&](auto&& f) {
-            for (uint32_t b0 = 0; b0 < Em; b0 += 64) {
-              const uint2 en = b0 + lane < Em
-                                   ? *reinterpret_cast<const uint2*>(list + 2 * (b0 + lane))
-                                   : make_uint2(kDeadPair, 0u);
-              f(en);
+#pragma unroll
+            for (int c = 0; c < kListBatch; ++c) {
+              const uint32_t b0 = (uint32_t)c * 64u;
+              if (b0 < Em) f(b0 + lane < Em ? en[c] : make_uint2(kDeadPair, 0u));
+            }
+            for (uint32_t b0 = kListBatch * 64u; b0 < Em; b0 += 64) {
+              const uint2 e = b0 + lane < Em
+                                  ? *reinterpret_cast<const uint2*>(list + 2 * (b0 + lane))
+                                  : make_uint2(kDeadPair, 0u);
+              f(e);
             }
           };
           auto for_ties = [&](auto&& f) {
@@ -2073,6 +2125,10 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
   std::lock_guard<std::mutex> lock(g_mu);
   Scratch& sc = g_scratch[std::make_pair(dev, stream)];
   if (sc.bytes < need) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+      return fail(TOPK_ERR_UNSUPPORTED, "the stream's team scratch (%zu bytes) must be set up by "
+                  "a call outside graph capture", need);
     if (sc.base) {
       e = hipStreamSynchronize(stream);
       if (e == hipSuccess) e = hipFree(sc.base);
