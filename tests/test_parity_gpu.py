@@ -227,6 +227,53 @@ def test_crafted_overflow_row_takes_direct_path():
     assert np.all(pc == T.PATH_DIRECT_OVERFLOW), pc
 
 
+def test_many_rows_mixed():
+    """More token rows than workgroups resident at once (the throughput
+    kernel): every kind of row next to every other in one launch, ragged and
+    short lengths, rows built to take each fallback, and the last rows of the
+    launch; on the sampled path and the forced direct path."""
+    rng = np.random.Generator(np.random.PCG64(2600))
+    rows, width, k = 2600, 16384, 512
+    kinds = ["normal", "bits", "ties", "negative", "neg_ties", "crowded"]
+    L = np.full((rows, width), W.POISON, np.uint16)
+    for i, kind in enumerate(kinds):
+        L[i::len(kinds)] = _random_rows(rng, L[i::len(kinds)].shape[0], width, kind)
+    pos = _sampled_positions_wg(width // 8)
+    mis = np.arange(100, 1300, 97)                       # misjudged rows
+    L[mis] = 0x3F00
+    L[np.ix_(mis, pos)] = (0x4000 + np.arange(pos.size) % 0x700).astype(np.uint16)
+    ovf = np.arange(150, 2600, 211)                      # overflowing rows
+    L[ovf] = W.f32_to_bf16_bits(np.abs(rng.standard_normal((ovf.size, width),
+                                                           dtype=np.float32)) + 1)
+    L[np.ix_(ovf, pos)] = 0x3C00
+    lens = np.full(rows, width, np.int32)
+    pick = rng.permutation(rows)
+    free = np.setdiff1d(pick, np.concatenate([mis, ovf]), assume_unique=False)
+    free = rng.permutation(free)
+    ragged, short = free[:400], free[400:650]
+    lens[ragged] = rng.integers(k + 1, width, size=ragged.size)
+    lens[short] = rng.integers(0, k + 1, size=short.size)
+    lens[free[650:660]] = [0, 1, k, k + 1, k + 7, width - 1, width - 8, -3, width + 9, 8 * 513 + 3]
+    lens[-3:] = [k, width, k + 1]                        # the launch's last rows
+    for r in range(rows):
+        L[r, max(0, min(int(lens[r]), width)):] = W.POISON
+    d = dict(logits=L, valid_len=lens, k=k, mode=0, width=width, pages=None, page_size=0)
+    o = run_oracle(d)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, o)
+    paths = _paths(pc)
+    print("paths", paths, flush=True)
+    assert -9 not in paths
+    assert np.all(pc[mis] == T.PATH_DIRECT_MISJUDGED), pc[mis]
+    assert np.all(pc[ovf] == T.PATH_DIRECT_OVERFLOW), pc[ovf]
+    assert paths.get(T.PATH_SHORT, 0) >= short.size
+    assert paths.get(T.PATH_SAMPLED, 0) > rows // 2
+    assert paths.get(T.PATH_SAMPLED_TIES, 0) > 0
+    g, pc = run_gpu(d, force_direct=True)
+    assert_parity(d, g, o)
+    assert set(_paths(pc)) <= {T.PATH_DIRECT_FORCED, T.PATH_SHORT}
+
+
 def _sampled_vectors_team(nvec, sv=1, nt=256):
     """Vectors every member of a token team samples for a row of nvec
     vectors (nvec > sv * nt): runs of 8 consecutive vectors, run r starting

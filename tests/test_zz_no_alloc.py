@@ -49,12 +49,15 @@ def _token_rows(rows, width, seed):
 
 def test_noalloc_matches_allocating_entry_point():
     # 20 rows of 2^20 tokens: several batches of the fixed scratch; then
-    # smaller calls on the same scratch: block rows, crowded rows with a
-    # block table, one-workgroup rows
+    # smaller calls on the same scratch: more one-workgroup rows than
+    # resident workgroups, block rows, crowded rows with a block table,
+    # one-workgroup rows, and many rows again
     cases = [("token 20 x 2^20", _token_rows(20, 1 << 20, 61)),
+             ("many rows 3000 x 16384", W.make(5, rows=3000, seed=66)),
              ("block 12 x 2^20", W.make(4, rows=12, seed=62)),
              ("crowded 7 x 150000", W.make(3, rows=7, seed=63)),
-             ("paged 40 x 16384", W.make(2, rows=40, seed=64))]
+             ("paged 40 x 16384", W.make(2, rows=40, seed=64)),
+             ("many rows 2100 x 16384", W.make(5, rows=2100, seed=67))]
     for name, d in cases:
         print(f"no-alloc case {name}", flush=True)
         got = _run(T.topk_bf16_rows_noalloc, d)
