@@ -13,7 +13,9 @@ from ._binding import (  # noqa: F401
     PATH_DIRECT_OVERFLOW,
     PATH_SAMPLED,
     PATH_SAMPLED_TIES,
+    PATH_DIRECT_DENSE,
     PATH_SHORT,
+    PATH_TOPS,
     TopkError,
     library,
     probe_library,
@@ -24,4 +26,6 @@ from ._binding import (  # noqa: F401
     release_scratch,
     status_string,
     topk_bf16_rows,
+    topk_bf16_rows_tops,
+    vector_maxima,
 )

@@ -23,6 +23,8 @@ PATH_SAMPLED_TIES = 2
 PATH_DIRECT_FORCED = 3
 PATH_DIRECT_MISJUDGED = 4
 PATH_DIRECT_OVERFLOW = 5
+PATH_TOPS = 6
+PATH_DIRECT_DENSE = 7
 
 ERR_UNSUPPORTED = -4
 
@@ -80,6 +82,13 @@ def library():
         lib.topk_bf16_rows_ordered_ex.argtypes = osig + [ctypes.POINTER(_Options),
                                                          ctypes.c_void_p]
         lib.topk_bf16_rows_ordered_ex.restype = ctypes.c_int
+        lib.topk_bf16_rows_tops.argtypes = sig[:7] + [ctypes.c_void_p, ctypes.c_int64] + sig[7:] + [
+            ctypes.POINTER(_Options), ctypes.c_void_p]
+        lib.topk_bf16_rows_tops.restype = ctypes.c_int
+        lib.topk_bf16_vector_maxima.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                ctypes.c_int64, ctypes.c_void_p]
+        lib.topk_bf16_vector_maxima.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_last_error.argtypes = []
@@ -176,6 +185,62 @@ def topk_bf16_rows_noalloc(logits: torch.Tensor, valid_len: torch.Tensor, k: int
                  stream, noalloc=True)[0]
 
 
+def topk_bf16_rows_tops(logits: torch.Tensor, valid_len: torch.Tensor, k: int, tops: torch.Tensor,
+                        mode=MODE_TOKEN, block_table: torch.Tensor | None = None,
+                        page_size: int = 64, out: torch.Tensor | None = None,
+                        width: int | None = None, force_direct: bool = False,
+                        path_codes: torch.Tensor | None = None,
+                        stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """topk_bf16_rows given the rows' vector maxima (see include/libtopk.h):
+    tops is [rows, >= ceil(width / 8)] 16-bit (int16/uint16) on the GPU, unit
+    stride along a row, the row stride a multiple of 8, 16-byte aligned, each
+    entry the largest key of its 8 logits below the valid length (0 where
+    none is), as vector_maxima writes it.  Other arguments as for
+    topk_bf16_rows.  Returns out."""
+    return _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
+                 path_codes, stream, tops=tops)[0]
+
+
+def vector_maxima(logits: torch.Tensor, valid_len: torch.Tensor, width: int | None = None,
+                  tops: torch.Tensor | None = None,
+                  stream: torch.cuda.Stream | None = None) -> torch.Tensor:
+    """The side array topk_bf16_rows_tops reads (topk_bf16_vector_maxima in
+    include/libtopk.h): tops[r, j] = the largest key among logits 8j .. 8j+7
+    of row r below valid_len[r], 0 where none is.  tops (int16 [rows,
+    >= ceil(width / 8) rounded up to 8], unit stride along a row, row stride a
+    multiple of 8) is allocated if None.  Returns tops."""
+    lib = library()
+    if logits.dim() != 2 or logits.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("logits must be 2-D 16-bit [rows, row_stride]")
+    rows = logits.shape[0]
+    if width is None:
+        width = logits.shape[1]
+    if int(width) < 0 or int(width) > logits.shape[1]:
+        raise ValueError(f"width {width} outside [0, logits.shape[1] = {logits.shape[1]}]")
+    if logits.shape[1] > 1 and logits.stride(1) != 1:
+        raise ValueError("logits rows must have unit stride")
+    dev = logits.device
+    if valid_len.dtype != torch.int32 or valid_len.numel() != rows or valid_len.device != dev:
+        raise ValueError("valid_len must be int32 [rows] on the same GPU")
+    valid_len = valid_len.contiguous()
+    nv = -(-int(width) // 8)
+    if tops is None:
+        tops = torch.zeros((rows, max(8, -(-nv // 8) * 8)), dtype=torch.int16, device=dev)
+    elif (tops.dtype not in (torch.int16, torch.uint16) or tops.dim() != 2
+          or tops.shape[0] != rows or tops.shape[1] < nv or tops.device != dev
+          or (rows > 0 and tops.shape[1] > 1 and tops.stride(1) != 1)):
+        raise ValueError("tops must be 16-bit [rows, >= ceil(width / 8)] on the same GPU")
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.topk_bf16_vector_maxima(logits.data_ptr(), int(logits.stride(0)),
+                                         valid_len.data_ptr(), int(rows), int(width),
+                                         tops.data_ptr(), int(tops.stride(0)),
+                                         ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise TopkError(rc, lib.topk_last_error().decode())
+    return tops
+
+
 def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int,
                            mode=MODE_TOKEN, block_table: torch.Tensor | None = None,
                            page_size: int = 64, out: torch.Tensor | None = None,
@@ -194,7 +259,7 @@ def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int
 
 def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_direct,
           path_codes, stream, ordered=False, valid=None, ids=None, want_ids=False,
-          noalloc=False):
+          noalloc=False, tops=None):
     lib = library()
     if logits.dim() != 2:
         raise ValueError("logits must be 2-D [rows, row_stride]")
@@ -240,6 +305,14 @@ def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_
             raise ValueError(f"block_table rows hold {block_table.shape[1]} pages; width "
                              f"{width} needs ceil(width / page_size) of them")
         bt = _BlockTable(block_table.data_ptr(), block_table.stride(0), int(page_size))
+    if tops is not None:
+        if (tops.dtype not in (torch.int16, torch.uint16) or tops.dim() != 2
+                or tops.shape[0] != rows or tops.device != dev
+                or (rows > 0 and tops.shape[1] > 1 and tops.stride(1) != 1)):
+            raise ValueError("tops must be 16-bit [rows, >= ceil(width / 8)] on the same GPU")
+        if tops.shape[1] < -(-int(width) // 8):
+            raise ValueError(f"tops rows hold {tops.shape[1]} maxima; width {width} needs "
+                             f"ceil(width / 8) of them")
     opts = None
     if force_direct or path_codes is not None:
         if path_codes is not None and (path_codes.dtype != torch.int32
@@ -262,6 +335,10 @@ def _call(logits, valid_len, k, mode, block_table, page_size, out, width, force_
                 rc = lib.topk_bf16_rows_ordered_ex(*args, ctypes.byref(opts), st)
         elif noalloc:
             rc = lib.topk_bf16_rows_noalloc(*args, st)
+        elif tops is not None:
+            targs = args[:7] + (tops.data_ptr(), int(tops.stride(0))) + args[7:]
+            rc = lib.topk_bf16_rows_tops(*targs, ctypes.byref(opts) if opts is not None else None,
+                                         st)
         elif opts is None:
             rc = lib.topk_bf16_rows(*args, st)
         else:

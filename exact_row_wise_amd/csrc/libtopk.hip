@@ -162,6 +162,12 @@ struct Params {
   int32_t ord;           // 1: ordered results, with counts and logical ids
   int32_t* valid;        // [rows] counts, or null
   int32_t* ids;          // [rows][k] logical element indices, or null
+  // vector-max bound: the producer's maxima of every 8 logits, and the LDS
+  // word offset of the per-wave hot-vector lists
+  const uint16_t* tops;  // [rows][tops_stride], or null
+  int64_t tops_stride;
+  int32_t hot_lds;
+  int32_t tops_lo;       // LDS word offset of the bound's low-byte bins
 };
 
 // ------------------------------------------------------------------ keys
@@ -232,6 +238,14 @@ __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
 // Overwrite elements r..7 of one staged vector (r valid elements, 0..8)
 // with 0xFFFF, whose key is 0 and whose signed value is -1: such an element
 // is never above a cutoff.  Only the last occupied vector slot needs it.
+// The first r of the 8 halves of v kept, the rest zeroed.
+__device__ __forceinline__ void keep_first(uint4& v, int r) {
+  v.x &= r >= 2 ? 0xFFFFFFFFu : (r == 1 ? 0x0000FFFFu : 0u);
+  v.y &= r >= 4 ? 0xFFFFFFFFu : (r == 3 ? 0x0000FFFFu : 0u);
+  v.z &= r >= 6 ? 0xFFFFFFFFu : (r == 5 ? 0x0000FFFFu : 0u);
+  v.w &= r >= 8 ? 0xFFFFFFFFu : (r == 7 ? 0x0000FFFFu : 0u);
+}
+
 __device__ __forceinline__ void poison_tail(uint4& v, int r) {
   v.x |= r >= 2 ? 0u : (r == 1 ? 0xFFFF0000u : 0xFFFFFFFFu);
   v.y |= r >= 4 ? 0u : (r == 3 ? 0xFFFF0000u : 0xFFFFFFFFu);
@@ -1071,12 +1085,12 @@ __device__ void short_ids(const Params& p, int row, int n, int tid = (int)thread
   if (p.valid && tid == 0) p.valid[row] = n;
 }
 
+// One row of the one-workgroup kernel.
 template <int MODE, int NT, int VPT, bool ONE, bool ORD>
-__global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
+__device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
   constexpr int NW = NT / 64;
   extern __shared__ uint32_t smem[];
   const uint32_t lds0 = lds_addr(smem);
-  const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = __lane_id();
   const int wave = tid >> 6;
@@ -1312,7 +1326,339 @@ __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
   set_path(p, row, code);
 }
 
+template <int MODE, int NT, int VPT, bool ONE, bool ORD>
+__global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
+  rows_wg_body<MODE, NT, VPT, ONE, ORD>(p, blockIdx.x);
+}
 
+
+
+// ============================================ the vector-max bound
+// A producer's side array of the largest key of every aligned group of 8
+// logits (vLLM kimi_k3 indexer page, IndexerScore epilogue: each 8 logits'
+// largest key, a side array 1/8 of the row) bounds the k-th key from below:
+// the k-th largest of those maxima, `low`, is the largest key of k distinct
+// groups, so at least k keys lie at or above it (the same page,
+// IndexerSelect passes 1 and 2).  Every key at or above low lies in a group
+// whose maximum reaches low ("hot" vectors, about k of them on smooth data),
+// so those groups alone are loaded; the survivors are their keys at or above
+// low, and the exact select runs over them as on the sampled path.
+
+constexpr int kHotWave = 256;  // hot vectors one wave gathers at most (4 per lane)
+constexpr int kTopsTPT = 8;    // 16-byte words of maxima per thread at most
+constexpr int kTopsLC = 8;     // copies of the bound's low-byte bins (lane mod 8)
+// Copies of the bound's high-byte bins (lane mod HC): 8 for rows of one
+// word of maxima per thread (at most 2048 maxima, 4 atomics a lane), 32 for
+// wider rows; a copy's stride puts the copies of one bin in distinct banks
+// (260 = 4 mod 32 for 8 copies, 289 = 1 mod 32 for 32), with spare words
+// past the bins.
+template <int TPT> struct TopsBins {
+  static constexpr int HC = TPT == 1 ? 8 : 32;
+  static constexpr int STRIDE = TPT == 1 ? 260 : 289;
+  static constexpr int WORDS = HC * STRIDE + 256;  // the copies, then their sums
+};
+
+
+// The q-th largest of a row's vector maxima, held 8 to a 16-byte word (word
+// wi[j] in slot j, -1 for none, not counted; maxima of no vector are 0): the
+// two 8-bit radix passes of sample_cutoff over every maximum, with more
+// copies of the bins, since every maximum costs an atomic and the maxima of
+// crowded rows share a few bins: TopsBins<TPT> copies of the high-byte bins
+// at h8 (TopsBins<TPT>::WORDS zeroed words; the sums go after the copies)
+// and kTopsLC copies of the low-byte bins at lo8 (kTopsLC kRelStride zeroed
+// words).
+template <int NT, int TPT>
+__device__ uint32_t tops_cutoff(const uint4 (&tw)[TPT], const int (&wi)[TPT], int jt,
+                                uint32_t q, uint32_t* h8, uint32_t* lo8, int tid) {
+  constexpr int HC = TopsBins<TPT>::HC, STRIDE = TopsBins<TPT>::STRIDE;
+  const int lane = tid & 63;
+  const uint32_t copy = (uint32_t)lane & (HC - 1);
+  // every lane adds every slot (no branch around the atomics): a slot past
+  // the row counts into one of its copy's 4 spare words past the bins
+  uint32_t* const hc = h8 + copy * STRIDE;
+  const uint32_t hspill = 256u + (((uint32_t)lane / HC) & 3u);
+  static_assert(STRIDE >= 260, "four spare words per copy of the high-byte bins");
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    if (j > jt) break;  // (uniform: the slots past jt hold no word)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t t = half_of(word_of(tw[j], e >> 1), e & 1);
+      atomicAdd(&hc[wi[j] >= 0 ? 255u - (t >> 8) : hspill], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* sums = h8 + HC * STRIDE;
+  if (tid < 256) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int c = 0; c < HC; ++c) t += h8[c * STRIDE + tid];
+    sums[tid] = t;
+  }
+  __syncthreads();
+  uint32_t i1, a1;
+  find_desc(sums, q, i1, a1, tid);
+  const uint32_t b1 = 255u - i1;
+  uint32_t* const loc = lo8 + (lane % kTopsLC) * kRelStride;
+  const uint32_t spill = 256u + (((uint32_t)lane / kTopsLC) & 15u);
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    if (j > jt) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t t = half_of(word_of(tw[j], e >> 1), e & 1);
+      atomicAdd(&loc[wi[j] >= 0 && (t >> 8) == b1 ? 255u - (t & 255u) : spill], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t i2, a2, t2;
+  find_copies<kTopsLC, kRelStride>(lo8, q - a1, i2, a2, t2, nullptr, tid);
+  return (b1 << 8) | (255u - i2);
+}
+
+// One token row (v > k, at least 2k vectors) on the vector-max bound: the
+// maxima are staged, low is found, each wave lists its hot vectors in its
+// LDS region and loads them (up to kHotWave), keeps their keys at or above
+// low in its survivor region, and the exact select writes the row.  A wave
+// with more hot vectors than it holds, or survivors beyond the regions, or a
+// bound of 0 (the keys past the length are 0) sends the row to the direct
+// path.  A workgroup of NT threads holds NT TPT 16-byte words of maxima.
+template <int NT, int TPT, bool ONE>
+__device__ __forceinline__ void tops_body(const Params& p, const int row, const int v,
+                                          const Out o) {
+  constexpr int NW = NT / 64, GPL = kHotWave / 64;
+  extern __shared__ uint32_t smem[];
+  const uint32_t lds0 = lds_addr(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k;
+  const int nvec = (v + 7) >> 3, ntw = (nvec + 7) >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+  const uint4* tsrc = reinterpret_cast<const uint4*>(p.tops + (int64_t)row * p.tops_stride);
+  uint32_t* sh = smem + kSampHist;
+  uint32_t* rel = smem + kRelHist;
+  uint32_t* bc = smem + kBc;
+  uint32_t* lists = smem + kLists;
+  int32_t* lpages = (p.page_lds && o.pages) ? reinterpret_cast<int32_t*>(smem + p.page_lds)
+                                            : nullptr;
+  // the bound's bins: TopsBins words at the start of the survivor area, the
+  // low-byte copies at p.tops_lo, past the survivor regions (which fill as
+  // soon as a wave has the bound, while others may still read those copies)
+  uint32_t* lo8 = smem + p.tops_lo;
+  // zero the relative histogram and the bound's bins
+  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = tid; i < (kRelHist - kSampHist + kRelWords) / 4; i += NT)
+    reinterpret_cast<uint4*>(sh)[i] = z4;
+  for (int i = tid; i < TopsBins<TPT>::WORDS / 4; i += NT) reinterpret_cast<uint4*>(lists)[i] = z4;
+  for (int i = tid; i < kTopsLC * kRelStride / 4; i += NT) reinterpret_cast<uint4*>(lo8)[i] = z4;
+  if (tid == 0) {
+    bc[BC_SLOT] = 0;
+    bc[BC_SLOT + 1] = 0;
+  }
+  // -- the maxima, in the slots of the sampled path's vectors (the last
+  // occupied slot shared out evenly over the waves, so that every wave lists
+  // about as many hot vectors); a lane without a word in a slot reads word 0
+  // and counts none of it
+  const int jt = (ntw - 1) / NT, rem = ntw - jt * NT;
+  uint4 tw[TPT];
+  int wi[TPT];
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) {
+    wi[j] = slot_vid<NT>(j, jt, rem, tid);
+    tw[j] = ld_vec(tsrc, (uint32_t)max(wi[j], 0));
+  }
+  // maxima of no vector of the row (past nvec, or a slot without a word)
+  // become 0: they then fall in the bottom bin of the bound's histogram,
+  // below the k-th largest of the row's own 2k or more maxima unless that
+  // is 0 too (the row then takes the direct path), and are never hot
+#pragma unroll
+  for (int j = 0; j < TPT; ++j) keep_first(tw[j], wi[j] >= 0 ? clamp8(nvec - 8 * wi[j]) : 0);
+  // the row's block-table entries ride along, for an LDS copy
+  constexpr int PPT = kPageLdsMax / NT;
+  int32_t pgv[PPT];
+  const int npg = lpages ? (v + (1 << p.page_shift) - 1) >> p.page_shift : 0;
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int i = j * NT + tid;
+    pgv[j] = i < npg ? o.pages[i] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < PPT; ++j) {
+    const int i = j * NT + tid;
+    if (i < npg) lpages[i] = pgv[j];
+  }
+  __syncthreads();  // histograms zeroed, block-table copy complete
+  const uint32_t low = tops_cutoff<NT, TPT>(tw, wi, jt, (uint32_t)k, lists, lo8, tid);
+
+  int code = TOPK_PATH_TOPS;
+  bool direct = false;
+  if (low == 0u) {
+    direct = true;
+    code = TOPK_PATH_DIRECT_MISJUDGED;
+  } else {
+    // -- this wave's hot vectors, listed in its LDS region: each lane
+    // counts its own, one wave scan gives its offset, then every lane
+    // stores every slot, a cold one (or one past the region) into a word of
+    // its own after the wave's kHotWave entries
+    uint32_t* hot = smem + p.hot_lds + wave * (kHotWave + 64);
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      if (j > jt) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t t = half_of(word_of(tw[j], e >> 1), e & 1);
+        mine += t >= low ? 1u : 0u;
+      }
+    }
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t hc = readlane(incl, 63);  // wave-uniform
+    uint32_t pos = incl - mine;
+    const uint32_t cold = (uint32_t)kHotWave + (uint32_t)lane;
+#pragma unroll
+    for (int j = 0; j < TPT; ++j) {
+      if (j > jt) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t t = half_of(word_of(tw[j], e >> 1), e & 1);
+        const bool h = t >= low;
+        hot[h && pos < (uint32_t)kHotWave ? pos : cold] = (uint32_t)(wi[j] * 8 + e);
+        pos += h ? 1u : 0u;
+      }
+    }
+    const uint32_t hn = min(hc, (uint32_t)kHotWave);
+    // -- load them: lane l takes entries l, l + 64, ... of the list
+    int gv[GPL];
+    uint4 g[GPL];
+#pragma unroll
+    for (int u = 0; u < GPL; ++u) {
+      const uint32_t i = (uint32_t)(u * 64 + lane);
+      gv[u] = i < hn ? (int)hot[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < GPL; ++u)
+      if ((uint32_t)(u * 64) < hn) g[u] = ld_vec(src, (uint32_t)max(gv[u], 0));
+    // -- their keys at or above low (above cs = low - 1), compacted as on
+    // the sampled path; a lane without a listed vector keeps nothing
+    const int32_t cs = (int32_t)low - 1 - 0x8000;
+    const uint32_t cap = (uint32_t)p.lcw;
+    const uint32_t wbase = readfirst((uint32_t)wave) * (cap + kSpare);
+    uint32_t* seg = lists + 2 * wbase;
+    const uint32_t first = lds0 + 4u * (kLists + 2u * wbase);
+    const uint32_t lim = first + cap * 8u;
+    uint32_t at = first;
+    const uint32_t dummy = lds0 + 4u * (kLists + 2u * (NW * (cap + kSpare) + lane));
+#pragma unroll
+    for (int u = 0; u < GPL; ++u) {
+      if ((uint32_t)(u * 64) < hn) {
+        uint4 x = g[u];
+        poison_tail(x, gv[u] >= 0 ? clamp8(v - 8 * gv[u]) : 0);
+        const uint32_t e8 = (uint32_t)max(gv[u], 0) * 8u;
+        if (cs >= 0) {
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) keep_word_lds(word_of(x, q2), e8 + 2 * q2, cs, lim, dummy, at);
+        } else {
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2)
+            keep_word_lds(skey2(word_of(x, q2)), e8 + 2 * q2, cs, lim, dummy, at);
+        }
+      }
+    }
+    const uint32_t wcnt = (at - first) / 8u;
+    // a wave with hot vectors it could not list reports a count past the
+    // cap: the select then routes the row to the direct path
+    if (lane == 0) bc[BC_CNT + wave] = hc > (uint32_t)kHotWave ? cap + 1u : wcnt;
+    lds_store2(min(at, lim) + 8u * lane, kDeadPair, 0u);
+    const int st = select_and_write<TOPK_MODE_TOKEN, NW, ONE>(seg, min(wcnt, cap), cs, (uint32_t)k,
+                                                              rel, sh, bc, cap, o, lpages, false,
+                                                              nullptr, tid);
+    if (st != SEL_DONE) {
+      // (fewer than k keys at or above low: maxima that break their
+      // definition)
+      direct = true;
+      code = st == SEL_OVERFLOW ? TOPK_PATH_DIRECT_OVERFLOW : TOPK_PATH_DIRECT_MISJUDGED;
+    }
+  }
+  if (direct) {
+    __syncthreads();
+    direct_select<TOPK_MODE_TOKEN, NT>(src, v, v, k, o, lists, bc, false, nullptr, tid);
+  }
+  set_path(p, row, code, tid);
+}
+
+// Token rows with their vector maxima, one workgroup per row: n <= k rows
+// as always; rows with fewer than 2k vectors (where the k-th largest
+// maximum bounds loosely) on the sampled path when they fit its registers
+// (16384 logits), else on the direct path; the rest on the bound.
+template <int TPT, bool ONE>
+__global__ __launch_bounds__(kRowNT) void topk_rows_tops(Params p) {
+  const int row = blockIdx.x;
+  const int v = clamp_len(p.valid_len[row], p.width);
+  const int k = p.k;
+  const Out o = row_out(p, row, false);
+  if (v <= k) {
+    write_short_token<kRowNT>(o, v, k);
+    set_path(p, row, TOPK_PATH_SHORT);
+    return;
+  }
+  if ((v + 7) >> 3 < 2 * k) {
+    if (v <= kRowNT * kRowTokenVPT * 8) {
+      rows_wg_body<TOPK_MODE_TOKEN, kRowNT, kRowTokenVPT, ONE, false>(p, row);
+    } else {
+      extern __shared__ uint32_t smem[];
+      const uint4* src = reinterpret_cast<const uint4*>(p.logits + (int64_t)row * p.row_stride);
+      direct_select<TOPK_MODE_TOKEN, kRowNT>(src, v, v, k, o, smem + kLists, smem + kBc);
+      set_path(p, row, TOPK_PATH_DIRECT_DENSE);
+    }
+    return;
+  }
+  tops_body<kRowNT, TPT, ONE>(p, row, v, o);
+}
+
+// The producer's side array, for callers whose scorer does not write it:
+// tops[r][j] = the largest key among logits 8j .. 8j+7 of row r below its
+// valid length, 0 where none is, for every j < ceil(width / 8) (and the
+// rest of the 16-byte word holding the last one).  One thread per 16-byte
+// word of maxima (8 vectors of 8 logits).
+struct MaxParams {
+  const uint16_t* logits;
+  int64_t row_stride;
+  const int32_t* valid_len;
+  int32_t width;
+  uint16_t* tops;
+  int64_t tops_stride;
+};
+
+__global__ __launch_bounds__(256) void topk_vector_maxima(MaxParams q, int rows) {
+  const int w = blockIdx.x * 256 + threadIdx.x;  // word of maxima
+  const int nvw = (q.width + 7) >> 3;            // vectors of the width
+  if (w * 8 >= nvw) return;
+  for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+  const int v = clamp_len(q.valid_len[row], q.width);
+  const int nvec = (v + 7) >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(q.logits + (int64_t)row * q.row_stride);
+  uint4 x[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int vid = w * 8 + e;
+    x[e] = vid < nvec ? ld_vec(src, (uint32_t)vid) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  uint32_t t[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int vid = w * 8 + e;
+    uint32_t m = 0;
+    if (vid < nvec) {
+      poison_tail(x[e], clamp8(v - 8 * vid));  // logits past the length: key 0
+#pragma unroll
+      for (int h = 0; h < 8; ++h) m = max(m, key1(half_of(word_of(x[e], h >> 1), h & 1)));
+    }
+    t[e] = m;
+  }
+  *reinterpret_cast<uint4*>(q.tops + (int64_t)row * q.tops_stride + (int64_t)w * 8) =
+      make_uint4(t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16),
+                 t[6] | (t[7] << 16));
+  }
+}
 
 // ============================================ team of workgroups per row
 // A row wider than one workgroup is split over member workgroups of fixed
@@ -2268,10 +2614,37 @@ int launch_rows(int mode, int rows, size_t lds, hipStream_t stream, const Params
                 lds, stream, p);
 }
 
+// Rows on the vector-max bound: for one word of maxima per thread, the
+// latency variant while every row's workgroup is resident, else the
+// throughput variant; wider rows are few.
+int launch_tops(int tpt, int rows, size_t lds, hipStream_t stream, const Params& p) {
+  if (tpt == 1) {
+    auto lat = topk_rows_tops<1, false>;
+    if (rows <= resident_grid(reinterpret_cast<const void*>(lat), kRowNT, lds))
+      return launch(lat, rows, kRowNT, lds, stream, p);
+    return launch(topk_rows_tops<1, true>, rows, kRowNT, lds, stream, p);
+  }
+  if (tpt == 2) return launch(topk_rows_tops<2, false>, rows, kRowNT, lds, stream, p);
+  if (tpt == 4) return launch(topk_rows_tops<4, false>, rows, kRowNT, lds, stream, p);
+  return launch(topk_rows_tops<8, false>, rows, kRowNT, lds, stream, p);
+}
+
+// Validation of a side array of vector maxima: 16-byte aligned rows of at
+// least ceil(width / 8) entries.
+int check_tops(const uint16_t* tops, int64_t tops_stride, int32_t width) {
+  if (!tops) return fail(TOPK_ERR_INVALID_ARG, "null vector maxima");
+  if (((uintptr_t)tops & 15u) != 0 || tops_stride % 8 != 0)
+    return fail(TOPK_ERR_MISALIGNED, "vector maxima rows not 16-byte aligned");
+  if (tops_stride < ((int64_t)width + 7) / 8)
+    return fail(TOPK_ERR_INVALID_ARG, "vector maxima rows shorter than ceil(width / 8)");
+  return TOPK_OK;
+}
+
 int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, int32_t rows,
         int32_t width, int32_t k, int32_t mode, const topk_block_table_t* bt, int32_t* out,
         const topk_options_t* opt, int ord, int32_t* valid, int32_t* ids, void* stream_ptr,
-        void* fixed = nullptr, size_t fixed_bytes = 0) {
+        void* fixed = nullptr, size_t fixed_bytes = 0, const uint16_t* tops = nullptr,
+        int64_t tops_stride = 0) {
   g_err[0] = '\0';
   if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
   if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, TOPK_MAX_K);
@@ -2316,9 +2689,38 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   p.valid = ord ? valid : nullptr;
   p.ids = ord ? ids : nullptr;
 
+  const int nvec_max = (width + 7) / 8;
+  // the vector maxima, when given, serve token rows (unordered results) of
+  // at least 2k vectors and at most kTopsTPT words of maxima per thread:
+  // one workgroup per row, whatever the width
+  if (tops && mode == TOPK_MODE_TOKEN && !ord && !p.force_direct && nvec_max >= 2 * k &&
+      nvec_max <= kRowNT * 8 * kTopsTPT) {
+    p.tops = tops;
+    p.tops_stride = tops_stride;
+    p.rows = rows;
+    p.row0 = 0;
+    p.lcw = row_lcw(k, kRowNT / 64);
+    const int ntw = (nvec_max + 7) / 8;
+    const int tpt = ntw <= kRowNT ? 1 : ntw <= 2 * kRowNT ? 2 : ntw <= 4 * kRowNT ? 4 : 8;
+    // the survivor area holds the bound's high-byte bins first; its
+    // low-byte bins lie past both those and the survivor regions
+    const int regions = (kRowNT / 64) * (p.lcw + kSpare) * 2 + 2 * 64;
+    const int h8 = tpt == 1 ? TopsBins<1>::WORDS : TopsBins<2>::WORDS;
+    const int lo = kLists + ((regions > h8 ? regions : h8) + 3) / 4 * 4;
+    p.tops_lo = lo;
+    size_t lds = row_lds_bytes(p.lcw, kRowNT / 64);
+    const size_t lo_end = (size_t)(lo + kTopsLC * kRelStride) * 4;
+    if (lds < lo_end) lds = lo_end;
+    p.hot_lds = (int32_t)(lds / 4);
+    lds += (size_t)(kRowNT / 64) * (kHotWave + 64) * 4;
+    if (bt && ((int64_t)width + bt->page_size - 1) / bt->page_size <= kPageLdsMax) {
+      p.page_lds = (int32_t)(lds / 4);
+      lds += (size_t)kPageLdsMax * 4;
+    }
+    return launch_tops(tpt, rows, lds, stream, p);
+  }
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
-  const int nvec_max = (width + 7) / 8;
   const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kRowBlockVPT : kRowTokenVPT);
   if (nvec_max <= cap_wg) {
     p.rows = rows;
@@ -2432,6 +2834,53 @@ int topk_bf16_rows_noalloc(const uint16_t* logits, int64_t row_stride, const int
   if (rc != TOPK_OK) return rc;
   return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr, 0,
              nullptr, nullptr, stream, ptr, kNoAllocBytes);
+}
+
+int topk_bf16_rows_tops(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
+                        int32_t rows, int32_t width, int32_t k, int32_t mode,
+                        const uint16_t* tops, int64_t tops_stride,
+                        const topk_block_table_t* block_table, int32_t* out,
+                        const topk_options_t* options, void* stream) {
+  g_err[0] = '\0';
+  if (mode == TOPK_MODE_TOKEN && rows > 0) {
+    const int rc = check_tops(tops, tops_stride, width);
+    if (rc != TOPK_OK) return rc;
+  }
+  return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, options, 0,
+             nullptr, nullptr, stream, nullptr, 0, mode == TOPK_MODE_TOKEN ? tops : nullptr,
+             tops_stride);
+}
+
+int topk_bf16_vector_maxima(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
+                            int32_t rows, int32_t width, uint16_t* tops, int64_t tops_stride,
+                            void* stream) {
+  g_err[0] = '\0';
+  if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
+  if (width < 0 || width > TOPK_MAX_WIDTH)
+    return fail(TOPK_ERR_INVALID_ARG, "width = %d outside [0, %d]", width, TOPK_MAX_WIDTH);
+  if (row_stride < width) return fail(TOPK_ERR_INVALID_ARG, "row_stride < width");
+  if (row_stride % 8 != 0) return fail(TOPK_ERR_MISALIGNED, "row_stride not a multiple of 8");
+  if (rows == 0 || width == 0) return TOPK_OK;
+  if (!logits || !valid_len) return fail(TOPK_ERR_INVALID_ARG, "null pointer");
+  if (((uintptr_t)logits & 15u) != 0) return fail(TOPK_ERR_MISALIGNED, "logits not 16-byte aligned");
+  if (((uintptr_t)valid_len & 3u) != 0)
+    return fail(TOPK_ERR_MISALIGNED, "valid_len not 4-byte aligned");
+  const int rc = check_tops(tops, tops_stride, width);
+  if (rc != TOPK_OK) return rc;
+  MaxParams q;
+  q.logits = logits;
+  q.row_stride = row_stride;
+  q.valid_len = valid_len;
+  q.width = width;
+  q.tops = tops;
+  q.tops_stride = tops_stride;
+  const int words = ((width + 7) / 8 + 7) / 8;
+  const dim3 grid((unsigned)((words + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
+  hipLaunchKernelGGL(topk_vector_maxima, grid, dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), q, rows);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TOPK_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+  return TOPK_OK;
 }
 
 int topk_bf16_rows_ordered(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,

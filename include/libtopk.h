@@ -93,8 +93,13 @@ enum topk_path {
     TOPK_PATH_DIRECT_FORCED = 3, /* direct radix, requested */
     TOPK_PATH_DIRECT_MISJUDGED = 4, /* direct radix: fewer than k keys at
                                        or above the sampled cutoff */
-    TOPK_PATH_DIRECT_OVERFLOW = 5   /* direct radix: more survivors above
+    TOPK_PATH_DIRECT_OVERFLOW = 5,  /* direct radix: more survivors above
                                        the cutoff than the buffers hold */
+    TOPK_PATH_TOPS = 6,             /* vector-max bound: only the vectors
+                                       whose maximum reaches it loaded */
+    TOPK_PATH_DIRECT_DENSE = 7      /* direct radix: a row given vector
+                                       maxima with fewer than 2k vectors,
+                                       too wide for the sampled registers */
 };
 
 /* Optional block table of the page transform (host struct; `pages` is a
@@ -154,6 +159,58 @@ int topk_bf16_rows_noalloc(const uint16_t *logits, int64_t row_stride,
                            int32_t width, int32_t k, int32_t mode,
                            const topk_block_table_t *block_table,
                            int32_t *out, void *stream);
+
+/* topk_bf16_rows given each row's vector maxima: the largest key of every
+ * aligned group of 8 logits, a side array 1/8 of the row that a scorer can
+ * write as it stores the logits (vLLM API page "vllm.models.kimi_k3.nvidia.
+ * specialized_decode.cutedsl.dsa.indexer", IndexerScore's epilogue).  The
+ * result is exactly that of topk_bf16_rows; only the route differs (the same
+ * page, IndexerSelect passes 1 and 2): the k-th largest maximum, low, is the
+ * largest key of k different groups, so the k-th key is at least low, and
+ * every key at or above low lies in a group whose maximum reaches low.  Only
+ * those groups (about k on smooth data) are loaded, so a row reads its
+ * maxima and about 16 k bytes of logits instead of 2 v bytes.
+ *   tops         device uint16 [rows, tops_stride]: tops[r][j], for every
+ *                j < ceil(v / 8) (v the clamped valid length), must be the
+ *                largest key (the order-preserving key above) among logits
+ *                8j .. 8j+7 of row r that lie below v, as
+ *                topk_bf16_vector_maxima writes it; entries from ceil(v / 8)
+ *                on are not read.  A side array that breaks this gives an
+ *                unspecified selection (never an access out of bounds).
+ *   tops_stride  entries between rows: a multiple of 8 (16-byte rows; tops
+ *                itself 16-byte aligned), at least ceil(width / 8)
+ *   options      as for topk_bf16_rows_ex, or NULL
+ * Other arguments as for topk_bf16_rows.  Which rows use the maxima: token
+ * rows, for an unforced call, when ceil(width / 8) lies between 2k and
+ * 32768 (width up to 262144, one workgroup per row).  There a row with
+ * n <= k is short as always; a row with fewer than 2k vectors (where the
+ * k-th largest maximum bounds loosely) takes the sampled path if it has at
+ * most 16384 logits, else the direct path (TOPK_PATH_DIRECT_DENSE); every
+ * other row takes the bound (TOPK_PATH_TOPS), or the direct path when a
+ * wave lists more than 256 hot groups, the survivors overflow, or low is 0.
+ * Other calls (block mode, whose -inf and NaN blocks are found only by
+ * reading every block; other widths; a forced direct path) ignore tops and
+ * run as topk_bf16_rows_ex, and tops may then be NULL.  Returns TOPK_OK or a
+ * negative topk_status; asynchronous like topk_bf16_rows. */
+int topk_bf16_rows_tops(const uint16_t *logits, int64_t row_stride,
+                        const int32_t *valid_len, int32_t rows, int32_t width,
+                        int32_t k, int32_t mode, const uint16_t *tops,
+                        int64_t tops_stride,
+                        const topk_block_table_t *block_table, int32_t *out,
+                        const topk_options_t *options, void *stream);
+
+/* The side array topk_bf16_rows_tops reads, for callers whose scorer does
+ * not write it: tops[r][j] = the largest key among logits 8j .. 8j+7 of row
+ * r below its clamped valid length, 0 where none is, for every
+ * j < ceil(width / 8); the rest of the 16-byte word holding entry
+ * ceil(width / 8) - 1 is written as 0.  Arguments as for topk_bf16_rows;
+ * tops and tops_stride as for topk_bf16_rows_tops.  One kernel that reads
+ * every valid logit once.  Returns TOPK_OK or a negative topk_status;
+ * asynchronous. */
+int topk_bf16_vector_maxima(const uint16_t *logits, int64_t row_stride,
+                            const int32_t *valid_len, int32_t rows,
+                            int32_t width, uint16_t *tops,
+                            int64_t tops_stride, void *stream);
 
 /* Deterministic ordered top-k of every row (vLLM API page
  * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.indexer",

@@ -6,7 +6,7 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 
 The arithmetic lives in ``topk_oracle.c`` (plain C: per row, element keys,
 a full ``qsort`` by (key desc, index asc), the first k; the ordered result
-sorts those k by index).  This package only
+sorts those k by index; the side array of vector maxima is a plain loop).  This package only
 compiles it with gcc and marshals numpy arrays.
 """
 from .oracle import (  # noqa: F401
@@ -25,5 +25,6 @@ from .oracle import (  # noqa: F401
     topk_row,
     topk,
     topk_ordered,
+    vector_maxima,
     lib_path,
 )

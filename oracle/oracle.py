@@ -91,6 +91,8 @@ class Oracle:
                                                  ctypes.c_int64, ctypes.c_int32, _i32p, _i32p,
                                                  _i32p]
         lib.oracle_topk_rows_ordered.restype = ctypes.c_int
+        lib.oracle_vector_maxima.argtypes = [_u16p, ctypes.c_int32, ctypes.c_int32, _u16p]
+        lib.oracle_vector_maxima.restype = None
         self.lib = lib
         self.path = path
 
@@ -118,6 +120,22 @@ class Oracle:
         keys = np.empty(max(r.size, 1), dtype=np.uint16)
         n = self.lib.oracle_row_keys(_u16(r), v, mode, _u16(keys))
         return keys[:n].copy()
+
+    def vector_maxima(self, logits, valid_len, width: int | None = None):
+        """oracle_vector_maxima per row: the largest key of every 8 logits
+        below the row's valid length (0 where none is), [rows, ceil(width/8)]."""
+        L = np.ascontiguousarray(np.asarray(logits, dtype=np.uint16))
+        if L.ndim == 1:
+            L = L[None, :]
+        rows = L.shape[0]
+        width = L.shape[1] if width is None else int(width)
+        vl = np.broadcast_to(np.asarray(valid_len, dtype=np.int64), (rows,))
+        nv = (width + 7) // 8
+        out = np.zeros((rows, max(nv, 1)), dtype=np.uint16)
+        for r in range(rows):
+            row = np.ascontiguousarray(L[r])
+            self.lib.oracle_vector_maxima(_u16(row), int(vl[r]), width, _u16(out[r]))
+        return out[:, :nv]
 
     def threshold(self, keys, k: int):
         """oracle_threshold: (T, count_gt, count_eq), or None if n <= k."""
@@ -236,6 +254,11 @@ class Oracle:
                 list(ex.map(lambda i: run(int(bounds[i]), int(bounds[i + 1])),
                             range(threads)))
         return out, ids, valid
+
+def vector_maxima(logits, valid_len, width=None):
+    """oracle_vector_maxima per row: uint16 [rows, ceil(width / 8)]."""
+    return default().vector_maxima(logits, valid_len, width)
+
 
 def default() -> Oracle:
     """The oracle built from oracle/topk_oracle.c (compiled on first use)."""

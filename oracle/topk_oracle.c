@@ -21,7 +21,8 @@
  *  [K3]  vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.
  *        cutedsl.dsa.indexer", IndexerSelect.emit (block-table transform)
  *        and the short-context bypass in IndexerSelect.kernel (length
- *        clamped at zero).
+ *        clamped at zero); IndexerScore's epilogue (the side array of each
+ *        8 logits' largest key).
  *
  * Readings where the pages leave a point open (each also listed in the
  * design notes):
@@ -352,4 +353,26 @@ int oracle_topk_rows_ordered(const uint16_t *logits, int64_t row_stride,
             return rc;
     }
     return 0;
+}
+
+/* [K3] IndexerScore epilogue: the side array of vector maxima.  tops[j],
+ * for every j < ceil(width / 8), is the largest key among logits 8j ..
+ * 8j+7 that lie below the clamped valid length, or 0 when none does (the
+ * epilogue starts each lane's maximum at 0 and folds in only the keys it
+ * stores).  A plain loop over the logits. */
+void oracle_vector_maxima(const uint16_t *row, int32_t valid_len, int32_t width,
+                          uint16_t *tops)
+{
+    int32_t v = clamp_len(valid_len, width);
+    int32_t nv = (width + 7) / 8;
+    int32_t j, i;
+    for (j = 0; j < nv; ++j) {
+        uint16_t best = 0;
+        for (i = 8 * j; i < 8 * j + 8 && i < v; ++i) {
+            uint16_t k = oracle_key(row[i]);
+            if (k > best)
+                best = k;
+        }
+        tops[j] = best;
+    }
 }

@@ -473,6 +473,74 @@ def pin_multirow_driver(orc):
                 assert out[r].tolist() == want_out, ctx
 
 
+def pin_vector_maxima(orc):
+    """The side array of vector maxima (vLLM kimi_k3 indexer page,
+    IndexerScore epilogue): closed forms on monotone rows (the maximum of a
+    vector is its last valid logit when values rise, its first when they
+    fall), nothing past the valid length, zero for vectors holding no valid
+    logit, and on random rows every entry is attained by a valid logit of its
+    vector and dominates the others."""
+    width = 100
+    rise = (0x3F80 + np.arange(width)).astype(np.uint16)       # 1.0 and up
+    fall = rise[::-1].copy()
+    for v in (0, 1, 7, 8, 9, 93, 100):
+        t = orc.vector_maxima(rise[None, :], [v], width)[0]
+        assert t.shape == (13,)
+        for j in range(13):
+            lastv = min(8 * j + 8, v) - 1
+            want = int(orc.key(rise[lastv])) if lastv >= 8 * j else 0
+            assert int(t[j]) == want, (v, j)
+        t = orc.vector_maxima(fall[None, :], [v], width)[0]
+        for j in range(13):
+            want = int(orc.key(fall[8 * j])) if 8 * j < v else 0
+            assert int(t[j]) == want, (v, j)
+    # the largest value sits past the length: it must not show
+    row = np.full(16, 0x3F80, np.uint16)
+    row[12] = 0x7F80                                           # +inf past v = 12
+    t = orc.vector_maxima(row[None, :], [12], 16)[0]
+    assert t.tolist() == [int(orc.key(0x3F80))] * 2
+    # negative NaNs only: key 0; a positive NaN: above +inf
+    t = orc.vector_maxima(np.array([[0xFFFF] * 8 + [0x7FC1] + [0] * 7], np.uint16), [16], 16)[0]
+    assert int(t[0]) == 0 and int(t[1]) > int(orc.key(0x7F80))
+    rng = np.random.Generator(np.random.PCG64(4242))
+    for trial in range(20):
+        width = int(rng.integers(1, 300))
+        rows = 3
+        L = rng.integers(0, 1 << 16, size=(rows, width), dtype=np.uint32).astype(np.uint16)
+        vl = rng.integers(-3, width + 4, size=rows)
+        t = orc.vector_maxima(L, vl, width)
+        for r in range(rows):
+            v = max(0, min(int(vl[r]), width))
+            keys = orc.key(L[r])
+            for j in range((width + 7) // 8):
+                seg = keys[8 * j:min(8 * j + 8, v)]
+                if seg.size == 0:
+                    assert int(t[r, j]) == 0
+                else:
+                    assert int(t[r, j]) in set(int(x) for x in seg)
+                    assert all(int(t[r, j]) >= int(x) for x in seg)
+
+
+def pin_vector_maxima_bound(orc):
+    """The property the select relies on: the k-th largest vector maximum is
+    at most the row's k-th largest key, and at least k keys lie at or above
+    it."""
+    rng = np.random.Generator(np.random.PCG64(4243))
+    for trial in range(12):
+        k = int(rng.integers(1, 40))
+        width = int(rng.integers(16 * k, 16 * k + 200))
+        row = rng.integers(0, 1 << 16, size=width, dtype=np.uint32).astype(np.uint16)
+        if trial % 2:
+            row = (rng.standard_normal(width, dtype=np.float32).view(np.uint32) >> 16).astype(
+                np.uint16)  # normal values, truncated to BF16
+        t = orc.vector_maxima(row[None, :], [width], width)[0]
+        low = int(np.sort(t)[::-1][k - 1])
+        keys = orc.row_keys(row, width, 0)
+        T = orc.threshold(keys, k)[0]
+        assert low <= int(T)
+        assert int((keys >= low).sum()) >= k
+
+
 ALL_PINS = [
     pin_key_fixed_points,
     pin_key_bijection,
@@ -496,6 +564,8 @@ ALL_PINS = [
     pin_ordered_rank_definition,
     pin_ordered_worked_cases,
     pin_multirow_driver,
+    pin_vector_maxima,
+    pin_vector_maxima_bound,
 ]
 
 

@@ -52,7 +52,8 @@ def test_header_declares_entry_points():
     assert "topk_bf16_rows" in names and "topk_status_string" in names
     assert "topk_bf16_rows_ordered" in names and "topk_bf16_rows_ordered_ex" in names
     assert "topk_bf16_rows_noalloc" in names
-    assert len(names) >= 8
+    assert "topk_bf16_rows_tops" in names and "topk_bf16_vector_maxima" in names
+    assert len(names) >= 10
 
 
 def test_library_exports_every_declared_symbol():
@@ -126,3 +127,57 @@ def test_ordered_rejects_bad_arguments(kw, status):
 def test_ordered_rows_zero_is_a_noop():
     assert _call_ordered(rows=0, logits=None, valid_len=None, out=None, valid=None,
                          ids=None) == 0
+
+
+def _call_tops(**kw):
+    lib = T.library()
+    a = dict(logits=16, row_stride=16, valid_len=64, rows=4, width=16, k=8, mode=0,
+             tops=1024, tops_stride=8, bt=None, out=128, opts=None, stream=None)
+    a.update(kw)
+    return lib.topk_bf16_rows_tops(a["logits"], a["row_stride"], a["valid_len"], a["rows"],
+                                   a["width"], a["k"], a["mode"], a["tops"], a["tops_stride"],
+                                   a["bt"], a["out"], a["opts"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), -1), (dict(mode=2), -1), (dict(row_stride=20), -2), (dict(out=None), -1),
+    (dict(tops=None), -1), (dict(tops=1032), -2), (dict(tops_stride=4), -2),
+    (dict(tops_stride=0), -1), (dict(width=200, row_stride=200, tops_stride=24), -1),
+])
+def test_tops_rejects_bad_arguments(kw, status):
+    """The entry point given vector maxima checks them (16-byte aligned rows
+    of at least ceil(width / 8) entries) besides the usual arguments."""
+    assert _call_tops(**kw) == status
+    assert T.library().topk_last_error()
+
+
+def test_tops_not_needed_in_block_mode_or_for_no_rows():
+    assert _call_tops(rows=0, logits=None, valid_len=None, out=None, tops=None) == 0
+    # block mode ignores the maxima: the same checks as topk_bf16_rows, and
+    # a null side array is accepted (nothing is launched for these bad k)
+    assert _call_tops(mode=1, tops=None, k=0) == -1
+
+
+def _call_maxima(**kw):
+    lib = T.library()
+    a = dict(logits=16, row_stride=16, valid_len=64, rows=4, width=16, tops=1024,
+             tops_stride=8, stream=None)
+    a.update(kw)
+    return lib.topk_bf16_vector_maxima(a["logits"], a["row_stride"], a["valid_len"], a["rows"],
+                                       a["width"], a["tops"], a["tops_stride"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), -1), (dict(width=-1), -1), (dict(row_stride=8), -1),
+    (dict(row_stride=20), -2), (dict(logits=None), -1), (dict(valid_len=None), -1),
+    (dict(logits=24), -2), (dict(tops=None), -1), (dict(tops=1026), -2),
+    (dict(tops_stride=12), -2), (dict(width=200, row_stride=200, tops_stride=16), -1),
+])
+def test_vector_maxima_rejects_bad_arguments(kw, status):
+    assert _call_maxima(**kw) == status
+    assert T.library().topk_last_error()
+
+
+def test_vector_maxima_nothing_to_do():
+    assert _call_maxima(rows=0, logits=None, valid_len=None, tops=None) == 0
+    assert _call_maxima(width=0, logits=None, valid_len=None, tops=None) == 0

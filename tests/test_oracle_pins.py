@@ -58,6 +58,11 @@ MUTANTS = [
      "const int32_t *prow = pages ? pages + (int64_t)r * page_size : NULL;\n        int rc = oracle_topk_row("),
     ("rows: logits row by width", "oracle_topk_row(logits + (int64_t)r * row_stride,",
      "oracle_topk_row(logits + (int64_t)r * width,"),
+    ("maxima ignore the length", "i < 8 * j + 8 && i < v;", "i < 8 * j + 8 && i < width;"),
+    ("maxima keep the smallest", "            if (k > best)\n                best = k;",
+     "            if (k < best || i == 8 * j)\n                best = k;"),
+    ("maxima of raw bits", "uint16_t k = oracle_key(row[i]);", "uint16_t k = row[i];"),
+    ("maxima one logit apart", "for (i = 8 * j; i < 8 * j + 8", "for (i = 8 * j + 1; i < 8 * j + 8"),
     ("rows: output row by width", "out + (int64_t)r * k);", "out + (int64_t)r * width);"),
     ("rows: first row skipped", "for (r = row_begin; r < row_end; ++r) {\n        const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row(",
      "for (r = row_begin + 1; r < row_end; ++r) {\n        const int32_t *prow = pages ? pages + (int64_t)r * pages_stride : NULL;\n        int rc = oracle_topk_row("),
