@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     topk_bf16_rows_ordered,
     library_path,
     release_scratch,
+    reserve_scratch,
     status_string,
     topk_bf16_rows,
     topk_bf16_rows_tops,

@@ -93,6 +93,8 @@ def library():
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_last_error.argtypes = []
         lib.topk_last_error.restype = ctypes.c_char_p
+        lib.topk_reserve_scratch.argtypes = [ctypes.c_int32] * 5 + [ctypes.c_void_p]
+        lib.topk_reserve_scratch.restype = ctypes.c_int
         lib.topk_release_scratch.argtypes = []
         lib.topk_release_scratch.restype = ctypes.c_int
         _lib = lib
@@ -131,6 +133,19 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream: torch.cuda.Stream
 
 def status_string(status: int) -> str:
     return library().topk_status_string(int(status)).decode()
+
+
+def reserve_scratch(rows: int, width: int, k: int, mode=MODE_TOKEN, ordered: bool = False,
+                    stream: torch.cuda.Stream | None = None) -> None:
+    """topk_reserve_scratch (include/libtopk.h): set up and pin the scratch of
+    `stream` (default: the current stream) for calls of up to `rows` rows of
+    this width, k and mode, before capturing such calls into a graph."""
+    lib = library()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    rc = lib.topk_reserve_scratch(int(rows), int(width), int(k), _mode(mode),
+                                  1 if ordered else 0, ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise TopkError(rc, lib.topk_last_error().decode())
 
 
 def release_scratch() -> None:

@@ -2457,24 +2457,35 @@ int fail(int status, const char* fmt, ...) {
 struct Scratch {
   void* base = nullptr;
   size_t bytes = 0;
+  bool reserved = false;  // sized by topk_reserve_scratch: calls never replace it
+  bool captured = false;  // used under graph capture: nothing replaces it
 };
 std::mutex g_mu;
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 
 // Team scratch, one buffer per (device, stream).  Every word a team kernel
 // reads was written by an earlier kernel of the same call, so nothing needs
-// zeroing between calls.
+// zeroing between calls.  A call that needs more than the buffer holds
+// replaces it (after synchronizing the stream) unless the buffer was
+// reserved, or used by a call under graph capture (a captured graph keeps
+// its address); the call then fails and names the reason.
 int get_scratch(hipStream_t stream, size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(TOPK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
   std::lock_guard<std::mutex> lock(g_mu);
   Scratch& sc = g_scratch[std::make_pair(dev, stream)];
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  const bool capturing =
+      hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone;
   if (sc.bytes < need) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
-      return fail(TOPK_ERR_UNSUPPORTED, "the stream's team scratch (%zu bytes) must be set up by "
-                  "a call outside graph capture", need);
+    if (capturing)
+      return fail(TOPK_ERR_UNSUPPORTED, "the stream's team scratch (%zu bytes) must be set up "
+                  "outside graph capture, by an earlier call or topk_reserve_scratch", need);
+    if (sc.reserved || sc.captured)
+      return fail(TOPK_ERR_UNSUPPORTED, "this call needs %zu bytes of team scratch on its "
+                  "stream, more than the %zu %s; reserve more before capturing", need, sc.bytes,
+                  sc.captured ? "held by a captured graph" : "reserved");
     if (sc.base) {
       e = hipStreamSynchronize(stream);
       if (e == hipSuccess) e = hipFree(sc.base);
@@ -2489,8 +2500,41 @@ int get_scratch(hipStream_t stream, size_t need, void** out) {
     }
     sc.bytes = need;
   }
+  if (capturing) sc.captured = true;
   *out = sc.base;
   return TOPK_OK;
+}
+
+// Geometry of the team path (rows wider than one workgroup): G members of
+// cv vectors per row, row_bytes of scratch per row, batch rows per launch:
+// all of them, unless the scratch cap (or a caller's fixed scratch) or
+// kTeamBatch bounds a launch; a capped batch of 8 rows or more holds whole
+// groups of 8 (one per XCD), and every launch's grid is padded to whole
+// groups of 8 anyway.  False when one row needs more than cap_bytes.
+struct TeamGeom {
+  int vpt, cv, G, batch;
+  size_t row_bytes;
+};
+bool team_geom(int32_t rows, int32_t width, int32_t mode, size_t cap_bytes, TeamGeom& t) {
+  const int nvec_max = (width + 7) / 8;
+  t.vpt = mode == TOPK_MODE_BLOCK ? kTeamBlockVPT
+                                  : (nvec_max <= kMaxMembers * kTeamNT * 4 ? 4 : 8);
+  t.cv = kTeamNT * t.vpt;
+  t.G = (nvec_max + t.cv - 1) / t.cv;  // <= kMaxMembers
+  t.row_bytes = (size_t)t.G * kMemberWords * 4;
+  if (t.row_bytes > cap_bytes) return false;
+  t.batch = rows < kTeamBatch ? rows : kTeamBatch;
+  if ((size_t)t.batch * t.row_bytes > cap_bytes) {
+    t.batch = (int)(cap_bytes / t.row_bytes);
+    t.batch = t.batch < 8 ? t.batch : t.batch / 8 * 8;
+  }
+  return true;
+}
+
+// Whether rows of this width take the team path.
+bool team_rows(int32_t width, int32_t mode) {
+  const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kRowBlockVPT : kRowTokenVPT);
+  return (width + 7) / 8 > cap_wg;
 }
 
 // The scratch of topk_bf16_rows_noalloc: one array per device, part of the
@@ -2721,8 +2765,7 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
   }
   // one workgroup of 512 threads per row while the row fits its
   // registers: 2048 vectors (token) or 4096 (block)
-  const int cap_wg = kRowNT * (mode == TOPK_MODE_BLOCK ? kRowBlockVPT : kRowTokenVPT);
-  if (nvec_max <= cap_wg) {
+  if (!team_rows(width, mode)) {
     p.rows = rows;
     p.row0 = 0;
     p.lcw = row_lcw(k, kRowNT / 64);
@@ -2743,24 +2786,13 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
 
   // team path: G members per row (filter kernel), then one workgroup per
   // row (select kernel).  Scratch: one slice per member of a launch's rows.
-  const int vpt = mode == TOPK_MODE_BLOCK ? kTeamBlockVPT
-                                          : (nvec_max <= kMaxMembers * kTeamNT * 4 ? 4 : 8);
-  const int cv = kTeamNT * vpt;
-  const int G = (nvec_max + cv - 1) / cv;  // <= kMaxMembers
-  const size_t row_bytes = (size_t)G * kMemberWords * 4;
-  // rows per launch: all of them, unless the scratch cap (or the caller's
-  // fixed scratch) or kTeamBatch bounds a launch; a capped batch of 8 rows
-  // or more holds whole groups of 8 (one per XCD), and every launch's grid
-  // is padded to whole groups of 8 anyway
   const size_t cap_bytes = fixed ? fixed_bytes : kTeamScratchMax;
-  if (row_bytes > cap_bytes)
+  TeamGeom tg;
+  if (!team_geom(rows, width, mode, cap_bytes, tg))
     return fail(TOPK_ERR_UNSUPPORTED, "one row of width %d needs %zu bytes of team scratch, "
-                "more than the %zu available", width, row_bytes, cap_bytes);
-  int batch = rows < kTeamBatch ? rows : kTeamBatch;
-  if ((size_t)batch * row_bytes > cap_bytes) {
-    batch = (int)(cap_bytes / row_bytes);
-    batch = batch < 8 ? batch : batch / 8 * 8;
-  }
+                "more than the %zu available", width, tg.row_bytes, cap_bytes);
+  const int vpt = tg.vpt, cv = tg.cv, G = tg.G, batch = tg.batch;
+  const size_t row_bytes = tg.row_bytes;
   void* team_buf = fixed;
   if (!fixed) {
     const int rc = get_scratch(stream, (size_t)batch * row_bytes, &team_buf);
@@ -2912,6 +2944,55 @@ const char* topk_status_string(int status) {
 }
 
 const char* topk_last_error(void) { return g_err; }
+
+int topk_reserve_scratch(int32_t rows, int32_t width, int32_t k, int32_t mode, int32_t ordered,
+                         void* stream_ptr) {
+  g_err[0] = '\0';
+  (void)ordered;  // the ordered results take no more scratch
+  if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
+  if (k < 1 || k > TOPK_MAX_K) return fail(TOPK_ERR_INVALID_ARG, "k = %d outside [1, %d]", k, TOPK_MAX_K);
+  if (mode != TOPK_MODE_TOKEN && mode != TOPK_MODE_BLOCK)
+    return fail(TOPK_ERR_INVALID_ARG, "mode = %d", mode);
+  if (width < 0 || width > TOPK_MAX_WIDTH)
+    return fail(TOPK_ERR_INVALID_ARG, "width = %d outside [0, %d]", width, TOPK_MAX_WIDTH);
+  if (rows == 0 || !team_rows(width, mode)) return TOPK_OK;  // every row fits one workgroup
+  TeamGeom tg;
+  if (!team_geom(rows, width, mode, kTeamScratchMax, tg))
+    return fail(TOPK_ERR_UNSUPPORTED, "one row of width %d needs more than %zu bytes of team "
+                "scratch", width, kTeamScratchMax);
+  const int64_t need = (int64_t)tg.batch * (int64_t)tg.row_bytes;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TOPK_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_mu);
+  Scratch& sc = g_scratch[std::make_pair(dev, stream)];
+  if (sc.bytes < (size_t)need) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) == hipSuccess && cap != hipStreamCaptureStatusNone)
+      return fail(TOPK_ERR_UNSUPPORTED, "scratch cannot be reserved under graph capture");
+    if (sc.captured)
+      return fail(TOPK_ERR_UNSUPPORTED, "the stream's team scratch (%zu bytes) is held by a "
+                  "captured graph; growing it to %lld bytes would free memory the graph uses "
+                  "(reserve before capturing)", sc.bytes, (long long)need);
+    if (sc.base) {
+      e = hipStreamSynchronize(stream);
+      if (e == hipSuccess) e = hipFree(sc.base);
+      sc.base = nullptr;
+      sc.bytes = 0;
+      if (e != hipSuccess) return fail(TOPK_ERR_HIP, "scratch release: %s", hipGetErrorString(e));
+    }
+    e = hipMalloc(&sc.base, (size_t)need);
+    if (e != hipSuccess) {
+      sc.base = nullptr;
+      return fail(TOPK_ERR_HIP, "scratch hipMalloc(%lld): %s", (long long)need,
+                  hipGetErrorString(e));
+    }
+    sc.bytes = (size_t)need;
+  }
+  sc.reserved = true;
+  return TOPK_OK;
+}
 
 int topk_release_scratch(void) {
   std::lock_guard<std::mutex> lock(g_mu);

@@ -38,17 +38,21 @@
  *
  * Execution.  The call enqueues its kernels on `stream` (a hipStream_t;
  * NULL = the default stream) and returns without waiting.  It allocates
- * nothing on the hot path: rows wider than one workgroup's share use a
- * per-(device, stream) scratch buffer that the library allocates on first
- * use for that stream and replaces by a larger one, after synchronizing
- * that stream, when a call needs more.  The scratch is never cleared: every
- * word a call reads there was written earlier in the same call.  A call
- * that has to allocate cannot run under graph capture (it fails with
- * TOPK_ERR_HIP), and a graph captured on a stream holds that stream's
- * scratch address: capture after the stream's largest call, since a later
- * call that replaces the scratch leaves earlier graphs pointing at freed
- * memory.  Calls that overlap on one stream's scratch are serialized by
- * the stream; calls on different streams get different scratch buffers.
+ * nothing on the hot path: rows wider than one workgroup's share (16384
+ * tokens, 4096 blocks) use a per-(device, stream) scratch buffer that the
+ * library allocates on first use for that stream and replaces by a larger
+ * one, after synchronizing that stream, when a call needs more.  The scratch
+ * is never cleared: every word a call reads there was written earlier in
+ * the same call.  Under graph capture nothing is allocated: a captured call
+ * needs a scratch buffer set up beforehand (by an earlier call on the stream
+ * or by topk_reserve_scratch), and otherwise fails with TOPK_ERR_UNSUPPORTED.
+ * A captured graph keeps the scratch address, so a buffer once used under
+ * capture (or reserved) is never replaced: a later call that would need
+ * more fails with TOPK_ERR_UNSUPPORTED (and a reason) instead of freeing
+ * memory a graph may still use.  Calls that overlap on one stream's scratch are serialized
+ * by the stream; calls on different streams get different scratch buffers;
+ * a graph replayed on another stream still uses the scratch of the stream
+ * it was captured on.
  *
  * Errors.  Argument errors are reported before anything is enqueued, by
  * a negative status; out is then untouched.  Values are never errors:
@@ -228,10 +232,10 @@ int topk_bf16_vector_maxima(const uint16_t *logits, int64_t row_stride,
  *   valid        device int32 [rows], or NULL (not written)
  *   ids          device int32 [rows, k], or NULL (not written)
  * Costs over topk_bf16_rows: rows up to 16384 tokens or 4096 blocks are
- * ordered from the registers that hold them; wider rows take two more
- * kernel launches and one more read of the row (two when the row leaves the
- * sampled path).  Scratch as for topk_bf16_rows, plus (2 + ceil(width /
- * 16384)) words per row of a wide-row batch.  Returns TOPK_OK or a negative
+ * ordered from the registers that hold them; wider rows are ordered from
+ * the survivor lists their members wrote (no further read of the row, no
+ * further launch; a row that leaves the sampled path is read once more).
+ * Scratch as for topk_bf16_rows.  Returns TOPK_OK or a negative
  * topk_status; asynchronous like topk_bf16_rows. */
 int topk_bf16_rows_ordered(const uint16_t *logits, int64_t row_stride,
                            const int32_t *valid_len, int32_t rows, int32_t width,
@@ -253,8 +257,24 @@ const char *topk_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
 const char *topk_last_error(void);
 
-/* Release every scratch buffer the library holds (synchronizes the
- * streams they belong to).  Optional; for tests and clean shutdown. */
+/* Size the scratch of `stream` on the current device for calls of up to
+ * `rows` rows of this width, k and mode (ordered or not: the same scratch),
+ * so that such calls can then be captured into HIP graphs (vLLM kimi_k3
+ * indexer page, the indexer's `reserve` of its logits scratch before
+ * capture).  Nothing is allocated when every row fits one workgroup.  A
+ * reserved scratch is never replaced by a call (a call that needs more
+ * fails with TOPK_ERR_UNSUPPORTED and a reason); further reservations grow
+ * it, for several call shapes, until a call under capture has used it:
+ * from then on nothing replaces it, and a larger reservation fails too.
+ * Not under graph capture.  Synchronizes the stream when it replaces a
+ * buffer.  Returns TOPK_OK or a negative topk_status. */
+int topk_reserve_scratch(int32_t rows, int32_t width, int32_t k, int32_t mode,
+                         int32_t ordered, void *stream);
+
+/* Release every scratch buffer the library holds, reserved ones included
+ * (synchronizes the streams they belong to).  Graphs captured with them
+ * must not be replayed afterwards.  Optional; for tests and clean
+ * shutdown. */
 int topk_release_scratch(void);
 
 #ifdef __cplusplus

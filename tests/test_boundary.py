@@ -181,3 +181,21 @@ def test_vector_maxima_rejects_bad_arguments(kw, status):
 def test_vector_maxima_nothing_to_do():
     assert _call_maxima(rows=0, logits=None, valid_len=None, tops=None) == 0
     assert _call_maxima(width=0, logits=None, valid_len=None, tops=None) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 1 << 20, 0, 0, 0), -1), ((4, 1 << 20, 8, 2, 0), -1), ((-1, 1 << 20, 8, 0, 0), -1),
+    ((4, (1 << 20) + 8, 8, 0, 0), -1), ((4, -1, 8, 0, 0), -1),
+])
+def test_reserve_rejects_bad_arguments(args, status):
+    assert T.library().topk_reserve_scratch(*args, None) == status
+    assert T.library().topk_last_error()
+
+
+def test_reserve_nothing_for_one_workgroup_rows():
+    # rows that fit one workgroup take no scratch: nothing is reserved (and
+    # no HIP call is made, so this runs without a GPU)
+    lib = T.library()
+    assert lib.topk_reserve_scratch(1000, 16384, 2048, 0, 0, None) == 0
+    assert lib.topk_reserve_scratch(1000, 32768, 2048, 1, 1, None) == 0
+    assert lib.topk_reserve_scratch(0, 1 << 20, 2048, 0, 0, None) == 0

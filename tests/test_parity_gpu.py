@@ -390,8 +390,7 @@ def test_graph_replays():
     scratch needs no clearing between calls)."""
     ds = [W.make(2, rows=48, width=16384, seed=401), W.make(3, rows=5, width=60000, seed=402),
           W.make(4, rows=6, width=150000, seed=403)]
-    # eager work in between: no wider than the captured team rows, so that
-    # the stream's scratch (captured by address) is not replaced
+    # eager work in between, on the same stream and scratch
     other = W.make(3, rows=7, width=50000, seed=404)
     os_ = [run_oracle(d) for d in ds]
     s = torch.cuda.Stream()
@@ -402,6 +401,10 @@ def test_graph_replays():
                                  page_size=d.get("page_size") or 64, width=d["width"])
                 for d, (L, VL, P) in zip(ds, dev)]
 
+    # the stream's scratch sized for every shape before the first call and
+    # the capture: calls never replace a reserved (or captured) scratch
+    for d in ds + [other]:
+        T.reserve_scratch(d["logits"].shape[0], d["width"], d["k"], d["mode"], stream=s)
     with torch.cuda.stream(s):
         calls()  # first use on this stream: the scratch is set up outside the capture
     torch.cuda.synchronize()
