@@ -2687,7 +2687,7 @@ int check_tops(const uint16_t* tops, int64_t tops_stride, int32_t width) {
 int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, int32_t rows,
         int32_t width, int32_t k, int32_t mode, const topk_block_table_t* bt, int32_t* out,
         const topk_options_t* opt, int ord, int32_t* valid, int32_t* ids, void* stream_ptr,
-        void* fixed = nullptr, size_t fixed_bytes = 0, const uint16_t* tops = nullptr,
+        bool noalloc = false, const uint16_t* tops = nullptr,
         int64_t tops_stride = 0) {
   g_err[0] = '\0';
   if (rows < 0) return fail(TOPK_ERR_INVALID_ARG, "rows < 0");
@@ -2786,16 +2786,19 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
 
   // team path: G members per row (filter kernel), then one workgroup per
   // row (select kernel).  Scratch: one slice per member of a launch's rows.
-  const size_t cap_bytes = fixed ? fixed_bytes : kTeamScratchMax;
+  const size_t cap_bytes = noalloc ? kNoAllocBytes : kTeamScratchMax;
   TeamGeom tg;
   if (!team_geom(rows, width, mode, cap_bytes, tg))
     return fail(TOPK_ERR_UNSUPPORTED, "one row of width %d needs %zu bytes of team scratch, "
                 "more than the %zu available", width, tg.row_bytes, cap_bytes);
   const int vpt = tg.vpt, cv = tg.cv, G = tg.G, batch = tg.batch;
   const size_t row_bytes = tg.row_bytes;
-  void* team_buf = fixed;
-  if (!fixed) {
-    const int rc = get_scratch(stream, (size_t)batch * row_bytes, &team_buf);
+  // (the entry point that allocates nothing: the fixed per-device array,
+  // looked up only now, after every argument check)
+  void* team_buf = nullptr;
+  {
+    const int rc = noalloc ? noalloc_scratch(&team_buf)
+                           : get_scratch(stream, (size_t)batch * row_bytes, &team_buf);
     if (rc != TOPK_OK) return rc;
   }
   int rc = TOPK_OK;
@@ -2860,12 +2863,8 @@ int topk_bf16_rows_ex(const uint16_t* logits, int64_t row_stride, const int32_t*
 int topk_bf16_rows_noalloc(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
                            int32_t rows, int32_t width, int32_t k, int32_t mode,
                            const topk_block_table_t* block_table, int32_t* out, void* stream) {
-  g_err[0] = '\0';
-  void* ptr = nullptr;
-  const int rc = noalloc_scratch(&ptr);
-  if (rc != TOPK_OK) return rc;
   return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, nullptr, 0,
-             nullptr, nullptr, stream, ptr, kNoAllocBytes);
+             nullptr, nullptr, stream, true);
 }
 
 int topk_bf16_rows_tops(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len,
@@ -2879,7 +2878,7 @@ int topk_bf16_rows_tops(const uint16_t* logits, int64_t row_stride, const int32_
     if (rc != TOPK_OK) return rc;
   }
   return run(logits, row_stride, valid_len, rows, width, k, mode, block_table, out, options, 0,
-             nullptr, nullptr, stream, nullptr, 0, mode == TOPK_MODE_TOKEN ? tops : nullptr,
+             nullptr, nullptr, stream, false, mode == TOPK_MODE_TOKEN ? tops : nullptr,
              tops_stride);
 }
 
