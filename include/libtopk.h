@@ -152,10 +152,11 @@ int topk_bf16_rows_ex(const uint16_t *logits, int64_t row_stride,
  * fixed 16 MiB scratch array that the library's code object holds on every
  * device it runs on, for the life of the process (its address is looked up
  * once per device, on the first call there).  Rows are processed in batches
- * that fit it; a single row never needs more than 2.4 MB, so no call is
- * refused for size (TOPK_ERR_UNSUPPORTED would name the reason).  Every call
- * on one device shares that device's array: calls that overlap in time on
- * one device, on any streams, race and must be serialized by the caller.
+ * that fit it; a single row needs at most 64 members' slices of 32,320
+ * bytes (about 2.1 MB), so no call is refused for size
+ * (TOPK_ERR_UNSUPPORTED would name the reason).  Every call on one device
+ * shares that device's array: calls that overlap in time on one device, on
+ * any streams, race and must be serialized by the caller.
  * Nothing in the array needs clearing between calls: every word a call
  * reads there was written earlier in the same call. */
 int topk_bf16_rows_noalloc(const uint16_t *logits, int64_t row_stride,
