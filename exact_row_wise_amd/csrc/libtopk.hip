@@ -519,11 +519,13 @@ __device__ void write_short_block(const Out o, const uint4* src, int n, int k,
 // one pass writing the selected indices (decode_topk_cute "Direct" path and
 // its note on replicated copies).  Reads the row from global memory; taken
 // when the sampled cutoff misjudged the row, or on request.  n > k.
-// `region` holds kDirectWords words of LDS.
+// `region` holds kDirectWords words of LDS.  Returns the k-th key and the
+// count of keys above it; with `ordered` nothing is written (the caller's
+// ordered pass writes).
 template <int MODE, int NT>
-__device__ void direct_select(const uint4* src, int v, int n, int k, const Out o,
-                              uint32_t* region, uint32_t* bc, bool ordered = false,
-                              uint2* tsel = nullptr, int tid = (int)threadIdx.x) {
+__device__ uint2 direct_select(const uint4* src, int v, int n, int k, const Out o,
+                               uint32_t* region, uint32_t* bc, bool ordered = false,
+                               int tid = (int)threadIdx.x) {
   const int copy = (tid & 63) & (kCopies - 1);
   const int nvec = (MODE == TOPK_MODE_BLOCK) ? n : (v + 7) >> 3;
   uint32_t* hist = region;
@@ -582,10 +584,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
   const uint32_t T = (b1 << 8) | b2;
   const uint32_t cgt = a1 + a2;
   const uint32_t take = (uint32_t)k - cgt;
-  if (ordered) {  // ordered results: the caller writes
-    *tsel = make_uint2(T, cgt);
-    return;
-  }
+  if (ordered) return make_uint2(T, cgt);  // ordered results: the caller writes
   for (int vid = tid; vid < nvec; vid += NT) {
     const uint4 raw = src[vid];
     if constexpr (MODE == TOPK_MODE_BLOCK) {
@@ -610,6 +609,7 @@ __device__ void direct_select(const uint4* src, int v, int n, int k, const Out o
       }
     }
   }
+  return make_uint2(T, cgt);
 }
 
 // --------------------------------------------------------- sampled path
@@ -1306,7 +1306,8 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE, NT>(src, v, n, k, o, lists, bc, ORD, ORD ? &tc : nullptr);
+    const uint2 dt = direct_select<MODE, NT>(src, v, n, k, o, lists, bc, ORD);
+    if constexpr (ORD) tc = dt;
   }
   if constexpr (ORD) {
     if (p.force_direct) {  // the sampled path did not stage the row
@@ -1580,7 +1581,7 @@ __device__ __forceinline__ void tops_body(const Params& p, const int row, const 
   }
   if (direct) {
     __syncthreads();
-    direct_select<TOPK_MODE_TOKEN, NT>(src, v, v, k, o, lists, bc, false, nullptr, tid);
+    direct_select<TOPK_MODE_TOKEN, NT>(src, v, v, k, o, lists, bc, false, tid);
   }
   set_path(p, row, code, tid);
 }
@@ -2014,9 +2015,10 @@ constexpr int kSelMem = kSelHist + 272;
 constexpr int kSelMhist = kSelMem + 16 * kMaxMembers;
 constexpr int kSelWave = kSelMhist + (kRelBins / 2) * kMaxMembers;
 enum { MT_E = 0, MT_TK = 1, MT_NQ = 2, MT_CUT = 3, MT_TW = 4, MT_GT = 8, MT_EQ = 9, MT_BASE = 10,
-       MT_QUOTA = 11 };
+       MT_QUOTA = 11, MT_X = 12 };
 constexpr int kListBatch = 8;  // 64-entry chunks of a member's list loaded together
-constexpr int kListPre = 2;    // of them, loaded with the headers
+constexpr int kListPre = 3;    // of them, loaded with the headers
+constexpr int kItemBatch = 4;  // chunks past those a wave loads together (unordered writes)
 
 // Stage 2: one 1024-thread workgroup per row.  Short rows are written
 // directly.  Otherwise the members' headers, histograms and first entries
@@ -2116,6 +2118,12 @@ topk_team_select(Params p) {
         *reinterpret_cast<uint4*>(e) = make_uint4(live ? h0.x : 0u, tk, nq, cut);
         *reinterpret_cast<uint4*>(e + MT_TW) = live ? h1 : make_uint4(0u, 0u, 0u, 0u);
       }
+      // the chunks past the first kListPre of every member's list, numbered
+      // over the row (member m's from e[MT_X] on), shared by all the waves
+      const uint32_t xm = live ? sat_sub((h0.x + 63u) >> 6, (uint32_t)kListPre) : 0u;
+      const uint32_t ix = wave_incl_scan(xm);
+      if (lane < kMaxMembers) mt[lane * 16 + MT_X] = live ? ix - xm : 0xFFFFFFFFu;
+      if (lane == 63) bc[BC_TMP + 5] = ix;
       const uint32_t itk = wave_incl_scan(tk), inq = wave_incl_scan(nq);
       const unsigned long long fd = __ballot(fl & kFlagDirect), fo = __ballot(fl & kFlagOverflow);
       const unsigned long long ft = __ballot(fl & kFlagTies);
@@ -2175,48 +2183,68 @@ topk_team_select(Params p) {
     }
     const uint32_t take = (uint32_t)k - cgt;
     if (!direct && !ORD) {
-      // -- unordered: every wave writes the lists of its members.  The first
-      // kListBatch chunks of all of them are loaded together (the first one
-      // came with the headers), then written; longer lists follow in batches.
+      // -- unordered: every wave writes the first chunks of its members'
+      // lists; the rest of the lists is shared by all the waves.
       unsigned long long* slot = reinterpret_cast<unsigned long long*>(bc + BC_SLOT);
-      uint2 en[kPreM][kListBatch];
-      uint32_t Em[kPreM];
-#pragma unroll
-      for (int u = 0; u < kPreM; ++u) {
-        const int m = wave + u * NW;
-        Em[u] = m < gr ? mt[m * 16 + MT_E] : 0u;
-#pragma unroll
-        for (int c = 0; c < kListPre; ++c) en[u][c] = pre[u][c];
-        if (m < gr && Em[u] > kListPre * 64u) {
-          const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
-#pragma unroll
-          for (int c = kListPre; c < kListBatch; ++c)
-            en[u][c] = ld_entry(list, (uint32_t)c * 64u + (uint32_t)lane);
-        }
-      }
+      // the first kListPre chunks of this wave's members, loaded with the
+      // headers
 #pragma unroll
       for (int u = 0; u < kPreM; ++u) {
         const int m = wave + u * NW;
         if (m < gr) {
-          const uint32_t* list = slices + (size_t)m * kMemberWords + kMemberList;
           const uint32_t g = (uint32_t)m * chunk;
-          const uint32_t E = Em[u];
+          const uint32_t E = mt[m * 16 + MT_E];
 #pragma unroll
-          for (int c = 0; c < kListBatch; ++c) {
+          for (int c = 0; c < kListPre; ++c) {
             const uint32_t b0 = (uint32_t)c * 64u;
             if (b0 < E) {
-              const uint2 e = b0 + lane < E ? en[u][c] : make_uint2(kDeadPair, 0u);
+              const uint2 e = b0 + lane < E ? pre[u][c] : make_uint2(kDeadPair, 0u);
               if (tie_pass) emit_chunk<MODE, true, false>(e, g, Ts, cgt, take, slot, o);
               else emit_chunk<MODE, true, true>(e, g, Ts, cgt, take, slot, o);
             }
           }
-          for (uint32_t b0 = kListBatch * 64u; b0 < E; b0 += 64u) {
-            const uint2 e = b0 + lane < E ? ld_entry(list, b0 + lane) : make_uint2(kDeadPair, 0u);
+        }
+      }
+      // the chunks past those, over all the waves: item i is chunk
+      // kListPre + i - X of the member m with X = e[MT_X] <= i (the last
+      // such), kItemBatch of a wave's items loaded together
+      const uint32_t nx = bc[BC_TMP + 5];
+      const uint32_t xl = lane < gr ? mt[lane * 16 + MT_X] : 0xFFFFFFFFu;
+      for (uint32_t i0 = (uint32_t)wave; i0 < nx; i0 += NW * kItemBatch) {
+        uint2 en[kItemBatch];
+        uint32_t im[kItemBatch], ib[kItemBatch], iE[kItemBatch];
+#pragma unroll
+        for (int t = 0; t < kItemBatch; ++t) {
+          const uint32_t i = i0 + (uint32_t)t * NW;
+          im[t] = 0;
+          ib[t] = 0;
+          iE[t] = 0;
+          if (i < nx) {
+            const int m = popc(__ballot(xl <= i)) - 1;
+            const uint32_t b0 = (kListPre + i - readlane(xl, m)) * 64u;
+            im[t] = (uint32_t)m;
+            ib[t] = b0;
+            iE[t] = mt[m * 16 + MT_E];
+            en[t] = ld_entry(slices + (size_t)m * kMemberWords + kMemberList, b0 + lane);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < kItemBatch; ++t) {
+          if (i0 + (uint32_t)t * NW < nx) {
+            const uint2 e = ib[t] + lane < iE[t] ? en[t] : make_uint2(kDeadPair, 0u);
+            const uint32_t g = im[t] * chunk;
             if (tie_pass) emit_chunk<MODE, true, false>(e, g, Ts, cgt, take, slot, o);
             else emit_chunk<MODE, true, true>(e, g, Ts, cgt, take, slot, o);
           }
-          if (tie_pass) {
-            // the first keys equal to the cutoff, from the tie regions
+        }
+      }
+      if (tie_pass) {
+        // the first keys equal to the cutoff, from the tie regions
+#pragma unroll
+        for (int u = 0; u < kPreM; ++u) {
+          const int m = wave + u * NW;
+          if (m < gr) {
+            const uint32_t g = (uint32_t)m * chunk;
             const uint32_t* tl = slices + (size_t)m * kMemberWords + kMemberTies;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -2340,7 +2368,7 @@ topk_team_select(Params p) {
           uint2 en[kListBatch];
 #pragma unroll
           for (int c = 0; c < kListBatch; ++c)
-            en[c] = ld_entry(list, (uint32_t)c * 64u + (uint32_t)lane);
+            if ((uint32_t)c * 64u < Em) en[c] = ld_entry(list, (uint32_t)c * 64u + (uint32_t)lane);
           auto for_list = [&](auto&& f) {
 #pragma unroll
             for (int c = 0; c < kListBatch; ++c) {
@@ -2408,7 +2436,8 @@ topk_team_select(Params p) {
   }
   if (direct) {
     __syncthreads();
-    direct_select<MODE, NT>(src, v, n, k, o, smem + kSelWave, bc, ORD, ORD ? &tc : nullptr);
+    const uint2 dt = direct_select<MODE, NT>(src, v, n, k, o, smem + kSelWave, bc, ORD);
+    if constexpr (ORD) tc = dt;
     if constexpr (ORD) {
       // the ordered write pass over the row, in spans of NT * 2 vectors
       constexpr int VPT = 2;
