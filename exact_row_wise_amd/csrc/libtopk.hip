@@ -69,6 +69,8 @@ constexpr int kSelNT = 1024;             // select workgroup size
 constexpr int kRowNT = 512;              // one-workgroup-per-row size
 constexpr int kRowTokenVPT = 4;          // 16-byte vectors per thread, one-workgroup token rows
 constexpr int kRowBlockVPT = 8;          // 16-byte vectors per thread, one-workgroup block rows
+constexpr int kWideNT = 1024;            // one-workgroup token rows when all are resident
+constexpr int kWideTokenVPT = 2;         // 16-byte vectors per thread at that size
 constexpr int kTeamBlockVPT = 12;        // 16-byte vectors per thread of a block work item
 constexpr int kTokenSV = 1;              // sample vectors per thread, token cutoff kernel
 constexpr int kBlockSV = 4;              // sample vectors per thread, block cutoff kernel
@@ -1166,12 +1168,13 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
         kb[j] = vid >= 0 ? (vid == n - 1 ? kKeyPosInf : block_key4(raw[j])) : 0u;
         s = vid >= 0 ? kb[j] : kNone;
       } else {
-        // sample: logit j mod 8 (that is, (vid / NT) mod 8) of the vector.
+        // sample: logit (vid / 512) mod 8 of the vector, whatever the
+        // workgroup size (with 512 threads, logit j mod 8 of slot j).
         // Slots before jt hold whole vectors; in slot jt, with a length
         // that is not a multiple of 8, the row's last vector is cut: its
         // logits past the length become the bottom key, and its sample is
-        // logit 0 when logit j mod 8 is past the length.
-        const int es = j & 7;
+        // logit 0 when its sampled logit is past the length.
+        const int es = NT == 512 ? (j & 7) : ((vid >> 9) & 7);
         const uint32_t se = key1(half_of(word_of(raw[j], es >> 1), es & 1));
         if (j < jt) {
           s = se;
@@ -2687,6 +2690,36 @@ int launch_rows(int mode, int rows, size_t lds, hipStream_t stream, const Params
                 lds, stream, p);
 }
 
+// Compute units of the current device (cached per device; 0 when the
+// runtime cannot say).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> g(mu);
+  auto it = done.find(dev);
+  if (it != done.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  return done[dev] = cus;
+}
+
+// Token rows at 1024 threads a row (2 vectors a thread), when there are no
+// more rows than compute units (a row's workgroup then has its unit to
+// itself; two of them on one unit, barriers of 16 waves and 16 waves' fixed
+// costs outweigh the shorter serial work); kNotLaunched otherwise.
+constexpr int kNotLaunched = 1;
+template <bool ORD>
+int launch_wide(int rows, size_t lds, hipStream_t stream, const Params& p) {
+  auto wide = topk_rows_wg<TOPK_MODE_TOKEN, kWideNT, kWideTokenVPT, false, ORD>;
+  if (rows > device_cus() ||
+      rows > resident_grid(reinterpret_cast<const void*>(wide), kWideNT, lds))
+    return kNotLaunched;
+  return launch(wide, rows, kWideNT, lds, stream, p);
+}
+
 // Rows on the vector-max bound: for one word of maxima per thread, the
 // latency variant while every row's workgroup is resident, else the
 // throughput variant; wider rows are few.
@@ -2803,6 +2836,20 @@ int run(const uint16_t* logits, int64_t row_stride, const int32_t* valid_len, in
       // the rows' block-table entries get an LDS copy after everything else
       p.page_lds = (int32_t)(lds / 4);
       lds += (size_t)kPageLdsMax * 4;
+    }
+    // few token rows: 1024 threads each, 2 vectors a thread, which halves
+    // every thread's serial work on a row's path
+    if (mode == TOPK_MODE_TOKEN) {
+      Params pw = p;
+      pw.lcw = row_lcw(k, kWideNT / 64);
+      size_t ldw = row_lds_bytes(pw.lcw, kWideNT / 64);
+      if (p.page_lds) {
+        pw.page_lds = (int32_t)(ldw / 4);
+        ldw += (size_t)kPageLdsMax * 4;
+      }
+      const int rc = ord ? launch_wide<true>(rows, ldw, stream, pw)
+                         : launch_wide<false>(rows, ldw, stream, pw);
+      if (rc != kNotLaunched) return rc;
     }
     // more rows than resident workgroups: the throughput variant, whose
     // exact select searches its bins with one wave (the other waves' copies

@@ -191,36 +191,43 @@ def test_block_mode_page_transform():
 
 
 def _sampled_positions_wg(nvec):
-    """Positions the one-workgroup token kernel samples: logit (j mod 8) of
-    the vector staged in slot j, i.e. logit (vid // 512) mod 8 of vector vid
-    (512-thread workgroups)."""
+    """Positions the one-workgroup token kernel samples: logit (vid // 512)
+    mod 8 of vector vid, at either workgroup size (with 512 threads, logit
+    j mod 8 of the vector staged in slot j)."""
     vid = np.arange(nvec)
     return vid * 8 + (vid // 512) % 8
 
 
-def test_crafted_misjudged_row_takes_direct_path():
+# 2 rows: 1024-thread workgroups (no more rows than compute units); 300 rows:
+# 512-thread workgroups, all resident
+CRAFTED_ROWS = [2, 300]
+
+
+@pytest.mark.parametrize("rows", CRAFTED_ROWS)
+def test_crafted_misjudged_row_takes_direct_path(rows):
     """Sampled positions hold the row's largest values and everything else is
     lower, so fewer than k keys lie at or above the cutoff."""
     width, k = 16384, 512
-    L = np.full((2, width), 0x3F00, np.uint16)                # 0.5 everywhere
+    L = np.full((rows, width), 0x3F00, np.uint16)             # 0.5 everywhere
     pos = _sampled_positions_wg(width // 8)
     L[:, pos] = (0x4000 + np.arange(pos.size) % 0x700).astype(np.uint16)
-    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+    d = dict(logits=L, valid_len=np.full(rows, width, np.int32), k=k, mode=0, width=width,
              pages=None, page_size=0)
     g, pc = run_gpu(d)
     assert_parity(d, g, run_oracle(d))
     assert np.all(pc == T.PATH_DIRECT_MISJUDGED), pc
 
 
-def test_crafted_overflow_row_takes_direct_path():
+@pytest.mark.parametrize("rows", CRAFTED_ROWS)
+def test_crafted_overflow_row_takes_direct_path(rows):
     """Sampled positions hold the smallest values, so almost every other key
     lies above the cutoff and the survivor regions overflow."""
     rng = np.random.Generator(np.random.PCG64(79))
     width, k = 16384, 512
-    L = W.f32_to_bf16_bits(np.abs(rng.standard_normal((2, width), dtype=np.float32)) + 1)
+    L = W.f32_to_bf16_bits(np.abs(rng.standard_normal((rows, width), dtype=np.float32)) + 1)
     pos = _sampled_positions_wg(width // 8)
     L[:, pos] = 0x3C00                                         # tiny positives
-    d = dict(logits=L, valid_len=np.full(2, width, np.int32), k=k, mode=0, width=width,
+    d = dict(logits=L, valid_len=np.full(rows, width, np.int32), k=k, mode=0, width=width,
              pages=None, page_size=0)
     g, pc = run_gpu(d)
     assert_parity(d, g, run_oracle(d))
