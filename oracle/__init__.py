@@ -6,8 +6,10 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 
 The arithmetic lives in ``topk_oracle.c`` (plain C: per row, element keys,
 a full ``qsort`` by (key desc, index asc), the first k; the ordered result
-sorts those k by index; the side array of vector maxima is a plain loop).  This package only
-compiles it with gcc and marshals numpy arrays.
+sorts those k by index; the side array of vector maxima is a plain loop),
+and in ``score_oracle.c`` (the FP8 MQA indexer logits: exact dot products,
+BF16 roundings in the stated order; ``score.py`` wraps it).  This package
+only compiles them with gcc and marshals numpy arrays.
 """
 from .oracle import (  # noqa: F401
     MODE_TOKEN,
@@ -28,3 +30,4 @@ from .oracle import (  # noqa: F401
     vector_maxima,
     lib_path,
 )
+from . import score  # noqa: F401

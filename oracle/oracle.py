@@ -34,18 +34,21 @@ def lib_path() -> str:
     return _LIB
 
 
-def compile_source(src: str, dst: str) -> str:
+def compile_source(src: str, dst: str, libs=()) -> str:
     """gcc -O2 -shared: one C file into one shared library."""
     tmp = dst + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-o", tmp, src]
+           "-o", tmp, src, *libs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, dst)
     return dst
 
 
 def build() -> str:
-    """Compile oracle/topk_oracle.c into oracle/liboracle.so."""
+    """Compile oracle/topk_oracle.c into oracle/liboracle.so, and the
+    scorer oracle (oracle/score_oracle.c) beside it."""
+    from . import score
+    score.build()
     return compile_source(SOURCE, _LIB)
 
 
