@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     PATH_SHORT,
     PATH_TOPS,
     TopkError,
+    fp8_mqa_logits,
     library,
     probe_library,
     stream_read,

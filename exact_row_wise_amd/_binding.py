@@ -89,6 +89,10 @@ def library():
                                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                                 ctypes.c_int64, ctypes.c_void_p]
         lib.topk_bf16_vector_maxima.restype = ctypes.c_int
+        lib.topk_fp8_mqa_logits.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64,
+                                            ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.topk_fp8_mqa_logits.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_last_error.argtypes = []
@@ -254,6 +258,68 @@ def vector_maxima(logits: torch.Tensor, valid_len: torch.Tensor, width: int | No
     if rc != 0:
         raise TopkError(rc, lib.topk_last_error().decode())
     return tops
+
+
+def fp8_mqa_logits(q: torch.Tensor, w: torch.Tensor, keys: torch.Tensor,
+                   key_scale: torch.Tensor, valid_len: torch.Tensor, qpr: int = 1,
+                   width: int | None = None, logits: torch.Tensor | None = None,
+                   tops: torch.Tensor | None = None,
+                   stream: torch.cuda.Stream | None = None):
+    """The FP8 MQA indexer logits and their vector maxima
+    (topk_fp8_mqa_logits in include/libtopk.h).
+    q          uint8 [rows, 32, 128] (E4M3 bytes), contiguous
+    w          BF16 or 16-bit patterns [rows, 32], contiguous
+    keys       uint8 [requests, key_stride, 128] (E4M3 bytes), contiguous
+    key_scale  uint8 [requests, key_stride] (UE8M0 bytes)
+    valid_len  int32 [rows]; rows = requests * qpr
+    logits     16-bit [rows, >= width] (unit stride along a row), tops 16-bit
+               [rows, >= ceil(width / 8) rounded up to 8]; allocated if None
+    Returns (logits, tops)."""
+    lib = library()
+    if q.dtype != torch.uint8 or q.dim() != 3 or tuple(q.shape[1:]) != (32, 128) or not q.is_contiguous():
+        raise ValueError("q must be contiguous uint8 [rows, 32, 128]")
+    rows = q.shape[0]
+    dev = q.device
+    if w.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or tuple(w.shape) != (rows, 32) \
+            or not w.is_contiguous() or w.device != dev:
+        raise ValueError("w must be contiguous 16-bit [rows, 32] on the same GPU")
+    if keys.dtype != torch.uint8 or keys.dim() != 3 or keys.shape[2] != 128 \
+            or not keys.is_contiguous() or keys.device != dev:
+        raise ValueError("keys must be contiguous uint8 [requests, key_stride, 128]")
+    requests, key_stride = keys.shape[0], keys.shape[1]
+    if key_scale.dtype != torch.uint8 or tuple(key_scale.shape) != (requests, key_stride) \
+            or not key_scale.is_contiguous() or key_scale.device != dev:
+        raise ValueError("key_scale must be contiguous uint8 [requests, key_stride]")
+    if int(qpr) < 1 or rows != requests * int(qpr):
+        raise ValueError(f"rows {rows} must be requests {requests} x qpr {qpr}")
+    if valid_len.dtype != torch.int32 or valid_len.numel() != rows or valid_len.device != dev:
+        raise ValueError("valid_len must be int32 [rows] on the same GPU")
+    valid_len = valid_len.contiguous()
+    if width is None:
+        width = key_stride
+    nv = -(-int(width) // 8)
+    if logits is None:
+        logits = torch.zeros((rows, max(8, -(-int(width) // 8) * 8)), dtype=torch.int16, device=dev)
+    elif (logits.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or logits.dim() != 2
+          or logits.shape[0] != rows or logits.shape[1] < int(width) or logits.device != dev
+          or (logits.shape[1] > 1 and logits.stride(1) != 1)):
+        raise ValueError("logits must be 16-bit [rows, >= width] on the same GPU")
+    if tops is None:
+        tops = torch.zeros((rows, max(8, -(-nv // 8) * 8)), dtype=torch.int16, device=dev)
+    elif (tops.dtype not in (torch.int16, torch.uint16) or tops.dim() != 2
+          or tops.shape[0] != rows or tops.shape[1] < nv or tops.device != dev
+          or (tops.shape[1] > 1 and tops.stride(1) != 1)):
+        raise ValueError("tops must be 16-bit [rows, >= ceil(width / 8)] on the same GPU")
+    with torch.cuda.device(dev):
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        rc = lib.topk_fp8_mqa_logits(q.data_ptr(), w.data_ptr(), keys.data_ptr(),
+                                     key_scale.data_ptr(), int(key_stride), valid_len.data_ptr(),
+                                     int(rows), int(qpr), int(width), logits.data_ptr(),
+                                     int(logits.stride(0)), tops.data_ptr(), int(tops.stride(0)),
+                                     ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise TopkError(rc, lib.topk_last_error().decode())
+    return logits, tops
 
 
 def topk_bf16_rows_ordered(logits: torch.Tensor, valid_len: torch.Tensor, k: int,

@@ -12,6 +12,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "libtopk.hip")
+SCORE_SRC = os.path.join(PKG, "csrc", "score.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopk.so")
 PROBE_SRC = os.path.join(PKG, "csrc", "stream_probe.hip")
@@ -26,7 +27,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def command(out: str = LIB, extra=(), src: str = SRC) -> list[str]:
+def command(out: str = LIB, extra=(), src=(SRC, SCORE_SRC)) -> list[str]:
+    srcs = [src] if isinstance(src, str) else list(src)
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # no packed FP32: the only floating point on the path sizes the work
@@ -37,7 +39,7 @@ def command(out: str = LIB, extra=(), src: str = SRC) -> list[str]:
         # wave's total; the backend's own aggregation would only add work
         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wall", "-Wno-unused-function",
-        "-I", INCLUDE, *extra, "-o", out, src,
+        "-I", INCLUDE, *extra, "-o", out, *srcs,
     ]
 
 
@@ -53,7 +55,7 @@ def _build_one(src: str, lib: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     _build_one(PROBE_SRC, PROBE_LIB, verbose)
-    return _build_one(SRC, LIB, verbose)
+    return _build_one((SRC, SCORE_SRC), LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -3020,6 +3020,16 @@ const char* topk_status_string(int status) {
 
 const char* topk_last_error(void) { return g_err; }
 
+}  // extern "C"
+
+// The status of a call made in another source file of the library, its
+// text kept for topk_last_error.
+__attribute__((visibility("hidden"))) int topk_report(int status, const char* text) {
+  return fail(status, "%s", text);
+}
+
+extern "C" {
+
 int topk_reserve_scratch(int32_t rows, int32_t width, int32_t k, int32_t mode, int32_t ordered,
                          void* stream_ptr) {
   g_err[0] = '\0';

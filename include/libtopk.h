@@ -217,6 +217,55 @@ int topk_bf16_vector_maxima(const uint16_t *logits, int64_t row_stride,
                             int32_t width, uint16_t *tops,
                             int64_t tops_stride, void *stream);
 
+/* The FP8 MQA indexer logits the selection runs on, with their side array
+ * of vector maxima (vLLM API page "vllm.models.kimi_k3.nvidia.
+ * specialized_decode.cutedsl.dsa.indexer": the module docstring's logit of
+ * query row t and key i at stock precision, and IndexerScore's epilogue).
+ * Row t belongs to request t / qpr, whose keys it shares with the other
+ * rows of the request; for every key i below the row's clamped valid
+ * length v:
+ *   logits[t][i] = bf16(2^(s - 127) * sum over heads h of
+ *                       bf16(relu(q[t][h] . key[i])) * w[t][h])
+ * where the dot product runs over the 128 dims in FP8 E4M3 (OCP, bias 7)
+ * and is taken as the matrix cores' FP32 result, s is the key's UE8M0 byte,
+ * and the sum is formed as the page states: four BF16 accumulators a_j, each
+ * a_j = bf16(r_h * w_h + a_j) over heads h = j, j+4, ..., j+28 in that
+ * order, then bf16(bf16(a_0 + a_2) + bf16(a_1 + a_3)); every bf16() rounds
+ * to nearest, ties to even.  tops[t][j] = the largest order-preserving key
+ * among logits 8j .. 8j+7 of row t below v, for j < ceil(v / 8): exactly
+ * the side array topk_bf16_rows_tops reads (pass logits with row stride
+ * logits_stride and the same tops).  Nothing else is written.
+ *   q            device FP8 E4M3 [rows, 32, 128], 16-byte aligned (the
+ *                query's MX scale 1; fold its scale into w)
+ *   w            device BF16 [rows, 32] head weights, 4-byte aligned
+ *   keys         device FP8 E4M3 [requests, key_stride, 128], 16-byte
+ *                aligned: request r's key i at keys + (r * key_stride + i)
+ *                * 128
+ *   key_scale    device uint8 [requests, key_stride]: UE8M0 bytes 0..254
+ *                (2^(s - 127); 255 is not a scale)
+ *   key_stride   keys per request slot, >= width
+ *   valid_len    device int32 [rows]: keys row t scores, clamped to
+ *                [0, width]
+ *   rows         query rows, a multiple of qpr; qpr in [1, 8]
+ *   width        keys per row at most, <= TOPK_MAX_WIDTH
+ *   logits       device BF16 [rows, logits_stride], logits_stride >= width
+ *   tops         device uint16 [rows, tops_stride], tops_stride >=
+ *                ceil(width / 8) (a multiple of 8 and 16-byte rows to feed
+ *                topk_bf16_rows_tops)
+ * The matrix cores' FP8 dot product may differ from the exact one by a few
+ * units of the largest product's precision (their accumulation order and
+ * width are the hardware's); a logit then differs from the one of the exact
+ * dot products by at most what that allows after the BF16 roundings (also,
+ * an FMA whose exact result lies within half an FP32 unit of a BF16 midpoint
+ * may round either way).  Returns TOPK_OK or a negative topk_status
+ * (TOPK_ERR_INVALID_ARG, TOPK_ERR_MISALIGNED, TOPK_ERR_HIP); asynchronous on
+ * `stream`, allocates nothing. */
+int topk_fp8_mqa_logits(const uint8_t *q, const uint16_t *w, const uint8_t *keys,
+                        const uint8_t *key_scale, int64_t key_stride,
+                        const int32_t *valid_len, int32_t rows, int32_t qpr,
+                        int32_t width, uint16_t *logits, int64_t logits_stride,
+                        uint16_t *tops, int64_t tops_stride, void *stream);
+
 /* Deterministic ordered top-k of every row (vLLM API page
  * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.indexer",
  * IndexerSelect: the selected keys in key order with -1 past the row's

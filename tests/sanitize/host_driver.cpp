@@ -71,6 +71,23 @@ int main() {
   expect("maxima rows -1", topk_bf16_vector_maxima(L, 256, VL, -1, 256, TW, 32, nullptr), -1);
   expect("maxima nothing", topk_bf16_vector_maxima(nullptr, 256, nullptr, 0, 256, nullptr, 0,
                                                    nullptr), 0);
+  const uint8_t* QB = reinterpret_cast<const uint8_t*>(uintptr_t(0x90000));
+  const uint8_t* KB = reinterpret_cast<const uint8_t*>(uintptr_t(0xA0000));
+  const uint8_t* SB = reinterpret_cast<const uint8_t*>(uintptr_t(0xB0000));
+  const uint16_t* WB = reinterpret_cast<const uint16_t*>(uintptr_t(0xC0000));
+  uint16_t* LB = reinterpret_cast<uint16_t*>(uintptr_t(0xD0000));
+  expect("score qpr 9", topk_fp8_mqa_logits(QB, WB, KB, SB, 100, VL, 9, 9, 100, LB, 100, TW, 16,
+                                            nullptr), -1);
+  expect("score rows", topk_fp8_mqa_logits(QB, WB, KB, SB, 100, VL, 5, 2, 100, LB, 100, TW, 16,
+                                           nullptr), -1);
+  expect("score key stride", topk_fp8_mqa_logits(QB, WB, KB, SB, 99, VL, 4, 2, 100, LB, 100, TW,
+                                                 16, nullptr), -1);
+  expect("score q aligned", topk_fp8_mqa_logits(QB + 8, WB, KB, SB, 100, VL, 4, 2, 100, LB, 100,
+                                                TW, 16, nullptr), -2);
+  expect("score null", topk_fp8_mqa_logits(QB, WB, nullptr, SB, 100, VL, 4, 2, 100, LB, 100, TW,
+                                           16, nullptr), -1);
+  expect("score nothing", topk_fp8_mqa_logits(nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0,
+                                              1, 100, nullptr, 0, nullptr, 0, nullptr), 0);
   expect("reserve k", topk_reserve_scratch(4, 1 << 20, 0, 0, 0, nullptr), -1);
   expect("reserve one workgroup", topk_reserve_scratch(4, 16384, 8, 0, 1, nullptr), 0);
   for (int s = -6; s <= 1; ++s) {

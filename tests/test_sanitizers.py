@@ -45,7 +45,8 @@ def test_host_checks_under_asan_and_ubsan(tmp_path):
     rc, log = _run([HIPCC, "--offload-arch=gfx950", "-O2", "-g", "-std=c++17", "-fPIC", "-shared",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", *san,
                     "-I", inc, "-o", lib,
-                    os.path.join(ROOT, "exact_row_wise_amd", "csrc", "libtopk.hip")])
+                    os.path.join(ROOT, "exact_row_wise_amd", "csrc", "libtopk.hip"),
+                    os.path.join(ROOT, "exact_row_wise_amd", "csrc", "score.hip")])
     assert rc == 0, log
     rc, log = _run([HIPCC, "-O1", "-g", "-std=c++17", *san[:4], "-I", inc, "-o", exe,
                     os.path.join(HERE, "host_driver.cpp"), "-L", str(tmp_path), "-ltopk_san",

@@ -1,0 +1,180 @@
+"""GPU parity of the FP8 MQA indexer logits (topk_fp8_mqa_logits) through
+the C ABI, against the scorer oracle (oracle/score_oracle.c), and of the
+selection they feed.
+
+Two bars.  On inputs whose products sum exactly in FP32 ("narrow" bytes)
+the matrix cores' dot products are exact, and every logit must equal the
+oracle's definition bit for bit.  On full-range inputs ("wide" bytes) the
+matrix cores' FP8 accumulation differs from the exact dot product (its order
+and width are the hardware's; measured at most 2^-12.2 of the sum of the
+products' magnitudes), so every logit must lie in the oracle's interval for
+an allowance of 2^-10 of that sum.  The side array must be exactly the 8-key
+maxima of the logits written, and the selection on them exactly the
+oracle's top-k of those logits."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import score
+import workloads as W
+from checker import check
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+T = None
+DELTA = 2.0 ** -10
+SENTINEL = 0x7E57
+
+
+def setup_module(module):
+    global T
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_row_wise_amd as _T
+    T = _T
+    T.library()
+
+
+def run_score(d, width=None):
+    """The scorer on d's inputs; logits and tops start as SENTINEL."""
+    width = d["width"] if width is None else width
+    rows = d["q"].shape[0]
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(d["q"]).to(dev)
+    w = torch.from_numpy(d["w"].view(np.int16)).to(dev)
+    keys = torch.from_numpy(d["keys"]).to(dev)
+    ks = torch.from_numpy(d["key_scale"]).to(dev)
+    vl = torch.from_numpy(d["valid_len"]).to(dev)
+    nv = (width + 7) // 8
+    logits = torch.full((rows, max(8, -(-width // 8) * 8)), SENTINEL, dtype=torch.int16, device=dev)
+    tops = torch.full((rows, max(8, -(-nv // 8) * 8)), SENTINEL, dtype=torch.int16, device=dev)
+    T.fp8_mqa_logits(q, w, keys, ks, vl, d["qpr"], width=width, logits=logits, tops=tops)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy().view(np.uint16), tops.cpu().numpy().view(np.uint16)
+
+
+def oracle_row(d, t, delta, cols=None):
+    """(exact, lo, hi) of row t over its valid keys (or the given columns)."""
+    so = score.load()
+    r = t // d["qpr"]
+    v = max(0, min(int(d["valid_len"][t]), d["width"]))
+    idx = np.arange(v) if cols is None else np.asarray(cols)
+    return so.mqa_logits(d["q"][t:t + 1], d["w"][t:t + 1], d["keys"][r][idx],
+                         d["key_scale"][r][idx], delta)
+
+
+def _vkey(b):
+    b = np.asarray(b, np.uint16).astype(np.uint32)
+    return np.where(b & 0x8000, b ^ 0xFFFF, b ^ 0x8000)
+
+
+def check_untouched_and_tops(d, logits, tops):
+    width = d["width"]
+    for t in range(logits.shape[0]):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        nv = (v + 7) // 8
+        assert np.all(logits[t, v:] == SENTINEL), f"row {t}: written past its length"
+        assert np.all(tops[t, nv:] == SENTINEL), f"row {t}: maxima written past the length"
+        want = oracle.vector_maxima(logits[t:t + 1, :max(v, 1)], np.array([v], np.int32),
+                                    max(v, 1))[0][:nv]
+        assert np.array_equal(tops[t, :nv], want), f"row {t}: maxima of the logits differ"
+
+
+@pytest.mark.parametrize("requests,qpr,width,ks", [(2, 3, 700, 720), (3, 1, 257, 257),
+                                                    (1, 2, 1031, 1100)])
+def test_narrow_inputs_bit_exact(requests, qpr, width, ks):
+    d = W.make_score(requests, qpr, width, "narrow", seed=width, key_stride=ks)
+    print(f"score narrow requests={requests} qpr={qpr} width={width}", flush=True)
+    logits, tops = run_score(d)
+    for t in range(d["q"].shape[0]):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        ex, lo, hi = oracle_row(d, t, 0.0)
+        assert np.array_equal(lo, ex) and np.array_equal(hi, ex)
+        bad = np.nonzero(logits[t, :v] != ex[0])[0]
+        assert bad.size == 0, f"row {t}: {bad.size} logits differ, first at key {bad[:3]}"
+    check_untouched_and_tops(d, logits, tops)
+
+
+@pytest.mark.parametrize("requests,qpr,width", [(3, 2, 1000), (2, 1, 4096)])
+def test_wide_inputs_within_the_interval(requests, qpr, width):
+    d = W.make_score(requests, qpr, width, "wide", seed=width + 7)
+    print(f"score wide requests={requests} qpr={qpr} width={width}", flush=True)
+    logits, tops = run_score(d)
+    same = total = 0
+    for t in range(d["q"].shape[0]):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        ex, lo, hi = oracle_row(d, t, DELTA)
+        g = _vkey(logits[t, :v])
+        out = np.nonzero((g < _vkey(lo[0])) | (g > _vkey(hi[0])))[0]
+        assert out.size == 0, f"row {t}: {out.size} logits outside the interval, first {out[:3]}"
+        same += int((logits[t, :v] == ex[0]).sum())
+        total += v
+    print(f"  {same} of {total} logits equal the exact dot products' ({same / max(total, 1):.3f})")
+    check_untouched_and_tops(d, logits, tops)
+
+
+def test_lengths_and_many_verify_rows():
+    """Valid lengths 0, 1, 7, 8, 9, 255, 256, 257, the width, past it and
+    negative (clamped); and 8 verify rows to a request."""
+    d = W.make_score(10, 1, 600, "narrow", seed=3, key_stride=640)
+    d["valid_len"] = np.array([0, 1, 7, 8, 9, 255, 256, 257, 600, 611], np.int32)
+    logits, tops = run_score(d)
+    for t in range(10):
+        v = max(0, min(int(d["valid_len"][t]), 600))
+        ex, _, _ = oracle_row(d, t, 0.0)
+        assert np.array_equal(logits[t, :v], ex[0]), f"row {t} (v={v})"
+    check_untouched_and_tops(d, logits, tops)
+    d = W.make_score(2, 8, 333, "narrow", seed=4)
+    d["valid_len"][3] = -3
+    logits, tops = run_score(d)
+    for t in range(16):
+        v = max(0, min(int(d["valid_len"][t]), 333))
+        ex, _, _ = oracle_row(d, t, 0.0)
+        assert np.array_equal(logits[t, :v], ex[0]), f"qpr 8 row {t} (v={v})"
+    check_untouched_and_tops(d, logits, tops)
+
+
+@pytest.mark.parametrize("kind", ["narrow", "wide"])
+def test_scores_feed_the_selection(kind):
+    """The scorer's logits and maxima into topk_bf16_rows_tops: the exact
+    top-k of the logits written (k = 512 over rows of 4096 .. 20000 keys)."""
+    d = W.make_score(6, 2, 20000, kind, seed=11)
+    logits, tops = run_score(d)
+    rows = logits.shape[0]
+    dev = torch.device("cuda", 0)
+    L = torch.from_numpy(logits.view(np.int16)).to(dev)
+    VL = torch.from_numpy(d["valid_len"]).to(dev)
+    tp = torch.from_numpy(tops.view(np.int16)).to(dev)
+    pc = torch.full((rows,), -9, dtype=torch.int32, device=dev)
+    k = 512
+    out = T.topk_bf16_rows_tops(L, VL, k, tp, 0, width=d["width"], path_codes=pc)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    sel = dict(logits=logits, valid_len=d["valid_len"], k=k, mode=0, width=d["width"],
+               pages=None, page_size=0)
+    o = oracle.topk(logits, d["valid_len"], k, 0, width=d["width"], threads=16)
+    bad = check(oracle.default(), sel, g, o)
+    assert not bad, "\n".join(bad)
+    assert np.all(pc.cpu().numpy() == T.PATH_TOPS), pc.cpu().numpy()
+
+
+def test_full_size_sampled():
+    """The benchmark's scorer workload (64 requests x 150000 keys, one
+    verify row each): 4000 sampled logits in the oracle's interval, and every
+    row's maxima those of its logits."""
+    c = W.SCORE_CONFIG
+    d = W.make_score(c["requests"], c["qpr"], c["width"], "wide", seed=0, ragged=True)
+    print(f"score full size {c['name']}", flush=True)
+    logits, tops = run_score(d)
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = d["q"].shape[0]
+    for t in range(rows):
+        v = max(0, min(int(d["valid_len"][t]), d["width"]))
+        cols = np.sort(rng.choice(v, size=min(v, 4000 // rows), replace=False))
+        ex, lo, hi = oracle_row(d, t, DELTA, cols)
+        g = _vkey(logits[t, cols])
+        assert np.all((g >= _vkey(lo[0])) & (g <= _vkey(hi[0]))), f"row {t}"
+    check_untouched_and_tops(d, logits, tops)

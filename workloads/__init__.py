@@ -197,3 +197,63 @@ def make(cfg: int, rows: int | None = None, width: int | None = None,
     return dict(name=spec["name"], cfg=cfg, logits=logits, valid_len=valid_len, k=k,
                 mode=mode, width=width, row_stride=stride, pages=pages,
                 page_size=PAGE if pages is not None else 0)
+
+
+# ------------------------------------------------------------ scorer inputs
+# The FP8 MQA indexer scorer's inputs (vLLM kimi_k3 indexer page, module
+# docstring and IndexerScore): per query row 32 heads x 128 dims of FP8
+# E4M3 and 32 BF16 head weights; per key 128 dims of FP8 E4M3 and a UE8M0
+# scale byte; the rows of a request (qpr of them, the verify rows of one
+# decode step) share its keys.  No trained query, weights or cache exist
+# here, so the bytes are drawn directly: a sign, an exponent field and a
+# mantissa per value (the generator decodes nothing).
+SCORE_CONFIG = dict(name="score_fp8_64x150000_q1", requests=64, qpr=1, width=150000)
+
+
+def _e4m3_bytes(rng, shape, kind: str) -> np.ndarray:
+    """E4M3 bytes: "narrow" exponent fields 6..9 (magnitudes 0.5 .. 7.5,
+    whose products sum exactly in FP32) and about 10 % zeros; "wide" fields
+    over 0..15, the sum of two uniform fields 0..7 and 0..8 (a quantized
+    activation's spread, down to the subnormals), never the NaN code.  Two
+    random bytes a value: sign and mantissa from the first, the exponent
+    field from the second."""
+    n = int(np.prod(shape))
+    raw = np.frombuffer(rng.bytes(2 * n), np.uint8).reshape(2, n)
+    sm = raw[0] & np.uint8(0x87)                      # sign and mantissa bits
+    if kind == "narrow":
+        exp = np.uint8(6) + (raw[1] & np.uint8(3))
+        b = sm | (exp << 3)
+        b = np.where(raw[1] >= np.uint8(230), np.uint8(0), b)
+    else:
+        exp = (raw[1] & np.uint8(7)) + ((raw[1] >> 3) % np.uint8(9))
+        b = sm | (exp << 3)
+        b = np.where((b & 0x7F) == 0x7F, b ^ np.uint8(1), b)
+    return b.astype(np.uint8).reshape(shape)
+
+
+def make_score(requests: int, qpr: int, width: int, kind: str = "wide", seed: int = 0,
+               key_stride: int | None = None, ragged: bool = True) -> dict:
+    """Seeded scorer inputs: q uint8 [rows, 32, 128], w BF16 patterns
+    [rows, 32], keys uint8 [requests, key_stride, 128], key_scale uint8
+    [requests, key_stride] (UE8M0 bytes 118..130), valid_len int32 [rows]
+    (request r's length U[width / 2, width] when ragged, else width; its
+    verify rows u = 0..qpr-1 see length - (qpr - 1 - u), clamped at 0)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = requests * qpr
+    ks = width if key_stride is None else key_stride
+    q = _e4m3_bytes(rng, (rows, 32, 128), kind)
+    keys = np.empty((requests, ks, 128), np.uint8)
+    for r in range(requests):
+        keys[r] = _e4m3_bytes(rng, (ks, 128), kind)
+    key_scale = rng.integers(118, 131, (requests, ks), dtype=np.uint8)
+    w = f32_to_bf16_bits(rng.standard_normal((rows, 32), dtype=np.float32) * np.float32(0.25))
+    if ragged:
+        lens = rng.integers(width // 2, width + 1, requests)
+    else:
+        lens = np.full(requests, width)
+    vl = np.empty(rows, np.int32)
+    for r in range(requests):
+        for u in range(qpr):
+            vl[r * qpr + u] = max(0, int(lens[r]) - (qpr - 1 - u))
+    return dict(q=q, w=w, keys=keys, key_scale=key_scale, valid_len=vl, qpr=qpr, width=width,
+                requests=requests, kind=kind)
