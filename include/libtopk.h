@@ -220,7 +220,7 @@ int topk_bf16_vector_maxima(const uint16_t *logits, int64_t row_stride,
 /* The FP8 MQA indexer logits the selection runs on, with their side array
  * of vector maxima (vLLM API page "vllm.models.kimi_k3.nvidia.
  * specialized_decode.cutedsl.dsa.indexer": the module docstring's logit of
- * query row t and key i at stock precision, and IndexerScore's epilogue).
+ * query row t and key i at the stock logits path's precision, and IndexerScore's epilogue).
  * Row t belongs to request t / qpr, whose keys it shares with the other
  * rows of the request; for every key i below the row's clamped valid
  * length v:

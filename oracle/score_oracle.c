@@ -8,7 +8,7 @@
  *
  * Source: vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.
  * cutedsl.dsa.indexer": the module docstring (the logit of query row t and
- * key i at stock precision) and IndexerScore (the epilogue: each head's
+ * key i at the stock logits path's precision) and IndexerScore (the epilogue: each head's
  * relu(q . k) rounded to BF16, the heads weighted by BF16 FMAs in two BF16x2
  * sums, then one BF16 add, then the key's UE8M0 scale; each 8 keys' largest
  * order-preserving key into a side array).
