@@ -1,5 +1,5 @@
 """ctypes wrapper of ``score_oracle.c`` (test infrastructure only): the FP8
-MQA indexer logits at the precision the K3.1 indexer page states.
+and MXFP4 MQA indexer logits at the precision the K3.1 indexer page states.
 
 Each method names the C function it calls; the C source cites the passages
 it follows.  ``ScoreOracle(path)`` wraps one compiled copy, so that tests can
@@ -50,6 +50,14 @@ class ScoreOracle:
         lib.oracle_mqa_logits.argtypes = [_u8p, _u16p, ctypes.c_int32, _u8p, _u8p,
                                           ctypes.c_int32, ctypes.c_double, _u16p, _u16p, _u16p]
         lib.oracle_mqa_logits.restype = None
+        lib.oracle_e2m1.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1.restype = ctypes.c_longdouble
+        lib.oracle_mxfp4_logit.argtypes = [_u8p, _u8p, _u16p, _u8p, _u8p, ctypes.c_double,
+                                           _u16p, _u16p, _u16p]
+        lib.oracle_mxfp4_logit.restype = None
+        lib.oracle_mxfp4_logits.argtypes = [_u8p, _u8p, _u16p, ctypes.c_int32, _u8p, _u8p,
+                                            ctypes.c_int32, ctypes.c_double, _u16p, _u16p, _u16p]
+        lib.oracle_mxfp4_logits.restype = None
         self.lib = lib
         self.path = path
 
@@ -99,6 +107,50 @@ class ScoreOracle:
         self.lib.oracle_mqa_logit(q.ctypes.data_as(_u8p), w.ctypes.data_as(_u16p),
                                   key.ctypes.data_as(_u8p), int(scale), float(delta),
                                   ctypes.byref(ex), ctypes.byref(lo), ctypes.byref(hi))
+        return int(ex.value), int(lo.value), int(hi.value)
+
+
+    def e2m1(self, nibbles):
+        """oracle_e2m1 of each 4-bit code (float64 of the exact value)."""
+        c = np.asarray(nibbles, dtype=np.uint8).ravel()
+        return np.array([float(self.lib.oracle_e2m1(int(x))) for x in c]).reshape(np.shape(nibbles))
+
+    def mxfp4_logits(self, q, q_scale, w, keys, key_scales, delta: float = 0.0):
+        """oracle_mxfp4_logits for one request: q uint8 [rows, HEADS, DIM / 2]
+        (E2M1, low nibble first), q_scale uint8 [rows, HEADS, 4], w BF16
+        patterns [rows, HEADS], keys uint8 [nkeys, DIM / 2], key_scales uint8
+        [nkeys, 4].  Returns (exact, lo, hi), uint16 [rows, nkeys] each."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        qs = np.ascontiguousarray(q_scale, dtype=np.uint8)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        keys = np.ascontiguousarray(keys, dtype=np.uint8)
+        ks = np.ascontiguousarray(key_scales, dtype=np.uint8)
+        rows, nk = q.shape[0], keys.shape[0]
+        assert q.shape[1:] == (HEADS, DIM // 2) and qs.shape == (rows, HEADS, 4)
+        assert w.shape == (rows, HEADS) and keys.shape[1] == DIM // 2 and ks.shape == (nk, 4)
+        ex = np.empty((rows, nk), np.uint16)
+        lo = np.empty_like(ex)
+        hi = np.empty_like(ex)
+        if rows and nk:
+            self.lib.oracle_mxfp4_logits(q.ctypes.data_as(_u8p), qs.ctypes.data_as(_u8p),
+                                         w.ctypes.data_as(_u16p), rows,
+                                         keys.ctypes.data_as(_u8p), ks.ctypes.data_as(_u8p), nk,
+                                         float(delta), ex.ctypes.data_as(_u16p),
+                                         lo.ctypes.data_as(_u16p), hi.ctypes.data_as(_u16p))
+        return ex, lo, hi
+
+    def mxfp4_logit(self, q, q_scale, w, key, key_scale, delta: float = 0.0):
+        """oracle_mxfp4_logit: (exact, lo, hi) patterns of one query row and key."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        qs = np.ascontiguousarray(q_scale, dtype=np.uint8)
+        w = np.ascontiguousarray(w, dtype=np.uint16)
+        key = np.ascontiguousarray(key, dtype=np.uint8)
+        ks = np.ascontiguousarray(key_scale, dtype=np.uint8)
+        ex, lo, hi = ctypes.c_uint16(), ctypes.c_uint16(), ctypes.c_uint16()
+        self.lib.oracle_mxfp4_logit(q.ctypes.data_as(_u8p), qs.ctypes.data_as(_u8p),
+                                    w.ctypes.data_as(_u16p), key.ctypes.data_as(_u8p),
+                                    ks.ctypes.data_as(_u8p), float(delta), ctypes.byref(ex),
+                                    ctypes.byref(lo), ctypes.byref(hi))
         return int(ex.value), int(lo.value), int(hi.value)
 
 

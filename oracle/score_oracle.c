@@ -1,6 +1,6 @@
 /*
- * score_oracle.c -- plain CPU definition of the FP8 MQA indexer logits that
- * feed the exact top-k (the scorer of the K3.1 decode indexer).
+ * score_oracle.c -- plain CPU definition of the FP8 and MXFP4 MQA indexer
+ * logits that feed the exact top-k (the scorer of the K3.1 decode indexer).
  *
  * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
  * CPU-baseline leg may load this library; the product path (libtopk) never
@@ -37,6 +37,16 @@
  *    rounded to BF16 may do so); the rest of the chain is monotone, so the
  *    interval bounds every result those allowances permit.
  *  - UE8M0 byte s scales by 2^(s - 127); 255 (NaN) is never an input.
+ *
+ * The MXFP4 logits (the same page: the FP4 cache's E2M1 keys with a UE8M0
+ * scale per 32 values, the FP4 query with its own scales, both applied
+ * inside the block-scaled MMA, and no scale after the head sum):
+ *   d_h   = sum over blocks b of 2^(sq[h][b] + sk[b] - 254) *
+ *           sum over the 32 dims c of block b of q[h][c] * key[c]   (E2M1 values, exact)
+ *   then r_h, a_j and total as above, and logit = total, -0 written as +0.
+ * Byte j of a row holds dims 2j (low nibble) and 2j + 1 (high nibble).  The
+ * long double sums are exact while one head's products span less than 2^50
+ * (scales within 40 of each other).
  */
 #include <float.h>
 #include <math.h>
@@ -59,6 +69,19 @@ long double oracle_e4m3(uint8_t x)
     else
         v = ldexpl(1.0L + m / 8.0L, e - 7);
     return (x & 0x80) ? -v : v;
+}
+
+/* OCP FP4 E2M1 (the low 4 bits of the argument): sign, 2 exponent bits
+ * (bias 1), 1 mantissa bit; exponent field 0 holds the subnormal m / 2. */
+long double oracle_e2m1(uint8_t nibble)
+{
+    const int e = (nibble >> 1) & 3, m = nibble & 1;
+    long double v;
+    if (e == 0)
+        v = m / 2.0L;
+    else
+        v = ldexpl(1.0L + m / 2.0L, e - 1);
+    return (nibble & 8) ? -v : v;
 }
 
 /* The BF16 value of a pattern (its bits are the top half of an FP32). */
@@ -124,22 +147,19 @@ static void fma_bf16(long double ab_c, long double *lo, long double *hi)
     *hi = d < t ? t : d;
 }
 
-/* The logit of one query row (q: HEADS x DIM E4M3 bytes, w: HEADS BF16
- * patterns) and one key (DIM E4M3 bytes, UE8M0 scale byte), as the BF16
- * pattern of the definition (*exact) and the interval [*lo, *hi] (BF16
- * patterns, lo <= hi in value) that a dot product within delta times the
- * sum of the products' magnitudes, and the FMA rounding allowance, permit. */
-void oracle_mqa_logit(const uint8_t *q, const uint16_t *w, const uint8_t *key, uint8_t scale,
-                      double delta, uint16_t *exact, uint16_t *lo, uint16_t *hi)
+/* The logit from the heads' dot products dd[h] and the sums of their
+ * products' magnitudes ss[h]: the definition's BF16 pattern (*exact) and the
+ * interval [*lo, *hi] (BF16 patterns, lo <= hi in value) that dot products
+ * within delta times those sums, and the FMA rounding allowance, permit.
+ * sc scales the BF16 total (the FP8 key scale; 1 for MXFP4, whose scales
+ * are in the dot products); with clear_neg_zero a -0 logit is written +0. */
+static void logit_of_heads(const long double *dd, const long double *ss, const uint16_t *w,
+                           double delta, long double sc, int clear_neg_zero, uint16_t *exact,
+                           uint16_t *lo, uint16_t *hi)
 {
     long double r[HEADS], rlo[HEADS], rhi[HEADS];
     for (int h = 0; h < HEADS; ++h) {
-        long double d = 0, s = 0;
-        for (int c = 0; c < DIM; ++c) {
-            const long double p = oracle_e4m3(q[h * DIM + c]) * oracle_e4m3(key[c]);
-            d += p;
-            s += fabsl(p);
-        }
+        const long double d = dd[h], s = ss[h];
         const long double dl = d - (long double)delta * s, dh = d + (long double)delta * s;
         r[h] = bf16r(fp32_round(d > 0 ? d : 0));
         rlo[h] = bf16r(fp32_round(dl > 0 ? dl : 0));
@@ -161,13 +181,73 @@ void oracle_mqa_logit(const uint8_t *q, const uint16_t *w, const uint8_t *key, u
             ah[j] = h2;
         }
     }
-    const long double sc = ldexpl(1.0L, (int)scale - 127);
     const long double t = bf16r(bf16r(a[0] + a[2]) + bf16r(a[1] + a[3]));
     const long double tl = bf16r(bf16r(al[0] + al[2]) + bf16r(al[1] + al[3]));
     const long double th = bf16r(bf16r(ah[0] + ah[2]) + bf16r(ah[1] + ah[3]));
     *exact = oracle_bf16_round(t * sc);
     *lo = oracle_bf16_round(tl * sc);
     *hi = oracle_bf16_round(th * sc);
+    if (clear_neg_zero) {
+        if (*exact == 0x8000)
+            *exact = 0;
+        if (*lo == 0x8000)
+            *lo = 0;
+        if (*hi == 0x8000)
+            *hi = 0;
+    }
+}
+
+/* The logit of one query row (q: HEADS x DIM E4M3 bytes, w: HEADS BF16
+ * patterns) and one key (DIM E4M3 bytes, UE8M0 scale byte), as the BF16
+ * pattern of the definition (*exact) and the interval [*lo, *hi] (BF16
+ * patterns, lo <= hi in value) that a dot product within delta times the
+ * sum of the products' magnitudes, and the FMA rounding allowance, permit. */
+void oracle_mqa_logit(const uint8_t *q, const uint16_t *w, const uint8_t *key, uint8_t scale,
+                      double delta, uint16_t *exact, uint16_t *lo, uint16_t *hi)
+{
+    long double dd[HEADS], ss[HEADS];
+    for (int h = 0; h < HEADS; ++h) {
+        long double d = 0, s = 0;
+        for (int c = 0; c < DIM; ++c) {
+            const long double p = oracle_e4m3(q[h * DIM + c]) * oracle_e4m3(key[c]);
+            d += p;
+            s += fabsl(p);
+        }
+        dd[h] = d;
+        ss[h] = s;
+    }
+    const long double sc = ldexpl(1.0L, (int)scale - 127);
+    logit_of_heads(dd, ss, w, delta, sc, 0, exact, lo, hi);
+}
+
+/* Dim c of a row of E2M1 nibbles (byte c / 2, the low nibble for even c). */
+static long double e2m1_dim(const uint8_t *row, int c)
+{
+    return oracle_e2m1((uint8_t)((row[c / 2] >> (4 * (c % 2))) & 15));
+}
+
+/* The MXFP4 logit of one query row (q: HEADS x DIM / 2 E2M1 bytes, q_scale:
+ * HEADS x 4 UE8M0 bytes, one per 32 dims of a head, w: HEADS BF16 patterns)
+ * and one key (DIM / 2 E2M1 bytes, key_scale: 4 UE8M0 bytes), with the
+ * interval of oracle_mqa_logit. */
+void oracle_mxfp4_logit(const uint8_t *q, const uint8_t *q_scale, const uint16_t *w,
+                        const uint8_t *key, const uint8_t *key_scale, double delta,
+                        uint16_t *exact, uint16_t *lo, uint16_t *hi)
+{
+    long double dd[HEADS], ss[HEADS];
+    for (int h = 0; h < HEADS; ++h) {
+        long double d = 0, s = 0;
+        for (int c = 0; c < DIM; ++c) {
+            const int b = c / 32;  /* the block of 32 dims that one scale byte covers */
+            const long double bs = ldexpl(1.0L, (int)q_scale[h * 4 + b] + (int)key_scale[b] - 254);
+            const long double p = e2m1_dim(q + h * (DIM / 2), c) * e2m1_dim(key, c) * bs;
+            d += p;
+            s += fabsl(p);
+        }
+        dd[h] = d;
+        ss[h] = s;
+    }
+    logit_of_heads(dd, ss, w, delta, 1.0L, 1, exact, lo, hi);
 }
 
 /* The logits of rows x keys of one request: row t's query at q + t *
@@ -183,5 +263,22 @@ void oracle_mqa_logits(const uint8_t *q, const uint16_t *w, int32_t rows, const 
             oracle_mqa_logit(q + (int64_t)t * HEADS * DIM, w + (int64_t)t * HEADS,
                              keys + (int64_t)i * DIM, scales[i], delta, exact + o, lo + o,
                              hi + o);
+        }
+}
+
+/* The MXFP4 logits of rows x keys of one request: row t's query at q + t *
+ * HEADS * DIM / 2, its scales at q_scale + t * HEADS * 4, its weights at w +
+ * t * HEADS; key i at keys + i * DIM / 2, its scales at key_scales + i * 4;
+ * outputs row-major [rows, nkeys] (patterns). */
+void oracle_mxfp4_logits(const uint8_t *q, const uint8_t *q_scale, const uint16_t *w,
+                         int32_t rows, const uint8_t *keys, const uint8_t *key_scales,
+                         int32_t nkeys, double delta, uint16_t *exact, uint16_t *lo, uint16_t *hi)
+{
+    for (int32_t t = 0; t < rows; ++t)
+        for (int32_t i = 0; i < nkeys; ++i) {
+            const int64_t o = (int64_t)t * nkeys + i;
+            oracle_mxfp4_logit(q + (int64_t)t * HEADS * (DIM / 2), q_scale + (int64_t)t * HEADS * 4,
+                               w + (int64_t)t * HEADS, keys + (int64_t)i * (DIM / 2),
+                               key_scales + (int64_t)i * 4, delta, exact + o, lo + o, hi + o);
         }
 }

@@ -1,8 +1,11 @@
-"""Pins of the FP8 MQA indexer logits oracle (oracle/score_oracle.c): facts
-fixed outside the oracle -- library routines (torch's FP8 E4M3 decode, its
-float32 -> bfloat16 rounding, an FP32 matmul on inputs whose sums it holds
-exactly), closed forms, invariants of the tolerance interval, and the
-hand-worked cases of tests/golden/mqa_worked.txt.
+"""Pins of the FP8 and MXFP4 MQA indexer logits oracle
+(oracle/score_oracle.c): facts fixed outside the oracle -- library routines
+(torch's FP8 E4M3 decode, its float32 -> bfloat16 rounding, an FP32 matmul
+on inputs whose sums it holds exactly), the E2M1 format's value table
+(tests/golden/e2m1_values.txt), closed forms, invariants of the tolerance
+interval, the hand-worked cases of tests/golden/mqa_worked.txt, and the
+reduction of MXFP4 inputs whose scales are powers of two shared by a whole
+dot product to the FP8 path (pinned on its own).
 
 Run as a script with a library path, it applies every pin to that library
 and exits non-zero when one fails (the planted-mistake tests do this).
@@ -16,6 +19,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GOLDEN = os.path.join(HERE, "golden", "mqa_worked.txt")
+E2M1_TABLE = os.path.join(HERE, "golden", "e2m1_values.txt")
 HEADS, DIM = 32, 128
 
 
@@ -190,8 +194,146 @@ def pin_interval(so):
     assert np.all(_value_key(lo2) <= kl) and np.all(_value_key(hi2) >= kh)
 
 
+def e2m1_table():
+    """{code: value} from tests/golden/e2m1_values.txt."""
+    out = {}
+    for line in open(E2M1_TABLE):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        code, value = line.split()[:2]
+        out[int(code, 16)] = float(value)
+    assert len(out) == 16
+    return out
+
+
+def _e4m3_byte_of(value):
+    """The E4M3 byte of an exactly representable value, found through
+    torch's float8_e4m3fn decode (not the oracle's)."""
+    torch = _torch()
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    hit = np.nonzero((vals == value) & ~np.isnan(vals) & (np.signbit(vals) == np.signbit(value)))[0]
+    assert hit.size == 1, value
+    return np.uint8(hit[0])
+
+
+def _fp8_of_fp4(rows_of_nibbles):
+    """E2M1 bytes [..., 64] (low nibble first) as E4M3 bytes [..., 128] of
+    the same values."""
+    table = e2m1_table()
+    lut = np.array([_e4m3_byte_of(table[c]) for c in range(16)], np.uint8)
+    b = np.asarray(rows_of_nibbles, np.uint8)
+    out = np.empty(b.shape[:-1] + (b.shape[-1] * 2,), np.uint8)
+    out[..., 0::2] = lut[b & 15]
+    out[..., 1::2] = lut[b >> 4]
+    return out
+
+
+def pin_e2m1_by_format_table(so):
+    """Every E2M1 code decodes to the value the format's definition gives
+    (the golden table), and each of those values is an E4M3 value under
+    torch's decode."""
+    table = e2m1_table()
+    v = so.e2m1(np.arange(16, dtype=np.uint8))
+    for c in range(16):
+        assert v[c] == table[c] and np.signbit(v[c]) == np.signbit(table[c]), (c, v[c], table[c])
+        _e4m3_byte_of(table[c])
+
+
+def pin_mxfp4_nibble_order(so):
+    """Closed form: a byte's two nibbles are two dims.  A key holding 6 in
+    the high nibble of byte 0 against a head holding 1 in the same nibble
+    (weight 1, all scales 1) gives 6 (0x40C0); the head's 1 in the other
+    nibble gives +0.  (Which nibble is the even dim cannot change a logit:
+    the query and the key share the order, and a byte never straddles two
+    scale blocks.)"""
+    q = np.zeros((HEADS, DIM // 2), np.uint8)
+    qs = np.full((HEADS, 4), 127, np.uint8)
+    key = np.zeros(DIM // 2, np.uint8)
+    ks = np.full(4, 127, np.uint8)
+    w = np.zeros(HEADS, np.uint16)
+    w[0] = 0x3F80
+    key[0] = 0x70   # dim 1: code 7 (6.0); dim 0: code 0
+    q[0, 0] = 0x20  # dim 1: code 2 (1.0)
+    assert so.mxfp4_logit(q, qs, w, key, ks)[0] == 0x40C0
+    q[0, 0] = 0x02  # dim 0: code 2
+    assert so.mxfp4_logit(q, qs, w, key, ks)[0] == 0x0000
+
+
+def _random_fp4(rng, shape):
+    return rng.integers(0, 256, shape, dtype=np.uint8)
+
+
+def pin_mxfp4_unit_scales_equal_fp8(so):
+    """With every scale 1 (byte 127) an MXFP4 logit is the FP8 logit of the
+    same values (E4M3 bytes by torch's decode, key scale 127): exact value
+    and tolerance interval alike."""
+    rng = np.random.default_rng(21)
+    for trial in range(24):
+        q4 = _random_fp4(rng, (HEADS, DIM // 2))
+        k4 = _random_fp4(rng, (DIM // 2,))
+        w = _bf16_bits_of_f32(rng.standard_normal(HEADS).astype(np.float32) * 0.5)
+        qs = np.full((HEADS, 4), 127, np.uint8)
+        ks = np.full(4, 127, np.uint8)
+        for delta in (0.0, 2.0 ** -20, 2.0 ** -10):
+            a = so.mxfp4_logit(q4, qs, w, k4, ks, delta)
+            b = so.mqa_logit(_fp8_of_fp4(q4), w, _fp8_of_fp4(k4), 127, delta)
+            a = tuple(0 if x == 0x8000 else x for x in a)
+            b = tuple(0 if x == 0x8000 else x for x in b)
+            assert a == b, (trial, delta, [hex(x) for x in a], [hex(x) for x in b])
+
+
+def pin_mxfp4_block_scales(so):
+    """Closed form: when only block b of the key holds values and every
+    head's scale of block b is the same sq, the two scales act as one power
+    of two on each dot product, so the logit is the FP8 logit of the same
+    values with the key scale byte sq + sk - 127 (the other blocks' scales
+    are then irrelevant)."""
+    rng = np.random.default_rng(22)
+    for trial in range(32):
+        b = trial % 4
+        q4 = _random_fp4(rng, (HEADS, DIM // 2))
+        k4 = np.zeros(DIM // 2, np.uint8)
+        k4[16 * b:16 * b + 16] = _random_fp4(rng, (16,))
+        w = _bf16_bits_of_f32(rng.standard_normal(HEADS).astype(np.float32) * 0.5)
+        qs = rng.integers(100, 155, (HEADS, 4)).astype(np.uint8)
+        sq = int(rng.integers(110, 145))
+        qs[:, b] = sq
+        ks = rng.integers(100, 155, 4).astype(np.uint8)
+        sk = int(rng.integers(110, 145))
+        ks[b] = sk
+        a = so.mxfp4_logit(q4, qs, w, k4, ks)[0]
+        f = so.mqa_logit(_fp8_of_fp4(q4), w, _fp8_of_fp4(k4), sq + sk - 127)[0]
+        assert (0 if a == 0x8000 else a) == (0 if f == 0x8000 else f), (trial, hex(a), hex(f))
+
+
+def pin_mxfp4_interval(so):
+    """The MXFP4 tolerance interval: a point with delta 0; with delta 2^-20
+    on block scales 120..134 it holds the exact value and grows with delta."""
+    rng = np.random.default_rng(23)
+    rows, nk = 2, 16
+    q = _random_fp4(rng, (rows, HEADS, DIM // 2))
+    qs = rng.integers(120, 135, (rows, HEADS, 4)).astype(np.uint8)
+    w = _bf16_bits_of_f32(rng.standard_normal((rows, HEADS)).astype(np.float32) * 0.5)
+    keys = _random_fp4(rng, (nk, DIM // 2))
+    ks = rng.integers(120, 135, (nk, 4)).astype(np.uint8)
+    ex, lo, hi = so.mxfp4_logits(q, qs, w, keys, ks, 0.0)
+    assert np.array_equal(lo, ex) and np.array_equal(hi, ex)
+    widths = []
+    for delta in (2.0 ** -20, 2.0 ** -12, 2.0 ** -6):
+        e2, l2, h2 = so.mxfp4_logits(q, qs, w, keys, ks, delta)
+        assert np.array_equal(e2, ex)
+        kl, ke, kh = _value_key(l2), _value_key(e2), _value_key(h2)
+        assert np.all(kl <= ke) and np.all(ke <= kh)
+        widths.append(int((kh - kl).sum()))
+    assert widths[0] <= widths[1] <= widths[2] and widths[2] > 0, widths
+
+
 ALL_PINS = [pin_e4m3_by_torch, pin_bf16_round_by_torch, pin_single_head_by_torch,
-            pin_sum_of_ones, pin_worked_cases, pin_interval]
+            pin_sum_of_ones, pin_worked_cases, pin_interval, pin_e2m1_by_format_table,
+            pin_mxfp4_nibble_order, pin_mxfp4_unit_scales_equal_fp8, pin_mxfp4_block_scales,
+            pin_mxfp4_interval]
 
 
 if __name__ == "__main__":

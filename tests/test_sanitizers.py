@@ -35,6 +35,19 @@ def test_oracle_under_asan_and_ubsan(tmp_path):
     assert "runtime error" not in log and "AddressSanitizer" not in log, log
 
 
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no gcc")
+def test_score_oracle_under_asan_and_ubsan(tmp_path):
+    exe = str(tmp_path / "score_driver")
+    rc, log = _run(["gcc", "-std=c11", "-O1", "-g", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=all", "-Wall", "-Wextra", "-Werror",
+                    os.path.join(HERE, "score_driver.c"),
+                    os.path.join(ROOT, "oracle", "score_oracle.c"), "-lm", "-o", exe])
+    assert rc == 0, log
+    rc, log = _run([exe])
+    assert rc == 0 and "score driver done" in log, log
+    assert "runtime error" not in log and "AddressSanitizer" not in log, log
+
+
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="no hipcc")
 def test_host_checks_under_asan_and_ubsan(tmp_path):
     lib = str(tmp_path / "libtopk_san.so")

@@ -1,4 +1,4 @@
-"""The FP8 MQA logits oracle against its pins, and the pins against planted
+"""The FP8 and MXFP4 MQA logits oracle against its pins, and the pins against planted
 mistakes (one-line changes to a temporary copy of oracle/score_oracle.c,
 compiled on the CPU; every copy must fail at least one pin)."""
 import os
@@ -40,6 +40,12 @@ MUTANTS = [
     ("interval without delta", "const long double dl = d - (long double)delta * s, dh = d + (long double)delta * s;",
      "const long double dl = d, dh = d;"),
     ("negative weights keep bounds", "(wh >= 0 ? rlo[h] : rhi[h]) * wh + al[j];", "rlo[h] * wh + al[j];"),
+    ("E2M1 bias 2", "v = ldexpl(1.0L + m / 2.0L, e - 1);", "v = ldexpl(1.0L + m / 2.0L, e - 2);"),
+    ("E2M1 subnormal step", "v = m / 2.0L;", "v = m / 4.0L;"),
+    ("blocks of 16 dims", "const int b = c / 32;", "const int b = c / 16 % 4;"),
+    ("query scales ignored", "(int)q_scale[h * 4 + b] + (int)key_scale[b] - 254", "127 + (int)key_scale[b] - 254"),
+    ("key scale of block 0 only", "(int)q_scale[h * 4 + b] + (int)key_scale[b] - 254", "(int)q_scale[h * 4 + b] + (int)key_scale[0] - 254"),
+    ("MXFP4 scaled again after the sum", "logit_of_heads(dd, ss, w, delta, 1.0L, 1, exact, lo, hi);", "logit_of_heads(dd, ss, w, delta, 2.0L, 1, exact, lo, hi);"),
 ]
 
 
