@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     PATH_TOPS,
     TopkError,
     fp8_mqa_logits,
+    mxfp4_mqa_logits,
     library,
     probe_library,
     stream_read,

@@ -93,6 +93,10 @@ def library():
                                             ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         lib.topk_fp8_mqa_logits.restype = ctypes.c_int
+        lib.topk_mxfp4_mqa_logits.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64,
+                                              ctypes.c_void_p] + [ctypes.c_int32] * 3 + [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        lib.topk_mxfp4_mqa_logits.restype = ctypes.c_int
         lib.topk_status_string.argtypes = [ctypes.c_int]
         lib.topk_status_string.restype = ctypes.c_char_p
         lib.topk_last_error.argtypes = []
@@ -275,21 +279,48 @@ def fp8_mqa_logits(q: torch.Tensor, w: torch.Tensor, keys: torch.Tensor,
     logits     16-bit [rows, >= width] (unit stride along a row), tops 16-bit
                [rows, >= ceil(width / 8) rounded up to 8]; allocated if None
     Returns (logits, tops)."""
+    return _score(False, q, None, w, keys, key_scale, valid_len, qpr, width, logits, tops,
+                  stream)
+
+
+def mxfp4_mqa_logits(q: torch.Tensor, q_scale: torch.Tensor, w: torch.Tensor,
+                     keys: torch.Tensor, key_scale: torch.Tensor, valid_len: torch.Tensor,
+                     qpr: int = 1, width: int | None = None, logits: torch.Tensor | None = None,
+                     tops: torch.Tensor | None = None,
+                     stream: torch.cuda.Stream | None = None):
+    """The MXFP4 MQA indexer logits and their vector maxima
+    (topk_mxfp4_mqa_logits in include/libtopk.h).
+    q          uint8 [rows, 32, 64] (E2M1, two a byte, low nibble first)
+    q_scale    uint8 [rows, 32, 4] (UE8M0 of each head's 32-dim blocks)
+    keys       uint8 [requests, key_stride, 64] (E2M1)
+    key_scale  uint8 [requests, key_stride, 4] (UE8M0 of each key's blocks)
+    the rest as for fp8_mqa_logits.  Returns (logits, tops)."""
+    return _score(True, q, q_scale, w, keys, key_scale, valid_len, qpr, width, logits, tops,
+                  stream)
+
+
+def _score(fp4, q, q_scale, w, keys, key_scale, valid_len, qpr, width, logits, tops, stream):
     lib = library()
-    if q.dtype != torch.uint8 or q.dim() != 3 or tuple(q.shape[1:]) != (32, 128) or not q.is_contiguous():
-        raise ValueError("q must be contiguous uint8 [rows, 32, 128]")
+    qb = 64 if fp4 else 128
+    if q.dtype != torch.uint8 or q.dim() != 3 or tuple(q.shape[1:]) != (32, qb) or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous uint8 [rows, 32, {qb}]")
     rows = q.shape[0]
     dev = q.device
+    if fp4 and (q_scale is None or q_scale.dtype != torch.uint8
+                or tuple(q_scale.shape) != (rows, 32, 4) or not q_scale.is_contiguous()
+                or q_scale.device != dev):
+        raise ValueError("q_scale must be contiguous uint8 [rows, 32, 4] on the same GPU")
     if w.dtype not in (torch.bfloat16, torch.int16, torch.uint16) or tuple(w.shape) != (rows, 32) \
             or not w.is_contiguous() or w.device != dev:
         raise ValueError("w must be contiguous 16-bit [rows, 32] on the same GPU")
-    if keys.dtype != torch.uint8 or keys.dim() != 3 or keys.shape[2] != 128 \
+    if keys.dtype != torch.uint8 or keys.dim() != 3 or keys.shape[2] != qb \
             or not keys.is_contiguous() or keys.device != dev:
-        raise ValueError("keys must be contiguous uint8 [requests, key_stride, 128]")
+        raise ValueError(f"keys must be contiguous uint8 [requests, key_stride, {qb}]")
     requests, key_stride = keys.shape[0], keys.shape[1]
-    if key_scale.dtype != torch.uint8 or tuple(key_scale.shape) != (requests, key_stride) \
+    ks_shape = (requests, key_stride, 4) if fp4 else (requests, key_stride)
+    if key_scale.dtype != torch.uint8 or tuple(key_scale.shape) != ks_shape \
             or not key_scale.is_contiguous() or key_scale.device != dev:
-        raise ValueError("key_scale must be contiguous uint8 [requests, key_stride]")
+        raise ValueError(f"key_scale must be contiguous uint8 {list(ks_shape)}")
     if int(qpr) < 1 or rows != requests * int(qpr):
         raise ValueError(f"rows {rows} must be requests {requests} x qpr {qpr}")
     if valid_len.dtype != torch.int32 or valid_len.numel() != rows or valid_len.device != dev:
@@ -312,11 +343,15 @@ def fp8_mqa_logits(q: torch.Tensor, w: torch.Tensor, keys: torch.Tensor,
         raise ValueError("tops must be 16-bit [rows, >= ceil(width / 8)] on the same GPU")
     with torch.cuda.device(dev):
         s = stream if stream is not None else torch.cuda.current_stream(dev)
-        rc = lib.topk_fp8_mqa_logits(q.data_ptr(), w.data_ptr(), keys.data_ptr(),
-                                     key_scale.data_ptr(), int(key_stride), valid_len.data_ptr(),
-                                     int(rows), int(qpr), int(width), logits.data_ptr(),
-                                     int(logits.stride(0)), tops.data_ptr(), int(tops.stride(0)),
-                                     ctypes.c_void_p(s.cuda_stream))
+        tail = (int(key_stride), valid_len.data_ptr(), int(rows), int(qpr), int(width),
+                logits.data_ptr(), int(logits.stride(0)), tops.data_ptr(), int(tops.stride(0)),
+                ctypes.c_void_p(s.cuda_stream))
+        if fp4:
+            rc = lib.topk_mxfp4_mqa_logits(q.data_ptr(), q_scale.data_ptr(), w.data_ptr(),
+                                           keys.data_ptr(), key_scale.data_ptr(), *tail)
+        else:
+            rc = lib.topk_fp8_mqa_logits(q.data_ptr(), w.data_ptr(), keys.data_ptr(),
+                                         key_scale.data_ptr(), *tail)
     if rc != 0:
         raise TopkError(rc, lib.topk_last_error().decode())
     return logits, tops

@@ -266,6 +266,37 @@ int topk_fp8_mqa_logits(const uint8_t *q, const uint16_t *w, const uint8_t *keys
                         int32_t width, uint16_t *logits, int64_t logits_stride,
                         uint16_t *tops, int64_t tops_stride, void *stream);
 
+/* The same logits and side array from an MXFP4 indexer cache (the same
+ * page: IndexerScore's FP4 path, whose block-scaled MMA applies the scales
+ * and whose epilogue applies none after the head sum):
+ *   logits[t][i] = sum over heads h of bf16(relu(d(t, h, i))) * w[t][h],
+ *   d(t, h, i) = sum over blocks b = 0..3 of 2^(qs[t][h][b] + ks[i][b] - 254)
+ *                * (sum over dims c of block b (32 dims) of q[t][h][c] * key[i][c])
+ * with the head chain, the BF16 roundings and tops exactly as for
+ * topk_fp8_mqa_logits (the four accumulators, the pairing), no scale after
+ * the sum, and a -0 logit written as +0.  Elements are OCP FP4 E2M1 (values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two a byte: dim 2j in
+ * the low nibble of byte j, 2j + 1 in the high nibble.
+ *   q            device E2M1 [rows, 32, 64], 16-byte aligned
+ *   q_scale      device UE8M0 [rows, 32, 4]: head h's scale of dims 32b ..
+ *                32b + 31 at byte (t * 32 + h) * 4 + b (a caller folding a
+ *                per-row query scale folds it into w instead)
+ *   w            device BF16 [rows, 32] head weights, 4-byte aligned
+ *   keys         device E2M1 [requests, key_stride, 64], 16-byte aligned
+ *   key_scale    device UE8M0 [requests, key_stride, 4]: key i's scale of
+ *                dims 32b .. 32b + 31 at byte (r * key_stride + i) * 4 + b
+ * and the other arguments as for topk_fp8_mqa_logits.  The matrix cores'
+ * block-scaled FP32 sums may differ from the exact dot product in its last
+ * FP32 bits (when the blocks' scales differ); a logit then differs from
+ * that of the exact dot products only where a BF16 rounding decides it.
+ * Returns TOPK_OK or a negative topk_status; asynchronous on `stream`,
+ * allocates nothing. */
+int topk_mxfp4_mqa_logits(const uint8_t *q, const uint8_t *q_scale, const uint16_t *w,
+                          const uint8_t *keys, const uint8_t *key_scale, int64_t key_stride,
+                          const int32_t *valid_len, int32_t rows, int32_t qpr,
+                          int32_t width, uint16_t *logits, int64_t logits_stride,
+                          uint16_t *tops, int64_t tops_stride, void *stream);
+
 /* Deterministic ordered top-k of every row (vLLM API page
  * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.dsa.indexer",
  * IndexerSelect: the selected keys in key order with -1 past the row's

@@ -88,6 +88,15 @@ int main() {
                                            16, nullptr), -1);
   expect("score nothing", topk_fp8_mqa_logits(nullptr, nullptr, nullptr, nullptr, 0, nullptr, 0,
                                               1, 100, nullptr, 0, nullptr, 0, nullptr), 0);
+  expect("mxfp4 q scale null", topk_mxfp4_mqa_logits(QB, nullptr, WB, KB, SB, 100, VL, 4, 2, 100,
+                                                     LB, 100, TW, 16, nullptr), -1);
+  expect("mxfp4 keys aligned", topk_mxfp4_mqa_logits(QB, SB, WB, KB + 4, SB, 100, VL, 4, 2, 100,
+                                                     LB, 100, TW, 16, nullptr), -2);
+  expect("mxfp4 tops stride", topk_mxfp4_mqa_logits(QB, SB, WB, KB, SB, 100, VL, 4, 2, 100, LB,
+                                                    100, TW, 12, nullptr), -1);
+  expect("mxfp4 nothing", topk_mxfp4_mqa_logits(nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                                nullptr, 0, 1, 100, nullptr, 0, nullptr, 0,
+                                                nullptr), 0);
   expect("reserve k", topk_reserve_scratch(4, 1 << 20, 0, 0, 0, nullptr), -1);
   expect("reserve one workgroup", topk_reserve_scratch(4, 16384, 8, 0, 1, nullptr), 0);
   for (int s = -6; s <= 1; ++s) {

@@ -53,8 +53,8 @@ def test_header_declares_entry_points():
     assert "topk_bf16_rows_ordered" in names and "topk_bf16_rows_ordered_ex" in names
     assert "topk_bf16_rows_noalloc" in names
     assert "topk_bf16_rows_tops" in names and "topk_bf16_vector_maxima" in names
-    assert "topk_fp8_mqa_logits" in names
-    assert len(names) >= 11
+    assert "topk_fp8_mqa_logits" in names and "topk_mxfp4_mqa_logits" in names
+    assert len(names) >= 12
 
 
 def test_library_exports_every_declared_symbol():
@@ -231,3 +231,36 @@ def test_score_nothing_to_do():
                        logits=None, tops=None) == 0
     assert _call_score(width=0, q=None, w=None, keys=None, key_scale=None, valid_len=None,
                        logits=None, tops=None) == 0
+
+
+def _call_score_fp4(**kw):
+    lib = T.library()
+    a = dict(q=4096, q_scale=5, w=64, keys=8192, key_scale=7, key_stride=100, valid_len=64,
+             rows=4, qpr=2, width=100, logits=1024, logits_stride=100, tops=2048, tops_stride=16,
+             stream=None)
+    a.update(kw)
+    return lib.topk_mxfp4_mqa_logits(a["q"], a["q_scale"], a["w"], a["keys"], a["key_scale"],
+                                     a["key_stride"], a["valid_len"], a["rows"], a["qpr"],
+                                     a["width"], a["logits"], a["logits_stride"], a["tops"],
+                                     a["tops_stride"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-2), -1), (dict(qpr=0), -1), (dict(qpr=9), -1), (dict(rows=5), -1),
+    (dict(width=-1), -1), (dict(width=(1 << 20) + 1), -1), (dict(q=None), -1),
+    (dict(q_scale=None), -1), (dict(w=None), -1), (dict(keys=None), -1),
+    (dict(key_scale=None), -1), (dict(valid_len=None), -1), (dict(logits=None), -1),
+    (dict(tops=None), -1), (dict(key_stride=99), -1), (dict(logits_stride=99), -1),
+    (dict(tops_stride=12), -1), (dict(q=4104), -2), (dict(keys=8200), -2), (dict(w=66), -2),
+    (dict(logits=1025), -2), (dict(tops=2049), -2),
+])
+def test_score_mxfp4_rejects_bad_arguments(kw, status):
+    assert _call_score_fp4(**kw) == status
+    assert T.library().topk_last_error()
+
+
+def test_score_mxfp4_nothing_to_do():
+    assert _call_score_fp4(rows=0, q=None, q_scale=None, w=None, keys=None, key_scale=None,
+                           valid_len=None, logits=None, tops=None) == 0
+    assert _call_score_fp4(width=0, q=None, q_scale=None, w=None, keys=None, key_scale=None,
+                           valid_len=None, logits=None, tops=None) == 0

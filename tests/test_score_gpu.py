@@ -1,4 +1,5 @@
-"""GPU parity of the FP8 MQA indexer logits (topk_fp8_mqa_logits) through
+"""GPU parity of the FP8 and MXFP4 MQA indexer logits (topk_fp8_mqa_logits,
+topk_mxfp4_mqa_logits) through
 the C ABI, against the scorer oracle (oracle/score_oracle.c), and of the
 selection they feed.
 
@@ -175,6 +176,135 @@ def test_full_size_sampled():
         v = max(0, min(int(d["valid_len"][t]), d["width"]))
         cols = np.sort(rng.choice(v, size=min(v, 4000 // rows), replace=False))
         ex, lo, hi = oracle_row(d, t, DELTA, cols)
+        g = _vkey(logits[t, cols])
+        assert np.all((g >= _vkey(lo[0])) & (g <= _vkey(hi[0]))), f"row {t}"
+    check_untouched_and_tops(d, logits, tops)
+
+
+# -- MXFP4 (topk_mxfp4_mqa_logits).  The matrix cores' block-scaled sums are
+# exact when each dot product's products share one power of two ("uniform"
+# scales: a head's four blocks alike and a key's four alike), and then
+# every logit must equal the oracle's; with a scale per block they may lose
+# the last FP32 bits (measured at most 2^-23.5 of the sum of the products'
+# magnitudes), and every logit must lie in the oracle's interval for an
+# allowance of 2^-20 of that sum.
+DELTA4 = 2.0 ** -20
+
+
+def run_score_fp4(d, width=None):
+    width = d["width"] if width is None else width
+    rows = d["q"].shape[0]
+    dev = torch.device("cuda", 0)
+    args = [torch.from_numpy(d[k]).to(dev) for k in ("q", "q_scale")]
+    w = torch.from_numpy(d["w"].view(np.int16)).to(dev)
+    keys = torch.from_numpy(d["keys"]).to(dev)
+    ks = torch.from_numpy(d["key_scale"]).to(dev)
+    vl = torch.from_numpy(d["valid_len"]).to(dev)
+    nv = (width + 7) // 8
+    logits = torch.full((rows, max(8, -(-width // 8) * 8)), SENTINEL, dtype=torch.int16, device=dev)
+    tops = torch.full((rows, max(8, -(-nv // 8) * 8)), SENTINEL, dtype=torch.int16, device=dev)
+    T.mxfp4_mqa_logits(args[0], args[1], w, keys, ks, vl, d["qpr"], width=width, logits=logits,
+                       tops=tops)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy().view(np.uint16), tops.cpu().numpy().view(np.uint16)
+
+
+def oracle_row_fp4(d, t, delta, cols=None):
+    so = score.load()
+    r = t // d["qpr"]
+    v = max(0, min(int(d["valid_len"][t]), d["width"]))
+    idx = np.arange(v) if cols is None else np.asarray(cols)
+    return so.mxfp4_logits(d["q"][t:t + 1], d["q_scale"][t:t + 1], d["w"][t:t + 1],
+                           d["keys"][r][idx], d["key_scale"][r][idx], delta)
+
+
+@pytest.mark.parametrize("requests,qpr,width,ks", [(2, 3, 700, 720), (3, 1, 257, 257),
+                                                    (1, 2, 1031, 1100)])
+def test_mxfp4_uniform_scales_bit_exact(requests, qpr, width, ks):
+    d = W.make_score_mxfp4(requests, qpr, width, "uniform", seed=width, key_stride=ks)
+    print(f"score mxfp4 uniform requests={requests} qpr={qpr} width={width}", flush=True)
+    logits, tops = run_score_fp4(d)
+    for t in range(d["q"].shape[0]):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        ex, lo, hi = oracle_row_fp4(d, t, 0.0)
+        assert np.array_equal(lo, ex) and np.array_equal(hi, ex)
+        bad = np.nonzero(logits[t, :v] != ex[0])[0]
+        assert bad.size == 0, f"row {t}: {bad.size} logits differ, first at key {bad[:3]}"
+    check_untouched_and_tops(d, logits, tops)
+
+
+@pytest.mark.parametrize("requests,qpr,width", [(3, 2, 1000), (2, 1, 4096)])
+def test_mxfp4_block_scales_within_the_interval(requests, qpr, width):
+    d = W.make_score_mxfp4(requests, qpr, width, "blocks", seed=width + 7)
+    print(f"score mxfp4 blocks requests={requests} qpr={qpr} width={width}", flush=True)
+    logits, tops = run_score_fp4(d)
+    same = total = 0
+    for t in range(d["q"].shape[0]):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        ex, lo, hi = oracle_row_fp4(d, t, DELTA4)
+        g = _vkey(logits[t, :v])
+        out = np.nonzero((g < _vkey(lo[0])) | (g > _vkey(hi[0])))[0]
+        assert out.size == 0, f"row {t}: {out.size} logits outside the interval, first {out[:3]}"
+        same += int((logits[t, :v] == ex[0]).sum())
+        total += v
+    print(f"  {same} of {total} logits equal the exact dot products' ({same / max(total, 1):.4f})")
+    check_untouched_and_tops(d, logits, tops)
+
+
+def test_mxfp4_lengths_and_many_verify_rows():
+    d = W.make_score_mxfp4(10, 1, 600, "uniform", seed=3, key_stride=640)
+    d["valid_len"] = np.array([0, 1, 7, 8, 9, 255, 256, 257, 600, 611], np.int32)
+    logits, tops = run_score_fp4(d)
+    for t in range(10):
+        v = max(0, min(int(d["valid_len"][t]), 600))
+        ex, _, _ = oracle_row_fp4(d, t, 0.0)
+        assert np.array_equal(logits[t, :v], ex[0]), f"row {t} (v={v})"
+    check_untouched_and_tops(d, logits, tops)
+    d = W.make_score_mxfp4(2, 8, 333, "uniform", seed=4)
+    d["valid_len"][3] = -3
+    logits, tops = run_score_fp4(d)
+    for t in range(16):
+        v = max(0, min(int(d["valid_len"][t]), 333))
+        ex, _, _ = oracle_row_fp4(d, t, 0.0)
+        assert np.array_equal(logits[t, :v], ex[0]), f"qpr 8 row {t} (v={v})"
+    check_untouched_and_tops(d, logits, tops)
+
+
+def test_mxfp4_scores_feed_the_selection():
+    d = W.make_score_mxfp4(6, 2, 20000, "blocks", seed=12)
+    logits, tops = run_score_fp4(d)
+    rows = logits.shape[0]
+    dev = torch.device("cuda", 0)
+    L = torch.from_numpy(logits.view(np.int16)).to(dev)
+    VL = torch.from_numpy(d["valid_len"]).to(dev)
+    tp = torch.from_numpy(tops.view(np.int16)).to(dev)
+    pc = torch.full((rows,), -9, dtype=torch.int32, device=dev)
+    k = 512
+    out = T.topk_bf16_rows_tops(L, VL, k, tp, 0, width=d["width"], path_codes=pc)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy()
+    sel = dict(logits=logits, valid_len=d["valid_len"], k=k, mode=0, width=d["width"],
+               pages=None, page_size=0)
+    o = oracle.topk(logits, d["valid_len"], k, 0, width=d["width"], threads=16)
+    bad = check(oracle.default(), sel, g, o)
+    assert not bad, "\n".join(bad)
+    assert np.all(pc.cpu().numpy() == T.PATH_TOPS), pc.cpu().numpy()
+
+
+def test_mxfp4_full_size_sampled():
+    """The benchmark's MXFP4 workload (64 requests x 150000 keys): 4000
+    sampled logits in the oracle's interval, every row's maxima those of
+    its logits."""
+    c = W.SCORE_FP4_CONFIG
+    d = W.make_score_mxfp4(c["requests"], c["qpr"], c["width"], "blocks", seed=0)
+    print(f"score full size {c['name']}", flush=True)
+    logits, tops = run_score_fp4(d)
+    rng = np.random.Generator(np.random.PCG64(6))
+    rows = d["q"].shape[0]
+    for t in range(rows):
+        v = max(0, min(int(d["valid_len"][t]), d["width"]))
+        cols = np.sort(rng.choice(v, size=min(v, 4000 // rows), replace=False))
+        ex, lo, hi = oracle_row_fp4(d, t, DELTA4, cols)
         g = _vkey(logits[t, cols])
         assert np.all((g >= _vkey(lo[0])) & (g <= _vkey(hi[0]))), f"row {t}"
     check_untouched_and_tops(d, logits, tops)

@@ -208,6 +208,7 @@ def make(cfg: int, rows: int | None = None, width: int | None = None,
 # here, so the bytes are drawn directly: a sign, an exponent field and a
 # mantissa per value (the generator decodes nothing).
 SCORE_CONFIG = dict(name="score_fp8_64x150000_q1", requests=64, qpr=1, width=150000)
+SCORE_FP4_CONFIG = dict(name="score_mxfp4_64x150000_q1", requests=64, qpr=1, width=150000)
 
 
 def _e4m3_bytes(rng, shape, kind: str) -> np.ndarray:
@@ -256,4 +257,41 @@ def make_score(requests: int, qpr: int, width: int, kind: str = "wide", seed: in
         for u in range(qpr):
             vl[r * qpr + u] = max(0, int(lens[r]) - (qpr - 1 - u))
     return dict(q=q, w=w, keys=keys, key_scale=key_scale, valid_len=vl, qpr=qpr, width=width,
+                requests=requests, kind=kind)
+
+
+def make_score_mxfp4(requests: int, qpr: int, width: int, kind: str = "blocks", seed: int = 0,
+                     key_stride: int | None = None, ragged: bool = True) -> dict:
+    """Seeded MXFP4 scorer inputs: q uint8 [rows, 32, 64] and keys uint8
+    [requests, key_stride, 64] of random E2M1 nibbles (two a byte), q_scale
+    uint8 [rows, 32, 4] and key_scale uint8 [requests, key_stride, 4] of
+    UE8M0 bytes 120..134, w and valid_len as make_score.  kind "uniform":
+    one scale for all four blocks of a head and of a key (each dot product
+    then sums exactly in FP32); "blocks": a scale per 32-dim block."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = requests * qpr
+    ks = width if key_stride is None else key_stride
+    q = rng.integers(0, 256, (rows, 32, 64), dtype=np.uint8)
+    keys = np.empty((requests, ks, 64), np.uint8)
+    for r in range(requests):
+        keys[r] = rng.integers(0, 256, (ks, 64), dtype=np.uint8)
+    if kind == "uniform":
+        q_scale = np.repeat(rng.integers(120, 135, (rows, 32, 1), dtype=np.uint8), 4, axis=2)
+        key_scale = np.repeat(rng.integers(120, 135, (requests, ks, 1), dtype=np.uint8), 4, axis=2)
+    elif kind == "blocks":
+        q_scale = rng.integers(120, 135, (rows, 32, 4), dtype=np.uint8)
+        key_scale = rng.integers(120, 135, (requests, ks, 4), dtype=np.uint8)
+    else:
+        raise ValueError(kind)
+    w = f32_to_bf16_bits(rng.standard_normal((rows, 32), dtype=np.float32) * np.float32(0.25))
+    if ragged:
+        lens = rng.integers(width // 2, width + 1, requests)
+    else:
+        lens = np.full(requests, width)
+    vl = np.empty(rows, np.int32)
+    for r in range(requests):
+        for u in range(qpr):
+            vl[r * qpr + u] = max(0, int(lens[r]) - (qpr - 1 - u))
+    return dict(q=q, q_scale=np.ascontiguousarray(q_scale), w=w, keys=keys,
+                key_scale=np.ascontiguousarray(key_scale), valid_len=vl, qpr=qpr, width=width,
                 requests=requests, kind=kind)
