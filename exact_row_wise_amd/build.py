@@ -31,13 +31,17 @@ def command(out: str = LIB, extra=(), src=(SRC, SCORE_SRC)) -> list[str]:
     srcs = [src] if isinstance(src, str) else list(src)
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-        # no packed FP32: the only floating point on the path sizes the work
-        # (sample ranks, the cutoff shift); keep the backend from forming
-        # packed FP32 ops from it
+        # no packed FP32: keep the backend from forming packed FP32 ops
+        # (the selection's floating point only sizes the work; the scorer's
+        # epilogue is scalar FP32 FMAs and roundings to BF16)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         # every wave-level atomic here is already issued by one lane with the
         # wave's total; the backend's own aggregation would only add work
         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
+        # the scorer's matrix-core results land in VGPRs, where its epilogue
+        # reads them, instead of AGPRs copied out one by one (the selection
+        # has no MFMA: its code is the same either way)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
         "-I", INCLUDE, *extra, "-o", out, *srcs,
     ]

@@ -72,6 +72,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ float lo_f(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float hi_f(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 
+// relu of a head's FP32 dot product (NaN counts as 0).  E2M1 inputs hold
+// no NaN, so there the sign bit alone decides: one integer maximum of the
+// bits (negatives and -0 become +0).
+template <bool FP4>
+__device__ __forceinline__ float relu(float x) {
+  if constexpr (FP4) return __int_as_float(max(__float_as_int(x), 0));
+  return x > 0.f ? x : 0.f;
+}
+
 // The order-preserving 16-bit key of a BF16 pattern.
 __device__ __forceinline__ uint32_t order16(uint32_t b) {
   return b ^ ((b & 0x8000u) ? 0xFFFFu : 0x8000u);
@@ -166,6 +175,15 @@ __global__ __launch_bounds__(kScoreNT) void topk_mqa_score(ScoreParams p) {
       qa = ld32(qt + (int64_t)lc * kDim + 32 * lg);
       qb = ld32(qt + (int64_t)(16 + lc) * kDim + 32 * lg);
     }
+    // the head weights as FP32 (the same in every lane: scalar registers)
+    const uint32_t* wt = reinterpret_cast<const uint32_t*>(p.w + (int64_t)t * kHeads);
+    float wf[kHeads];
+#pragma unroll
+    for (int i = 0; i < kHeads / 2; ++i) {
+      const uint32_t x = wt[i];
+      wf[2 * i] = lo_f(x);
+      wf[2 * i + 1] = hi_f(x);
+    }
     // heads x keys, relu, BF16, into the wave's transpose area: key row
     // 16 c + l % 16, heads 4 (l / 16) .. +4 (and 16 more)
 #pragma unroll
@@ -173,10 +191,10 @@ __global__ __launch_bounds__(kScoreNT) void topk_mqa_score(ScoreParams p) {
       const v4f da = FP4 ? mfma_fp4(qa, kop[c], sqa, ksc[c]) : mfma_fp8(qa, kop[c]);
       const v4f db = FP4 ? mfma_fp4(qb, kop[c], sqb, ksc[c]) : mfma_fp8(qb, kop[c]);
       uint8_t* row = lt + (16 * c + lc) * kRowBytes;
-      const uint2 pa = make_uint2(pack_bf16(da[0] > 0.f ? da[0] : 0.f, da[1] > 0.f ? da[1] : 0.f),
-                                  pack_bf16(da[2] > 0.f ? da[2] : 0.f, da[3] > 0.f ? da[3] : 0.f));
-      const uint2 pb = make_uint2(pack_bf16(db[0] > 0.f ? db[0] : 0.f, db[1] > 0.f ? db[1] : 0.f),
-                                  pack_bf16(db[2] > 0.f ? db[2] : 0.f, db[3] > 0.f ? db[3] : 0.f));
+      const uint2 pa = make_uint2(pack_bf16(relu<FP4>(da[0]), relu<FP4>(da[1])),
+                                  pack_bf16(relu<FP4>(da[2]), relu<FP4>(da[3])));
+      const uint2 pb = make_uint2(pack_bf16(relu<FP4>(db[0]), relu<FP4>(db[1])),
+                                  pack_bf16(relu<FP4>(db[2]), relu<FP4>(db[3])));
       *reinterpret_cast<uint2*>(row + 8 * lg) = pa;
       *reinterpret_cast<uint2*>(row + 32 + 8 * lg) = pb;
     }
@@ -192,16 +210,13 @@ __global__ __launch_bounds__(kScoreNT) void topk_mqa_score(ScoreParams p) {
       r[2 * i] = x.x;
       r[2 * i + 1] = x.y;
     }
-    // the head weights (the same in every lane)
-    const uint32_t* wt = reinterpret_cast<const uint32_t*>(p.w + (int64_t)t * kHeads);
     // accumulators j = 0..3 over heads j, j + 4, ...: pairs (0, 1), (2, 3)
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t w01 = wt[2 * i], w23 = wt[2 * i + 1];
       const uint32_t r01 = r[2 * i], r23 = r[2 * i + 1];
-      const uint32_t s01 = pack_bf16(fmaf(lo_f(r01), lo_f(w01), a0), fmaf(hi_f(r01), hi_f(w01), a1));
-      const uint32_t s23 = pack_bf16(fmaf(lo_f(r23), lo_f(w23), a2), fmaf(hi_f(r23), hi_f(w23), a3));
+      const uint32_t s01 = pack_bf16(fmaf(lo_f(r01), wf[4 * i], a0), fmaf(hi_f(r01), wf[4 * i + 1], a1));
+      const uint32_t s23 = pack_bf16(fmaf(lo_f(r23), wf[4 * i + 2], a2), fmaf(hi_f(r23), wf[4 * i + 3], a3));
       a0 = lo_f(s01);
       a1 = hi_f(s01);
       a2 = lo_f(s23);
