@@ -308,3 +308,86 @@ def test_mxfp4_full_size_sampled():
         g = _vkey(logits[t, cols])
         assert np.all((g >= _vkey(lo[0])) & (g <= _vkey(hi[0]))), f"row {t}"
     check_untouched_and_tops(d, logits, tops)
+
+
+def test_scorers_in_a_replayed_graph():
+    """Both scorers and the selection after them, captured into one HIP
+    graph and replayed three times with eager work and synchronizations in
+    between: every replay's logits, maxima and selection equal the eager
+    calls' (the scorers allocate nothing and record no memset)."""
+    dev = torch.device("cuda", 0)
+    d8 = W.make_score(2, 2, 3000, "wide", seed=31)
+    d4 = W.make_score_mxfp4(2, 2, 3000, "blocks", seed=32)
+    stream = torch.cuda.Stream(dev)
+    outs = {}
+    bufs = {}
+    for name, d in (("fp8", d8), ("fp4", d4)):
+        rows, width = d["q"].shape[0], d["width"]
+        b = dict(q=torch.from_numpy(d["q"]).to(dev), w=torch.from_numpy(d["w"].view(np.int16)).to(dev),
+                 keys=torch.from_numpy(d["keys"]).to(dev), ks=torch.from_numpy(d["key_scale"]).to(dev),
+                 vl=torch.from_numpy(d["valid_len"]).to(dev),
+                 logits=torch.zeros((rows, -(-width // 8) * 8), dtype=torch.int16, device=dev),
+                 tops=torch.zeros((rows, 384), dtype=torch.int16, device=dev),
+                 out=torch.zeros((rows, 256), dtype=torch.int32, device=dev))
+        if name == "fp4":
+            b["qs"] = torch.from_numpy(d["q_scale"]).to(dev)
+        bufs[name] = (d, b)
+
+    def calls():
+        for name, (d, b) in bufs.items():
+            if name == "fp4":
+                T.mxfp4_mqa_logits(b["q"], b["qs"], b["w"], b["keys"], b["ks"], b["vl"], d["qpr"],
+                                   width=d["width"], logits=b["logits"], tops=b["tops"],
+                                   stream=stream)
+            else:
+                T.fp8_mqa_logits(b["q"], b["w"], b["keys"], b["ks"], b["vl"], d["qpr"],
+                                 width=d["width"], logits=b["logits"], tops=b["tops"],
+                                 stream=stream)
+            T.topk_bf16_rows_tops(b["logits"], b["vl"], 256, b["tops"], 0, width=d["width"],
+                                  out=b["out"], stream=stream)
+
+    def snapshot():
+        # the selection's unique part: each row's selected keys as a sorted
+        # multiset (ties at the k-th key may be taken in any order), after
+        # checking that its indices are distinct and valid
+        torch.cuda.synchronize()
+        res = {}
+        for n, (d, b) in bufs.items():
+            lg = b["logits"].cpu().numpy().view(np.uint16)
+            out = b["out"].cpu().numpy()
+            keys = []
+            for t in range(out.shape[0]):
+                v = int(d["valid_len"][t])
+                idx = out[t]
+                assert np.all((idx >= 0) & (idx < v)) and np.unique(idx).size == idx.size, (n, t)
+                keys.append(np.sort(_vkey(lg[t, idx])))
+            res[n] = (b["logits"].cpu().clone(), b["tops"].cpu().clone(), np.array(keys))
+        return res
+
+    def poison():
+        for n, (d, b) in bufs.items():
+            b["logits"].fill_(0x7E57)
+            b["tops"].fill_(0x7E57)
+            b["out"].fill_(-7)
+        torch.cuda.synchronize()
+
+    poison()
+    with torch.cuda.stream(stream):
+        calls()
+    want = snapshot()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        calls()
+    for rep in range(3):
+        poison()
+        with torch.cuda.stream(stream):
+            graph.replay()
+        got = snapshot()
+        for n in want:
+            assert torch.equal(got[n][0], want[n][0]), f"replay {rep}: {n} logits differ"
+            assert torch.equal(got[n][1], want[n][1]), f"replay {rep}: {n} maxima differ"
+            assert np.array_equal(got[n][2], want[n][2]), f"replay {rep}: {n} selection differs"
+        with torch.cuda.stream(stream):
+            calls()  # eager work between the replays
+        torch.cuda.synchronize()
+    del graph
