@@ -13,15 +13,14 @@
 // key into a side array (the vector maxima topk_bf16_rows_tops takes).
 //
 // MI355X design.  Keys are the only large stream (FP8: 128 + 1 bytes a key;
-// MXFP4: 64 + 4), so
-// the kernel is HBM-bound: a workgroup of 4 waves takes 256 consecutive keys
-// of one request and reads each key once for all the request's rows.  Per
-// wave and row, 8 FP8 MFMAs (16 heads x 16 keys x 128 dims each) give the
-// 32 heads of 64 keys (MXFP4: the block-scaled form of the same MFMA, each
-// lane's scale byte covering its 32-dim block); an LDS transpose hands every
-// lane one key's 32 heads,
-// and the lane runs the BF16 chain in FP32 FMAs, each result rounded to BF16
-// by the hardware conversion (to nearest, ties to even).
+// MXFP4: 64 + 4), so the kernel is HBM-bound: a workgroup of 4 waves takes
+// 256 consecutive keys of one request and reads each key once for all the
+// request's rows.  Per wave and row, 8 FP8 MFMAs (16 heads x 16 keys x 128
+// dims each) give the 32 heads of 64 keys (MXFP4: the block-scaled form of
+// the same MFMA, each lane's scale byte covering its 32-dim block); an LDS
+// transpose hands every lane one key's 32 heads, and the lane runs the BF16
+// chain in FP32 FMAs, each result rounded to BF16 by the hardware
+// conversion (to nearest, ties to even).
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
