@@ -391,3 +391,42 @@ def test_scorers_in_a_replayed_graph():
             calls()  # eager work between the replays
         torch.cuda.synchronize()
     del graph
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_odd_strides_and_offsets(fp4):
+    """Logits and maxima rows of odd strides at an odd element offset (the
+    stores are 2-byte), keys in a slot wider than the width: the logits
+    equal the oracle's, nothing past a row's length or between rows is
+    written."""
+    width, ks = 777, 900
+    d = (W.make_score_mxfp4(3, 1, width, "uniform", seed=41, key_stride=ks) if fp4
+         else W.make_score(3, 1, width, "narrow", seed=41, key_stride=ks))
+    rows = d["q"].shape[0]
+    dev = torch.device("cuda", 0)
+    lstride, tstride = width + 5, (width + 7) // 8 + 3
+    lbuf = torch.full((rows * lstride + 2,), SENTINEL, dtype=torch.int16, device=dev)
+    tbuf = torch.full((rows * tstride + 2,), SENTINEL, dtype=torch.int16, device=dev)
+    logits = lbuf[1:1 + rows * lstride].view(rows, lstride)
+    tops = tbuf[1:1 + rows * tstride].view(rows, tstride)
+    args = [torch.from_numpy(d["q"]).to(dev)]
+    if fp4:
+        args.append(torch.from_numpy(d["q_scale"]).to(dev))
+    args += [torch.from_numpy(d["w"].view(np.int16)).to(dev), torch.from_numpy(d["keys"]).to(dev),
+             torch.from_numpy(d["key_scale"]).to(dev), torch.from_numpy(d["valid_len"]).to(dev)]
+    fn = T.mxfp4_mqa_logits if fp4 else T.fp8_mqa_logits
+    fn(*args, d["qpr"], width=width, logits=logits, tops=tops)
+    torch.cuda.synchronize()
+    lb = lbuf.cpu().numpy().view(np.uint16)
+    tb = tbuf.cpu().numpy().view(np.uint16)
+    assert lb[0] == SENTINEL and lb[-1] == SENTINEL and tb[0] == SENTINEL and tb[-1] == SENTINEL
+    lg = lb[1:1 + rows * lstride].reshape(rows, lstride)
+    tp = tb[1:1 + rows * tstride].reshape(rows, tstride)
+    for t in range(rows):
+        v = max(0, min(int(d["valid_len"][t]), width))
+        ex, _, _ = oracle_row_fp4(d, t, 0.0) if fp4 else oracle_row(d, t, 0.0)
+        assert np.array_equal(lg[t, :v], ex[0]), f"row {t}"
+        assert np.all(lg[t, v:] == SENTINEL), f"row {t}: written past its length"
+        nv = (v + 7) // 8
+        want = oracle.vector_maxima(ex, np.array([v], np.int32), max(v, 1))[0][:nv]
+        assert np.array_equal(tp[t, :nv], want) and np.all(tp[t, nv:] == SENTINEL), f"row {t} maxima"
