@@ -173,6 +173,22 @@ struct Params {
   int32_t tops_lo;       // LDS word offset of the bound's low-byte bins
 };
 
+// Row of workgroup b of a one-workgroup-per-row launch.  Workgroups go to
+// the XCDs round robin (b mod 8), so with b itself as the row, row r would
+// always run on XCD r mod 8, and rows whose cost follows a period of the
+// row index that shares a factor with 8 (every tenth row costly: all of
+// them odd) would load some XCDs more than others, which then finish last.
+// Each group of 8 consecutive rows still goes to the 8 XCDs, one row each,
+// but rotated by the top 3 bits of a Fibonacci hash of the group index, so
+// that every XCD draws its rows from all residues of any period; a last
+// group of fewer than 8 rows keeps b.
+__device__ __forceinline__ int spread_row(const Params& p, int b) {
+  const int g = b & ~7;
+  if (g + 8 > p.rows) return b;
+  const uint32_t h = ((uint32_t)(b >> 3) * 2654435761u) >> 29;
+  return g + (int)(((uint32_t)b + h) & 7u);
+}
+
 // ------------------------------------------------------------------ keys
 // Two BF16 patterns in one word -> their two keys in the same halves:
 // a half with the sign bit set is inverted entirely, any other half only
@@ -1333,7 +1349,10 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
 
 template <int MODE, int NT, int VPT, bool ONE, bool ORD>
 __global__ __launch_bounds__(NT) void topk_rows_wg(Params p) {
-  rows_wg_body<MODE, NT, VPT, ONE, ORD>(p, blockIdx.x);
+  // the throughput variant runs its rows in several waves of workgroups,
+  // spread over the XCDs; with every row resident at once the order of
+  // rows on the XCDs changes nothing but which rows share a unit
+  rows_wg_body<MODE, NT, VPT, ONE, ORD>(p, ONE ? spread_row(p, blockIdx.x) : (int)blockIdx.x);
 }
 
 
@@ -1596,7 +1615,7 @@ __device__ __forceinline__ void tops_body(const Params& p, const int row, const 
 // (16384 logits), else on the direct path; the rest on the bound.
 template <int TPT, bool ONE>
 __global__ __launch_bounds__(kRowNT) void topk_rows_tops(Params p) {
-  const int row = blockIdx.x;
+  const int row = ONE ? spread_row(p, blockIdx.x) : (int)blockIdx.x;
   const int v = clamp_len(p.valid_len[row], p.width);
   const int k = p.k;
   const Out o = row_out(p, row, false);

@@ -234,13 +234,16 @@ def test_crafted_overflow_row_takes_direct_path(rows):
     assert np.all(pc == T.PATH_DIRECT_OVERFLOW), pc
 
 
-def test_many_rows_mixed():
+@pytest.mark.parametrize("rows", [2600, 2605])
+def test_many_rows_mixed(rows):
     """More token rows than workgroups resident at once (the throughput
-    kernel): every kind of row next to every other in one launch, ragged and
-    short lengths, rows built to take each fallback, and the last rows of the
-    launch; on the sampled path and the forced direct path."""
+    kernel, whose workgroups take the rows of each group of 8 in a hashed
+    rotation; 2605 rows leave a last group of 5): every kind of row next to
+    every other in one launch, ragged and short lengths, rows built to take
+    each fallback, and the last rows of the launch; on the sampled path and
+    the forced direct path."""
     rng = np.random.Generator(np.random.PCG64(2600))
-    rows, width, k = 2600, 16384, 512
+    width, k = 16384, 512
     kinds = ["normal", "bits", "ties", "negative", "neg_ties", "crowded"]
     L = np.full((rows, width), W.POISON, np.uint16)
     for i, kind in enumerate(kinds):
@@ -249,7 +252,7 @@ def test_many_rows_mixed():
     mis = np.arange(100, 1300, 97)                       # misjudged rows
     L[mis] = 0x3F00
     L[np.ix_(mis, pos)] = (0x4000 + np.arange(pos.size) % 0x700).astype(np.uint16)
-    ovf = np.arange(150, 2600, 211)                      # overflowing rows
+    ovf = np.arange(150, rows, 211)                      # overflowing rows
     L[ovf] = W.f32_to_bf16_bits(np.abs(rng.standard_normal((ovf.size, width),
                                                            dtype=np.float32)) + 1)
     L[np.ix_(ovf, pos)] = 0x3C00
@@ -279,6 +282,35 @@ def test_many_rows_mixed():
     g, pc = run_gpu(d, force_direct=True)
     assert_parity(d, g, o)
     assert set(_paths(pc)) <= {T.PATH_DIRECT_FORCED, T.PATH_SHORT}
+
+
+def test_many_block_rows():
+    """Block rows, more than workgroups resident at once (the block
+    throughput kernel): ragged lengths, -inf blocks, NaN blocks, short rows
+    and a last group of fewer than 8 rows."""
+    rng = np.random.Generator(np.random.PCG64(2603))
+    rows, width, k = 2603, 16384, 512
+    L = W.f32_to_bf16_bits(rng.standard_normal((rows, width), dtype=np.float32))
+    nblk = width // 8
+    blk = L.reshape(rows, nblk, 8)
+    blk[rng.random((rows, nblk)) < 0.02] = W.BF16_NEG_INF
+    nan_rows = rng.choice(rows, 40, replace=False)
+    blk[nan_rows, rng.integers(0, nblk, 40), rng.integers(0, 8, 40)] = 0xFFC1
+    lens = (rng.integers(8 * k + 8, width + 1, size=rows) // 8 * 8).astype(np.int32)
+    short = rng.choice(rows, 200, replace=False)
+    lens[short] = rng.integers(0, 8 * k + 1, size=short.size)
+    lens[-5:] = [width, 8 * k, 8 * k + 8, width - 5, 13]
+    for r in range(rows):
+        L[r, max(0, min(int(lens[r]), width)):] = W.POISON
+    d = dict(logits=L, valid_len=lens, k=k, mode=W.MODE_BLOCK, width=width, pages=None,
+             page_size=0)
+    o = run_oracle(d)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, o)
+    paths = _paths(pc)
+    print("paths", paths, flush=True)
+    assert -9 not in paths
+    assert paths.get(T.PATH_SAMPLED, 0) > rows // 2
 
 
 def _sampled_vectors_team(nvec, sv=1, nt=256):
