@@ -86,6 +86,7 @@ constexpr int kRelWords = kRelCopies * kRelStride;
 constexpr int kRowLoCopies = 2;           // copies of the low-byte sample bins, one-workgroup kernel
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
+constexpr int kAllSampled = 256;         // token rows of at most this many vectors: every logit sampled
 
 constexpr uint32_t kKeyNegInf = 0x007Fu; // key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF80u; // key(+inf): the pinned newest block
@@ -1174,7 +1175,7 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
     // sampled slots: every slot in token mode (one logit of every vector),
     // every SE-th slot in block mode (at most 2048 block keys)
     constexpr int SE = (MODE == TOPK_MODE_TOKEN || VPT * NT <= 2048) ? 1 : VPT * NT / 2048;
-    constexpr int NSK = VPT / SE;
+    constexpr int NSK = VPT / SE;  // one sample a sampled slot
     uint32_t sk[NSK];
     uint32_t S = 0;  // samples over the workgroup
 #pragma unroll
@@ -1210,6 +1211,17 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
         S += (uint32_t)(j < jt ? NT : (j == jt ? rem : 0));
       }
     }
+    // token rows of at most kAllSampled vectors: with one sample a vector
+    // the sampled rank's margin spans most of such a row, and its k-th key
+    // lies near zero, where keys spread over many exponents, so the cutoff
+    // would fall 256 keys or more below it and the exact select would need
+    // two more passes.  Every logit is a sample there instead (a thread's
+    // one vector gives 8), which gives the k-th key itself.  Only while
+    // every row is resident, where the slowest row is the call's time (the
+    // throughput variant's code for the other rows is then left as it was:
+    // the extra branch cost it 1.4 % on full rows).
+    const bool all = MODE == TOPK_MODE_TOKEN && !ONE && jt == 0 && rem <= kAllSampled;
+    if (all) S = (uint32_t)v;
 #pragma unroll
     for (int j = 0; j < PPT; ++j) {
       const int i = j * NT + tid;
@@ -1217,7 +1229,27 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
     }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
     __syncthreads();  // histograms zeroed, block-table copy complete
-    const uint32_t c = sample_cutoff<NSK, NT, kRowLoCopies>(sk, (jt + SE - 1) / SE, q, lists, sh);
+    uint32_t c;
+    if (MODE == TOPK_MODE_TOKEN && all) {
+      const int vid = slot_vid<NT>(0, 0, rem);
+      uint32_t s8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        s8[e] = (vid >= 0 && vid * 8 + e < v) ? key1(half_of(word_of(raw[0], e >> 1), e & 1))
+                                              : kNone;
+      c = sample_cutoff<8, NT, kRowLoCopies>(s8, 0, q, lists, sh);
+    } else {
+      c = sample_cutoff<NSK, NT, kRowLoCopies>(sk, (jt + SE - 1) / SE, q, lists, sh);
+    }
+    // every element sampled: c is the k-th key itself.  The cutoff moves to
+    // the key below it, so that the keys equal to it survive and the exact
+    // select finds it one bin above the cutoff (no tie pass), when every
+    // wave's whole share of the row fits its survivor region (rows of one
+    // slot: ceil(rem / NW) vectors a wave, 4 entries each in token mode);
+    // otherwise the keys equal to it take the tie pass.
+    if ((MODE == TOPK_MODE_BLOCK || all) && S >= (uint32_t)n && c > 0u && jt == 0 &&
+        (uint32_t)((rem + NW - 1) / NW) * (MODE == TOPK_MODE_TOKEN ? 4u : 1u) <= (uint32_t)p.lcw)
+      c -= 1u;
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
       // a zero cutoff would make the zero keys of slots past the length ties

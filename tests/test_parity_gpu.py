@@ -313,6 +313,69 @@ def test_many_block_rows():
     assert paths.get(T.PATH_SAMPLED, 0) > rows // 2
 
 
+@pytest.mark.parametrize("k", [64, 512])
+@pytest.mark.parametrize("rows", [96, 2600])
+def test_short_rows_every_logit_sampled(k, rows):
+    """Token rows of k + 1 .. 2048 logits (at most 256 vectors).  With every
+    row resident (96 rows) every logit is a sample, the cutoff is the key just
+    below the exact k-th key, and the rows take the sampled path, not the
+    direct path, whatever their values (ties at the k-th key included); with
+    k of 205 or more every wave's share fits its survivor region, so not the
+    tie pass either.  The throughput kernel (2600 rows) keeps one sample a
+    vector: the same results, on the sampled path, the tie pass or, for a
+    tied row the samples misjudge, the direct path.  Constant rows of 0xFFFF
+    (k-th key 0) take the direct path."""
+    rng = np.random.Generator(np.random.PCG64(4000 + k + rows))
+    width = 2048
+    kinds = ["normal", "bits", "ties", "negative", "neg_ties", "crowded"]
+    L = np.full((rows, width), W.POISON, np.uint16)
+    for i, kind in enumerate(kinds):
+        L[i::len(kinds)] = _random_rows(rng, L[i::len(kinds)].shape[0], width, kind)
+    L[7] = 0x3F80                                          # a constant row
+    L[8] = 0xFFFF                                          # every key 0
+    lens = rng.integers(k + 1, width + 1, size=rows).astype(np.int32)
+    lens[:6] = [k + 1, k + 7, 2047, 2048, 8 * 129 + 5, 1000]
+    for r in range(rows):
+        L[r, lens[r]:] = W.POISON
+    d = dict(logits=L, valid_len=lens, k=k, mode=0, width=width, pages=None, page_size=0)
+    o = run_oracle(d)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, o)
+    paths = _paths(pc)
+    print("paths", paths, flush=True)
+    assert pc[8] == T.PATH_DIRECT_MISJUDGED
+    others = np.delete(pc, 8)
+    if rows < 1000:   # every row resident: every logit sampled
+        allowed = [T.PATH_SAMPLED] + ([] if k >= 205 else [T.PATH_SAMPLED_TIES])
+    else:             # one sample a vector: a tied short row may be misjudged
+        allowed = [T.PATH_SAMPLED, T.PATH_SAMPLED_TIES, T.PATH_DIRECT_MISJUDGED]
+    assert np.all(np.isin(others, allowed)), _paths(others)
+
+
+@pytest.mark.parametrize("rows", [40, 2600])
+def test_short_block_rows_every_block_sampled(rows):
+    """Block rows of at most 512 blocks, where every block is sampled: the
+    cutoff is the key just below the exact k-th block key, so no tie pass;
+    ragged lengths, -inf and NaN blocks, and constant rows."""
+    rng = np.random.Generator(np.random.PCG64(4100 + rows))
+    width, k = 4096, 256
+    L = W.f32_to_bf16_bits(rng.standard_normal((rows, width), dtype=np.float32))
+    blk = L.reshape(rows, width // 8, 8)
+    blk[rng.random((rows, width // 8)) < 0.05] = W.BF16_NEG_INF
+    blk[3, 17, 2] = 0x7FC1
+    L[5] = 0x4000
+    lens = rng.integers(8 * k + 1, width + 1, size=rows).astype(np.int32)
+    lens[:3] = [8 * k + 1, width, width - 3]
+    for r in range(rows):
+        L[r, lens[r]:] = W.POISON
+    d = dict(logits=L, valid_len=lens, k=k, mode=W.MODE_BLOCK, width=width, pages=None,
+             page_size=0)
+    o = run_oracle(d)
+    g, pc = run_gpu(d)
+    assert_parity(d, g, o)
+    assert np.all(pc == T.PATH_SAMPLED), _paths(pc)
+
+
 def _sampled_vectors_team(nvec, sv=1, nt=256):
     """Vectors every member of a token team samples for a row of nvec
     vectors (nvec > sv * nt): runs of 8 consecutive vectors, run r starting
