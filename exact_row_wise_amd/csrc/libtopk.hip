@@ -86,7 +86,7 @@ constexpr int kRelWords = kRelCopies * kRelStride;
 constexpr int kRowLoCopies = 2;           // copies of the low-byte sample bins, one-workgroup kernel
 constexpr int kDirectWords = 256 * kCopies + 256;   // direct path LDS words
 constexpr int kPageLdsMax = 1024;        // block-table entries a one-workgroup row copies to LDS
-constexpr int kAllSampled = 256;         // token rows of at most this many vectors: every logit sampled
+constexpr int kAllSampled = 512;         // token rows of at most this many vectors: every logit sampled
 
 constexpr uint32_t kKeyNegInf = 0x007Fu; // key(-inf)
 constexpr uint32_t kKeyPosInf = 0xFF80u; // key(+inf): the pinned newest block
@@ -1229,7 +1229,7 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
     }
     const uint32_t q = sample_rank((uint32_t)k, (uint32_t)n, S);
     __syncthreads();  // histograms zeroed, block-table copy complete
-    uint32_t c;
+    uint32_t c, sa = 0, se = 0;
     if (MODE == TOPK_MODE_TOKEN && all) {
       const int vid = slot_vid<NT>(0, 0, rem);
       uint32_t s8[8];
@@ -1237,18 +1237,22 @@ __device__ __forceinline__ void rows_wg_body(const Params& p, const int row) {
       for (int e = 0; e < 8; ++e)
         s8[e] = (vid >= 0 && vid * 8 + e < v) ? key1(half_of(word_of(raw[0], e >> 1), e & 1))
                                               : kNone;
-      c = sample_cutoff<8, NT, kRowLoCopies>(s8, 0, q, lists, sh);
+      c = sample_cutoff<8, NT, kRowLoCopies>(s8, 0, q, lists, sh, &sa, &se);
     } else {
       c = sample_cutoff<NSK, NT, kRowLoCopies>(sk, (jt + SE - 1) / SE, q, lists, sh);
     }
     // every element sampled: c is the k-th key itself.  The cutoff moves to
     // the key below it, so that the keys equal to it survive and the exact
-    // select finds it one bin above the cutoff (no tie pass), when every
-    // wave's whole share of the row fits its survivor region (rows of one
-    // slot: ceil(rem / NW) vectors a wave, 4 entries each in token mode);
-    // otherwise the keys equal to it take the tie pass.
-    if ((MODE == TOPK_MODE_BLOCK || all) && S >= (uint32_t)n && c > 0u && jt == 0 &&
-        (uint32_t)((rem + NW - 1) / NW) * (MODE == TOPK_MODE_TOKEN ? 4u : 1u) <= (uint32_t)p.lcw)
+    // select finds it one bin above the cutoff (no tie pass).  Block rows of
+    // one slot: every wave's whole share (ceil(rem / NW) entries) fits its
+    // survivor region.  Token rows: when the keys at or above the k-th
+    // (exact counts, sa + se) fill at most half of the waves' regions (a
+    // wave that still overflows sends the row to the direct path).
+    // Otherwise the keys equal to it take the tie pass.
+    if (S >= (uint32_t)n && c > 0u && jt == 0 &&
+        (MODE == TOPK_MODE_BLOCK
+             ? (uint32_t)((rem + NW - 1) / NW) <= (uint32_t)p.lcw
+             : all && sa + se <= (uint32_t)(NW * p.lcw / 2)))
       c -= 1u;
 
     if (MODE == TOPK_MODE_TOKEN && c == 0u) {
