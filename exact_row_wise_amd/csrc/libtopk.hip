@@ -1039,12 +1039,32 @@ __device__ uint32_t ordered_regs(const uint4 (&raw)[VPT], const uint32_t (&kb)[K
         ga[j] = kb[j] > T;
         te[j] = kb[j] == T;
       } else {
+        if (T >= 0x8000u) {
+          // a non-negative k-th key: the raw halves, as signed 16-bit
+          // numbers, order non-negative values as their keys do, and every
+          // negative value is below it, so no key is formed
+          const int32_t Ts = (int32_t)T - 0x8000;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t key = key1(half_of(word_of(raw[j], e >> 1), e & 1));
-          const bool ok = vid * 8 + e < v;
-          ga[j] |= (uint32_t)(ok && key > T) << e;
-          te[j] |= (uint32_t)(ok && key == T) << e;
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = word_of(raw[j], e >> 1);
+            const int32_t h = (e & 1) ? hi16s(w) : lo16s(w);
+            ga[j] |= (uint32_t)(h > Ts) << e;
+            te[j] |= (uint32_t)(h == Ts) << e;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t key = key1(half_of(word_of(raw[j], e >> 1), e & 1));
+            ga[j] |= (uint32_t)(key > T) << e;
+            te[j] |= (uint32_t)(key == T) << e;
+          }
+        }
+        // elements past the row's length (the last vector only)
+        const int r = v - vid * 8;
+        if (r < 8) {
+          const uint32_t okm = r > 0 ? (1u << r) - 1u : 0u;
+          ga[j] &= okm;
+          te[j] &= okm;
         }
       }
     }
