@@ -314,10 +314,11 @@ def test_many_block_rows():
 
 
 @pytest.mark.parametrize("k", [64, 512])
-@pytest.mark.parametrize("rows", [96, 2600])
+@pytest.mark.parametrize("rows", [96, 600, 2600])
 def test_short_rows_every_logit_sampled(k, rows):
     """Token rows of k + 1 .. 4096 logits (at most 512 vectors).  With every
-    row resident (96 rows) every logit is a sample, and the cutoff is the key
+    row resident (96 rows: a CU and 1024 threads a row; 600 rows: 512
+    threads a row) every logit is a sample, and the cutoff is the key
     just below the exact k-th key unless the keys at or above it would fill
     more than half the survivor regions (then the tie pass): the sampled path
     or the tie pass, never the direct path, whatever the values, and mostly
